@@ -1,0 +1,239 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each ``pins_*`` function takes the implementation under test as arguments and
+returns the names of the checks it fails (empty = pinned). ``test_oracle_pins.py``
+runs them on the real oracle; ``test_oracle_mutations.py`` runs them on copies of
+the oracle with planted mistakes and requires every mutant to be caught.
+
+The references used here are independent of the oracle's code:
+- brute force: pure-Python loops with ``math.exp`` / ``math.fsum``;
+- closed forms: one key, zero query, identical keys, constant values, two keys
+  (a sigmoid), huge scores (no overflow), empty key sets;
+- invariants: shift of all keys, joint permutation of K and V, chunked merge
+  equals the unchunked result over contiguous / striped / random partitions with
+  empty chunks, merge associativity;
+- const-max: Cauchy-Schwarz bound, equality with exact attention when the bound
+  overshoots by less than ~85 nats, and the clamp collapse beyond it, including
+  the closed form of a single key.
+"""
+
+import math
+
+import numpy as np
+
+TOL = 1e-12
+
+
+def brute_attention(q, k, v, scale, allowed=None):
+    """Pure-Python attention with the row log-sum-exp (natural log)."""
+    v = np.asarray(v, dtype=np.float64)
+    Sq, Sk, Dv = len(q), len(k), v.shape[1]
+    out, lses = [], []
+    for i in range(Sq):
+        s = []
+        for j in range(Sk):
+            if allowed is not None and not allowed[i][j]:
+                continue
+            s.append((j, scale * math.fsum(float(a) * float(b) for a, b in zip(q[i], k[j]))))
+        if not s:
+            out.append([0.0] * Dv)
+            lses.append(-math.inf)
+            continue
+        m = max(x for _, x in s)
+        z = math.fsum(math.exp(x - m) for _, x in s)
+        lse = m + math.log(z)
+        row = [math.fsum(math.exp(x - lse) * float(v[j][d]) for j, x in s) for d in range(Dv)]
+        out.append(row)
+        lses.append(lse)
+    return np.array(out).reshape(Sq, Dv), np.array(lses)
+
+
+def _close(a, b, tol=TOL):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        return False
+    fin = np.isfinite(b)
+    if not np.array_equal(np.isfinite(a), fin):
+        return False
+    if not np.array_equal(a[~fin], b[~fin]):
+        return False
+    return bool(np.all(np.abs(a[fin] - b[fin]) <= tol * (1.0 + np.abs(b[fin]))))
+
+
+def pins_attention(attn):
+    """attn(q, k, v, scale, allowed=None) -> (O, lse)."""
+    bad = []
+    rng = np.random.default_rng(7)
+    # brute force, with masks including a row with no visible key
+    for case in range(6):
+        Sq, Sk, D, Dv = rng.integers(1, 7), rng.integers(1, 8), rng.integers(1, 6), rng.integers(1, 5)
+        q = rng.normal(size=(Sq, D)) * 1.7
+        k = rng.normal(size=(Sk, D))
+        v = rng.normal(size=(Sk, Dv))
+        scale = 0.3 + 0.2 * case
+        allowed = None
+        if case % 2:
+            allowed = rng.random((Sq, Sk)) < 0.6
+            allowed[0, :] = False
+        o1, l1 = attn(q, k, v, scale, allowed)
+        o2, l2 = brute_attention(q, k, v, scale, allowed)
+        if not (_close(o1, o2, 1e-12) and _close(l1, l2, 1e-12)):
+            bad.append(f"brute_force[{case}]")
+    # one key: O = v0, lse = s00
+    q = rng.normal(size=(3, 4)); k = rng.normal(size=(1, 4)); v = rng.normal(size=(1, 2))
+    o, l = attn(q, k, v, 0.5)
+    if not (_close(o, np.repeat(v, 3, 0)) and _close(l, 0.5 * (q @ k[0]))):
+        bad.append("one_key")
+    # zero query: O = mean(V), lse = log(Sk)
+    k = rng.normal(size=(5, 4)); v = rng.normal(size=(5, 3))
+    o, l = attn(np.zeros((2, 4)), k, v, 0.9)
+    if not (_close(o, np.repeat(v.mean(0, keepdims=True), 2, 0)) and _close(l, np.full(2, math.log(5)))):
+        bad.append("zero_query")
+    # identical keys: O = mean(V), lse = s + log(Sk)
+    q = rng.normal(size=(2, 4)); k1 = rng.normal(size=(1, 4))
+    o, l = attn(q, np.repeat(k1, 6, 0), v[:1].repeat(6, 0) + np.arange(6)[:, None], 0.7)
+    want_o = v[:1] + np.arange(6).mean()
+    if not (_close(o, np.repeat(want_o, 2, 0)) and _close(l, 0.7 * (q @ k1[0]) + math.log(6))):
+        bad.append("identical_keys")
+    # constant values: O = that vector
+    q = rng.normal(size=(3, 4)); k = rng.normal(size=(7, 4)); cv = rng.normal(size=(1, 5))
+    o, _ = attn(q, k, np.repeat(cv, 7, 0), 1.1)
+    if not _close(o, np.repeat(cv, 3, 0)):
+        bad.append("constant_values")
+    # two keys: sigmoid weights
+    q = np.array([[1.0, -2.0]]); k = np.array([[0.5, 0.25], [-1.0, 3.0]]); v = np.array([[2.0], [-4.0]])
+    s0, s1 = 0.8 * (0.5 - 0.5), 0.8 * (-1.0 - 6.0)
+    sig = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+    o, l = attn(q, k, v, 0.8)
+    if not (_close(o, [[sig * 2.0 + (1 - sig) * -4.0]]) and _close(l, [math.log(math.exp(s0) + math.exp(s1))])):
+        bad.append("two_keys")
+    # huge scores: no overflow (the max must come off before exp)
+    q = np.array([[40.0, 0.0]]); k = np.array([[40.0, 0.0], [39.5, 0.0]]); v = np.array([[1.0], [3.0]])
+    o, l = attn(q, k, v, 1.0)
+    s0, s1 = 1600.0, 1580.0
+    w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+    if not (_close(o, [[1.0 * (1 - w1) + 3.0 * w1]]) and _close(l, [s0 + math.log1p(math.exp(s1 - s0))])):
+        bad.append("huge_scores")
+    # empty key set
+    o, l = attn(rng.normal(size=(2, 3)), np.zeros((0, 3)), np.zeros((0, 2)), 1.0)
+    if not (np.all(o == 0) and np.all(l == -np.inf) and o.shape == (2, 2)):
+        bad.append("empty_keys")
+    # shift invariance: k_j -> k_j + u shifts lse by scale*q.u, O unchanged
+    q = rng.normal(size=(4, 6)); k = rng.normal(size=(9, 6)); v = rng.normal(size=(9, 3)); u = rng.normal(size=6)
+    o1, l1 = attn(q, k, v, 0.4)
+    o2, l2 = attn(q, k + u, v, 0.4)
+    if not (_close(o1, o2, 1e-11) and _close(l2 - l1, 0.4 * (q @ u), 1e-11)):
+        bad.append("shift_invariance")
+    # joint permutation of K and V
+    perm = rng.permutation(9)
+    o3, l3 = attn(q, k[perm], v[perm], 0.4)
+    if not (_close(o1, o3, 1e-12) and _close(l1, l3, 1e-12)):
+        bad.append("permutation")
+    return bad
+
+
+def pins_merge(attn, merge):
+    """merge(o_list, lse_list) -> (O, lse); attn as in ``pins_attention``."""
+    bad = []
+    rng = np.random.default_rng(11)
+    # two partials with known weights: lse log1 and log3 -> 1/4, 3/4
+    o, l = merge([np.array([[4.0, 0.0]]), np.array([[0.0, 8.0]])], [np.array([0.0]), np.array([math.log(3.0)])])
+    if not (_close(o, [[1.0, 6.0]]) and _close(l, [math.log(4.0)])):
+        bad.append("two_partials")
+    # all partials empty
+    o, l = merge([np.ones((2, 3)), np.ones((2, 3))], [np.full(2, -np.inf), np.full(2, -np.inf)])
+    if not (np.all(o == 0) and np.all(l == -np.inf)):
+        bad.append("all_empty")
+    # one partial empty: result is the other one
+    o, l = merge([np.full((1, 2), 5.0), np.array([[1.0, 2.0]])], [np.array([-np.inf]), np.array([2.5])])
+    if not (_close(o, [[1.0, 2.0]]) and _close(l, [2.5])):
+        bad.append("one_empty")
+    # huge lse values do not overflow
+    o, l = merge([np.array([[1.0]]), np.array([[3.0]])], [np.array([1000.0]), np.array([1000.0])])
+    if not (_close(o, [[2.0]]) and _close(l, [1000.0 + math.log(2.0)])):
+        bad.append("huge_lse")
+    # chunked merge equals unchunked: contiguous, striped, random, with empty chunks
+    Sq, Sk, D = 5, 24, 4
+    q = rng.normal(size=(Sq, D)) * 1.5; k = rng.normal(size=(Sk, D)); v = rng.normal(size=(Sk, 3))
+    full_o, full_l = attn(q, k, v, 0.6)
+    parts = {
+        "contiguous4": [np.arange(6 * r, 6 * r + 6) for r in range(4)],
+        "striped3": [np.arange(r, Sk, 3) for r in range(3)],
+        "random5_with_empty": np.array_split(rng.permutation(Sk), 4) + [np.array([], dtype=int)],
+        "single": [np.arange(Sk)],
+    }
+    for name, idx in parts.items():
+        os_, ls_ = zip(*[attn(q, k[i], v[i], 0.6) for i in idx])
+        o, l = merge(list(os_), list(ls_))
+        if not (_close(o, full_o, 1e-11) and _close(l, full_l, 1e-11)):
+            bad.append(f"chunked_{name}")
+    # causal mask split across chunks (fully masked rows inside chunks)
+    pos_q = np.array([0, 5, 11, 17, 23]); pos_k = np.arange(Sk)
+    allowed = pos_q[:, None] >= pos_k[None, :]
+    full_o, full_l = attn(q, k, v, 0.6, allowed)
+    os_, ls_ = zip(*[attn(q, k[6 * r:6 * r + 6], v[6 * r:6 * r + 6], 0.6, allowed[:, 6 * r:6 * r + 6]) for r in range(4)])
+    o, l = merge(list(os_), list(ls_))
+    if not (_close(o, full_o, 1e-11) and _close(l, full_l, 1e-11)):
+        bad.append("chunked_causal")
+    # associativity
+    a, b, c = (attn(q, k[i], v[i], 0.6) for i in (np.arange(0, 7), np.arange(7, 15), np.arange(15, 24)))
+    ab = merge([a[0], b[0]], [a[1], b[1]])
+    o1, l1 = merge([ab[0], c[0]], [ab[1], c[1]])
+    o2, l2 = merge([a[0], b[0], c[0]], [a[1], b[1], c[1]])
+    if not (_close(o1, o2, 1e-12) and _close(l1, l2, 1e-12)):
+        bad.append("associativity")
+    return bad
+
+
+def pins_const_max(attn, const_max, bound):
+    """const_max(q, k_chunks, v_chunks, scale) -> (O, lse, c);
+    bound(q, k_chunks, scale) -> (c, kmax_sq)."""
+    bad = []
+    rng = np.random.default_rng(13)
+    q = rng.normal(size=(6, 8)); ks = [rng.normal(size=(5, 8)) for _ in range(3)]
+    vs = [rng.normal(size=(5, 4)) for _ in range(3)]
+    k_all = np.concatenate(ks); v_all = np.concatenate(vs)
+    c, kmax_sq = bound(q, ks, 0.35)
+    # the bound by its definition, by brute force
+    want_kmax = max(math.fsum(x * x for x in row) for row in k_all)
+    want_c = [0.35 * math.sqrt(math.fsum(x * x for x in row)) * math.sqrt(want_kmax) for row in q]
+    if not (_close(c, want_c) and _close([kmax_sq], [want_kmax])):
+        bad.append("bound_definition")
+    # the bound is an upper bound on every score (Cauchy-Schwarz)
+    if not np.all(0.35 * (q @ k_all.T) <= c[:, None] + 1e-12):
+        bad.append("bound_is_upper")
+    # the largest key sits in the last chunk: the max must span all chunks
+    ks2 = [x.copy() for x in ks]; ks2[-1][2] *= 5.0
+    c2, _ = bound(q, ks2, 0.35)
+    if not _close(c2, 0.35 * np.linalg.norm(q, axis=1) * np.linalg.norm(ks2[-1][2])):
+        bad.append("bound_spans_chunks")
+    # equals exact attention when the overshoot is moderate
+    o, l, _ = const_max(q, ks, vs, 0.35)
+    eo, el = attn(q, k_all, v_all, 0.35)
+    if not (_close(o, eo, 1e-11) and _close(l, el, 1e-11)):
+        bad.append("equals_exact")
+    # single key with an overshoot of delta nats: sum = exp(-delta); clamp at 1e-37
+    for delta, name in ((80.0, "overshoot_80"), (90.0, "overshoot_90")):
+        qd = np.array([[1.0, 0.0]])
+        k_hit = np.array([[0.0, 0.0]])            # the key the row attends: score 0
+        k_far = np.array([[0.0, delta]])          # a loud key the row does not see at all... orthogonal
+        vv = np.array([[2.0], [7.0]])
+        # scores: 0 and 0; bound c = 1 * |q| * delta = delta -> each term exp(-delta)
+        o, l, cc = const_max(qd, [k_hit, k_far], [vv[:1], vv[1:]], 1.0)
+        z = 2.0 * math.exp(-delta)
+        zc = max(z, 1e-37)
+        want_o = (2.0 + 7.0) * math.exp(-delta) / zc
+        want_l = delta + math.log(zc)
+        if not (_close(cc, [delta]) and _close(o, [[want_o]], 1e-9) and _close(l, [want_l], 1e-9)):
+            bad.append(name)
+    # at 80 nats it still matches exact attention; at 90 it has collapsed
+    o80, l80, _ = const_max(np.array([[1.0, 0.0]]), [np.zeros((1, 2)), np.array([[0.0, 80.0]])],
+                            [np.array([[2.0]]), np.array([[7.0]])], 1.0)
+    if not (_close(o80, [[4.5]], 1e-9) and _close(l80, [math.log(2.0)], 1e-9)):
+        bad.append("no_collapse_at_80")
+    o90, _, _ = const_max(np.array([[1.0, 0.0]]), [np.zeros((1, 2)), np.array([[0.0, 90.0]])],
+                          [np.array([[2.0]]), np.array([[7.0]])], 1.0)
+    if abs(float(o90[0, 0]) - 4.5) < 1.0:
+        bad.append("collapse_at_90")
+    return bad

@@ -1,0 +1,138 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and require the pins
+to reject every one: a pin that no mistake can fail would pin nothing."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from pins import pins_attention, pins_const_max, pins_merge
+
+
+def _attn_factory(scale_pow=1, use_max=True, lse_log=np.log, normalise=True, honour_mask=True,
+                  lse_adds_max=True, swap_qk_in_pv=False):
+    def attn(q, k, v, scale, allowed=None):
+        q = np.asarray(q, float); k = np.asarray(k, float); v = np.asarray(v, float)
+        Sq, Sk = q.shape[0], k.shape[0]
+        o = np.zeros((Sq, v.shape[1])); lse = np.full(Sq, -np.inf)
+        if Sk == 0 or Sq == 0:
+            return o, lse
+        s = (scale ** scale_pow) * (q @ k.T)
+        if allowed is not None and honour_mask:
+            s = np.where(allowed, s, -np.inf)
+        with np.errstate(all="ignore"):
+            m = s.max(axis=1) if use_max else np.zeros(Sq)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.exp(s - m[:, None])
+            z = e.sum(axis=1)
+            live = z > 0
+            lse = np.where(live, (m if lse_adds_max else 0.0) + lse_log(np.where(live, z, 1.0)), -np.inf)
+            p = e / np.where(live, z, 1.0)[:, None] if normalise else e
+            if swap_qk_in_pv:
+                p = p[:, ::-1]
+            o = np.where(live[:, None], p @ v, 0.0)
+        return o, lse
+    return attn
+
+
+ATTN_MUTANTS = {
+    "scale_dropped": _attn_factory(scale_pow=0),
+    "scale_squared": _attn_factory(scale_pow=2),
+    "no_max_subtraction": _attn_factory(use_max=False),
+    "lse_log10": _attn_factory(lse_log=np.log10),
+    "unnormalised_output": _attn_factory(normalise=False),
+    "mask_ignored": _attn_factory(honour_mask=False),
+    "lse_missing_max": _attn_factory(lse_adds_max=False),
+    "value_rows_reversed": _attn_factory(swap_qk_in_pv=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_caught(name):
+    assert pins_attention(ATTN_MUTANTS[name]), f"{name} passed every attention pin"
+
+
+def _merge_factory(kind):
+    def merge(o_parts, lse_parts):
+        L = np.stack([np.asarray(x, float) for x in lse_parts]); O = np.stack([np.asarray(x, float) for x in o_parts])
+        with np.errstate(all="ignore"):
+            M = L.max(axis=0)
+            live = np.isfinite(M)
+            Ms = np.where(live, M, 0.0)
+            if kind == "no_max":
+                g = np.log(np.exp(L).sum(axis=0))
+            elif kind == "global_is_max":
+                g = M
+            else:
+                g = np.where(live, Ms + np.log(np.exp(L - Ms).sum(axis=0)), -np.inf)
+            gs = np.where(np.isfinite(g), g, 0.0)
+            if kind == "inverted_weight":
+                w = np.where(np.isfinite(L), np.exp(gs - L), 0.0)
+            elif kind == "plain_mean":
+                w = np.where(np.isfinite(L), 1.0 / L.shape[0], 0.0)
+            else:
+                w = np.where(np.isfinite(L), np.exp(L - gs), 0.0)
+            out = (w[..., None] * O).sum(axis=0)
+        return out, g
+    return merge
+
+
+@pytest.mark.parametrize("kind", ["no_max", "global_is_max", "inverted_weight", "plain_mean"])
+def test_merge_mutant_caught(kind):
+    assert pins_merge(oracle.attention, _merge_factory(kind)), kind
+
+
+def _bound_factory(kind):
+    def bound(q, k_chunks, scale):
+        q = np.asarray(q, float)
+        ks = [np.asarray(x, float) for x in k_chunks]
+        if kind == "first_chunk_only":
+            ks = ks[:1]
+        kmax = max(float((x * x).sum(axis=1).max()) for x in ks if len(x))
+        qn2 = (q * q).sum(axis=1)
+        if kind == "no_sqrt":
+            return scale * qn2 * kmax, kmax
+        if kind == "no_scale":
+            return np.sqrt(qn2 * kmax), kmax
+        return scale * np.sqrt(qn2) * math.sqrt(kmax), kmax
+    return bound
+
+
+def _const_max_factory(bound, clamp=1e-37, lse_adds_c=True):
+    def cm(q, k_chunks, v_chunks, scale):
+        q = np.asarray(q, float)
+        c, _ = bound(q, k_chunks, scale)
+        Z = np.zeros(q.shape[0]); A = np.zeros((q.shape[0], np.asarray(v_chunks[0]).shape[1]))
+        with np.errstate(all="ignore"):
+            for kc, vc in zip(k_chunks, v_chunks):
+                p = np.exp(scale * (q @ np.asarray(kc, float).T) - c[:, None])
+                Z += p.sum(axis=1); A += p @ np.asarray(vc, float)
+            Zc = np.maximum(Z, clamp) if clamp else Z
+            return A / Zc[:, None], (c if lse_adds_c else 0.0) + np.log(Zc), c
+    return cm
+
+
+CM_MUTANTS = {
+    "bound_first_chunk_only": (_bound_factory("first_chunk_only"), {}),
+    "bound_no_sqrt": (_bound_factory("no_sqrt"), {}),
+    "bound_no_scale": (_bound_factory("no_scale"), {}),
+    "no_clamp": (_bound_factory("ok"), {"clamp": 0.0}),
+    "clamp_too_high": (_bound_factory("ok"), {"clamp": 1e-30}),
+    "lse_missing_c": (_bound_factory("ok"), {"lse_adds_c": False}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CM_MUTANTS))
+def test_const_max_mutant_caught(name):
+    bound, kw = CM_MUTANTS[name]
+    assert pins_const_max(oracle.attention, _const_max_factory(bound, **kw), bound), name
+
+
+def test_unmutated_factories_pass():
+    """The factories themselves, without a planted mistake, pass: so a caught mutant is
+    caught for its mistake, not for a difference in the harness."""
+    assert pins_attention(_attn_factory()) == []
+    assert pins_merge(oracle.attention, _merge_factory("ok")) == []
+    b = _bound_factory("ok")
+    assert pins_const_max(oracle.attention, _const_max_factory(b), b) == []
