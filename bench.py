@@ -1,0 +1,286 @@
+"""Benchmark of the context-parallel attention hot path on one MI355X.
+
+Headline (``value``): one rank's ring pass of the Wan2.2-shaped workload (10 heads of
+128, S = 32768 over cp = 8, local 4096 queries): 8 online-max steps, each fed by a
+double-buffered K/V chunk copy, then the LSE merge. value = algorithmic TFLOP/s of the
+whole pass (4*H*Sq*S*D flops), inputs resident in HBM when timing starts.
+
+Also reported (``workloads``): the const-max ring on the 720p share (40 heads,
+local 9450), the striped causal ring at S = 128k (all 8 ranks' passes), DCP decode
+over two interleaved paged shards (KV GB/s), and the tiny fp32 ring.
+
+``roofline`` is measured live for the dominant kernel with HIP events on the stream it
+is launched on; ``cpu_baseline`` times the fp64 oracle on a bounded row sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def ring_flops(H, Sq, Sk, D):
+    return 4.0 * H * Sq * Sk * D
+
+
+def time_ring(rp, steps, warmup, torch):
+    """Runs warmup + timed ring passes; returns (ms per pass, mean step-kernel ms, per-step ms)."""
+    cp = rp.cp
+    for _ in range(warmup):
+        rp.run()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cp)]
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for k in range(steps):
+        rp.run(timing_events=ev[k])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    per_step = [sum(ev[k][s][0].elapsed_time(ev[k][s][1]) for k in range(steps)) / steps for s in range(cp)]
+    return ms, per_step
+
+
+def headline(args, torch, ca, workloads, gen, dev):
+    wl = workloads.workload("wan22_cp8_online")
+    log(f"[bench] generating {wl.name} inputs")
+    t = gen.ring_inputs(wl, dev)
+    q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout)
+    kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
+    vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
+    del t
+    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online")
+    log("[bench] timing ring pass")
+    ms, per_step = time_ring(rp, args.steps, args.warmup, torch)
+    Sq = wl.local_S
+    flops_pass = ring_flops(wl.H, Sq, wl.S, wl.D)
+    flops_step = ring_flops(wl.H, Sq, wl.local_S, wl.D)
+    step_ms = sum(per_step) / len(per_step)
+    achieved = flops_step / (step_ms * 1e-3) / 1e12
+    return {
+        "wl": wl, "ms": ms, "tflops": flops_pass / (ms * 1e-3) / 1e12, "step_ms": step_ms,
+        "per_step_ms": per_step,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_step_bf16 (ring_attn_step)",
+                     "per_launch": f"{flops_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128"},
+        "inputs": (q, kp, vp),
+    }
+
+
+def cpu_baseline(q, kp, vp, D, budget_s=12.0):
+    """fp64 oracle on a bounded sample of query rows (all heads, full key range)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    H = q.shape[2]
+    scale = oracle.default_scale(D)
+    S = kp.shape[0] * kp.shape[2]
+    k_all = oracle.to_f64(kp[:, 0].reshape(S, H, D))
+    v_all = oracle.to_f64(vp[:, 0].reshape(S, H, D))
+    rng = np.random.default_rng(0)
+    rows_done, t_total, batch = 0, 0.0, 32
+    while t_total < budget_s and rows_done < q.shape[1]:
+        rows = rng.choice(q.shape[1], size=batch, replace=False)
+        qs = oracle.to_f64(q[0, rows])
+        t0 = time.perf_counter()
+        for h in range(H):
+            oracle.attention(qs[:, h], k_all[:, h], v_all[:, h], scale)
+        t_total += time.perf_counter() - t0
+        rows_done += batch
+    flops = ring_flops(H, rows_done, S, D)
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows x {H} heads against all {S} keys (fp64 numpy oracle, "
+                      f"{t_total:.1f} s); same per-row work as the GPU pass"}
+
+
+def run_constmax(args, torch, ca, workloads, gen, dev):
+    wl = workloads.workload("wan22_720p_constmax")
+    log(f"[bench] {wl.name}")
+    t = gen.ring_inputs(wl, dev)
+    q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout).contiguous()
+    kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
+    vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
+    del t
+    out = {}
+    for variant in ("constmax", "online"):
+        rp = ca.ring.RingPass(q, kp, vp, 0, variant=variant)
+        ms, per_step = time_ring(rp, max(2, args.steps // 4), 1, torch)
+        fl = ring_flops(wl.H, wl.local_S, wl.S, wl.D)
+        step_ms = sum(per_step) / len(per_step)
+        ach = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D) / (step_ms * 1e-3) / 1e12
+        out[variant] = {"ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                        "step_kernel_ms": round(step_ms, 4), "step_tflops": round(ach, 2),
+                        "frac_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
+        del rp
+    return {"workload": wl.name, "config": f"B=1 H=40 D=128 S=75600 cp=8 local=9450 bf16", **out}
+
+
+def run_striped(args, torch, ca, workloads, gen, dev):
+    wl = workloads.workload("striped_causal_128k")
+    log(f"[bench] {wl.name}")
+    t = gen.ring_inputs(wl, dev)
+    kp = ca.ring.chunk_pool(t["k"], wl.cp, "striped")
+    vp = ca.ring.chunk_pool(t["v"], wl.cp, "striped")
+    qs = [ca.ring.shard(t["q"], wl.cp, r, "striped").contiguous() for r in range(wl.cp)]
+    del t
+    copy_stream = torch.cuda.Stream()
+    per_rank = []
+    step_ms_all = []
+    for r in range(wl.cp):
+        rp = ca.ring.RingPass(qs[r], kp, vp, r, layout="striped", causal=True, copy_stream=copy_stream)
+        ms, per_step = time_ring(rp, max(1, args.steps // 10), 1, torch)
+        per_rank.append(ms)
+        step_ms_all.extend(per_step)
+        del rp
+    S, H, D = wl.S, wl.H, wl.D
+    total = 4.0 * H * D * S * (S + 1) / 2
+    tot_ms = sum(per_rank)
+    mean = tot_ms / len(per_rank)
+    return {"workload": wl.name, "config": "B=1 H=32 D=128 S=131072 cp=8 striped causal bf16, all 8 ranks",
+            "ms_all_ranks": round(tot_ms, 3), "tflops": round(total / (tot_ms * 1e-3) / 1e12, 2),
+            "per_rank_ms": [round(x, 3) for x in per_rank],
+            "rank_balance_max_over_mean": round(max(per_rank) / mean, 4),
+            "mean_step_kernel_ms": round(sum(step_ms_all) / len(step_ms_all), 4)}
+
+
+def run_decode(args, torch, ca, workloads, gen, dev):
+    wl = workloads.workload("dcp_decode_gqa")
+    log(f"[bench] {wl.name}: building paged shards")
+    d = gen.decode_inputs(wl, dev)
+    shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], d["ctx"], r, wl.shards,
+                                       wl.interleave, wl.block_size, d["block_rand"]) for r in range(wl.shards)]
+    del d["k_seq"], d["v_seq"]
+    run = ca.dcp.DcpDecode(d["q"], shards)
+    steps = max(5, args.steps)
+    for _ in range(2):
+        run.run()
+    torch.cuda.synchronize()
+    kv_bytes = sum(sc.nbytes_kv for sc in shards)
+    cs = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in shards]
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for k in range(steps):
+        for r, sc in enumerate(shards):
+            ev[k][r][0].record(cs)
+            ca.dcp_decode_partial(run.q, sc.k_pool, sc.v_pool, sc.block_table, sc.local_lens,
+                                  out=run.o_parts[r], lse=run.lse_parts[r], workspace=run.ws[r])
+            ev[k][r][1].record(cs)
+        ca.lse_merge(run.o_parts, run.lse_parts, out=run.out, lse_out=run.lse)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    shard_ms = [sum(ev[k][r][0].elapsed_time(ev[k][r][1]) for k in range(steps)) / steps for r in range(len(shards))]
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    per_launch = [sc.nbytes_kv / (m * 1e-3) / 1e9 for sc, m in zip(shards, shard_ms)]
+    ach = sum(per_launch) / len(per_launch)
+    return {"workload": wl.name, "config": "B=32 Hq=64 Hkv=8 D=128 bf16, ctx U[32k,128k], block 16, 2 interleaved shards",
+            "kv_bytes": kv_bytes, "ms_per_step": round(ms, 4), "kv_GBps": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "dcp_decode_split_kernel + combine (dcp_decode_partial)",
+                         "per_launch": "one shard's resident K+V bytes = local tokens * Hkv * D * 2 * 2"}}
+
+
+def run_tiny(args, torch, ca, workloads, gen, dev):
+    wl = workloads.workload("tiny_ring_fp32")
+    t = gen.ring_inputs(wl, dev)
+    q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout).contiguous()
+    kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
+    vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
+    res = {"workload": wl.name, "config": "B=1 H=2 D=64 S=512 cp=4 fp32"}
+    for variant in ("online", "constmax"):
+        rp = ca.ring.RingPass(q, kp, vp, 0, variant=variant)
+        ms, _ = time_ring(rp, 10, 2, torch)
+        res[f"{variant}_ms_per_pass"] = round(ms, 4)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share only: the ring's other ranks are simulated on the same "
+              "device, so --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import context_attention_lse_amd as ca
+    import workloads
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ca._lib.load()
+
+    h = headline(args, torch, ca, workloads, gen, dev)
+    wl = h["wl"]
+    line = {
+        "metric": "ring-step attention TFLOP/s (% bf16 MFMA peak); DCP decode KV GB/s (% HBM)",
+        "value": round(h["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded torch.randn; Q,K RMS-normalised across 40 heads x 128, gain 1)",
+        "config": {"workload": wl.name, "B": wl.B, "heads": wl.H, "head_dim": wl.D, "global_seq": wl.S,
+                   "cp": wl.cp, "local_seq": wl.local_S, "rank": 0, "steps_per_pass": wl.cp,
+                   "flops_per_pass": ring_flops(wl.H, wl.local_S, wl.S, wl.D)},
+        "roofline": h["roofline"],
+        "step_kernel_ms": round(h["step_ms"], 4),
+    }
+    extra = {}
+    if not args.headline_only:
+        q, kp, vp = h.pop("inputs")
+        for fn in (run_constmax, run_striped, run_decode, run_tiny):
+            try:
+                extra[fn.__name__[4:]] = fn(args, torch, ca, workloads, gen, dev)
+            except Exception as e:  # report, do not hide
+                extra[fn.__name__[4:]] = {"error": repr(e)}
+            torch.cuda.empty_cache()
+        line["workloads"] = extra
+    if not args.no_cpu_baseline:
+        q, kp, vp = h["inputs"] if "inputs" in h else (q, kp, vp)
+        log("[bench] cpu baseline (fp64 oracle sample)")
+        line["cpu_baseline"] = cpu_baseline(q, kp, vp, wl.D)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

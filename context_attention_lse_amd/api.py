@@ -1,0 +1,209 @@
+"""Python binding of libctxattn: the C entry points under the same names.
+
+Argument marshalling only. Each function checks devices and dtypes, allocates the
+outputs it is not given (with torch, the caller-side allocator), and passes raw
+pointers, sizes and the current HIP stream to the library. Every computation runs
+in the library's HIP kernels; there is no other implementation to fall back to.
+
+Tensors follow the library's layouts: attention inputs are [B, S, H, D] (any
+strides with D contiguous), outputs [B, H, S, D] fp32 and LSE [B, H, S] fp32.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (CA_BF16, CA_FP32, CA_MASK_CAUSAL_INCL, CA_MASK_CAUSAL_STRICT, CA_MASK_NONE,  # noqa: F401
+                   CA_PHASE_ACCUMULATE, CA_PHASE_FINAL, CA_PHASE_INIT, CtxAttnError)
+
+MASKS = {"none": CA_MASK_NONE, "causal_incl": CA_MASK_CAUSAL_INCL, "causal_strict": CA_MASK_CAUSAL_STRICT}
+_DT = {torch.bfloat16: CA_BF16, torch.float32: CA_FP32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    return _DT[t.dtype]
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(t: torch.Tensor) -> _lib.ca_strides:
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, S, H, D] tensor, got shape {tuple(t.shape)}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the head dimension D must be contiguous")
+    return _lib.ca_strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _scale(scale):
+    return 0.0 if scale is None else float(scale)
+
+
+def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, stream=None):
+    """Online-max attention of q [B, Sq, H, D] against one K/V chunk [B, Sk, H, D].
+    Returns (o [B, H, Sq, D] fp32, lse [B, H, Sq] fp32)."""
+    _check_cuda(q, k, v, out, lse)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    if q.dtype != k.dtype or k.dtype != v.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _lib.call("ring_attn_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
+              B, H, Sq, Sk, D, _scale(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
+              _ptr(out), _ptr(lse), _stream(stream))
+    return out, lse
+
+
+def key_sqnorm_max(k, kmax_sq=None, accumulate=False, stream=None):
+    """Per (b, h) max of |k_j|^2 over the chunk, optionally max-folded into kmax_sq [B, H]."""
+    _check_cuda(k, kmax_sq)
+    B, S, H, D = k.shape
+    if kmax_sq is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing kmax_sq")
+        kmax_sq = torch.empty((B, H), dtype=torch.float32, device=k.device)
+    _lib.call("key_sqnorm_max", _ptr(k), _strides(k), _dtype_code(k), B, S, H, D, _ptr(kmax_sq),
+              int(bool(accumulate)), _stream(stream))
+    return kmax_sq
+
+
+def const_max_bound(q, kmax_sq, scale=None, out=None, stream=None):
+    """Per-row bound c [B, H, Sq] = scale * |q_i| * sqrt(kmax_sq[b, h])."""
+    _check_cuda(q, kmax_sq, out)
+    B, Sq, H, D = q.shape
+    if out is None:
+        out = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _lib.call("const_max_bound", _ptr(q), _strides(q), _dtype_code(q), B, Sq, H, D, _scale(scale),
+              _ptr(kmax_sq), _ptr(out), _stream(stream))
+    return out
+
+
+def const_max_acc_size(B, H, Sq, D) -> int:
+    """Floats of the const-max accumulator: [B, H, Sq, D] output then [B, H, Sq] row sums."""
+    return B * H * Sq * (D + 1)
+
+
+def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dtype=torch.float32,
+                             scale=None, stream=None):
+    """One const-max ring step. acc: fp32 tensor of const_max_acc_size floats (None allowed
+    when phase == INIT|FINAL). On the FINAL phase returns (o [B, H, Sq, D], lse [B, H, Sq])."""
+    _check_cuda(q, k, v, c, acc, out, lse)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    if acc is not None and acc.numel() < const_max_acc_size(B, H, Sq, D):
+        raise ValueError("acc is too small")
+    final = bool(phase & CA_PHASE_FINAL)
+    if final:
+        if out is None:
+            out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _lib.call("ring_attn_const_max_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
+              B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase),
+              _ptr(out) if final else None, _DT.get(out.dtype, CA_FP32) if final else CA_FP32,
+              _ptr(lse) if final else None, _stream(stream))
+    return (out, lse) if final else None
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse_out=None, out_dtype=torch.float32, stream=None):
+    """Merge n partials: o_parts [n, ..., D] fp32, lse_parts [n, ...] fp32 (contiguous).
+    Returns (o [..., D], lse [...])."""
+    _check_cuda(o_parts, lse_parts, out, lse_out)
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    n, D = o_parts.shape[0], o_parts.shape[-1]
+    lead = tuple(o_parts.shape[1:-1])
+    if tuple(lse_parts.shape) != (n,) + lead:
+        raise ValueError(f"lse_parts shape {tuple(lse_parts.shape)} does not match {(n,) + lead}")
+    rows = 1
+    for x in lead:
+        rows *= x
+    if out is None:
+        out = torch.empty(lead + (D,), dtype=out_dtype, device=o_parts.device)
+    if lse_out is None:
+        lse_out = torch.empty(lead, dtype=torch.float32, device=o_parts.device)
+    _lib.call("lse_merge", n, _ptr(o_parts), _ptr(lse_parts), rows, D, _ptr(out), _DT[out.dtype],
+              _ptr(lse_out), _stream(stream))
+    return out, lse_out
+
+
+def dcp_decode_workspace_size(B, Hq, D, block_size, max_blocks) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.call("dcp_decode_workspace_size", B, Hq, D, block_size, max_blocks, ctypes.byref(n))
+    return int(n.value)
+
+
+def dcp_decode_partial(q, k_pool, v_pool, block_table, local_lens, scale=None, out=None, lse=None,
+                       workspace=None, stream=None):
+    """One DCP shard's decode partial. q [B, Hq, D] bf16; k_pool [NB, Hkv, 16, D];
+    v_pool [NB, Hkv, D, 16]; block_table [B, max_blocks] int32; local_lens [B] int32.
+    Returns (o [B, Hq, D] fp32, lse [B, Hq] fp32)."""
+    _check_cuda(q, k_pool, v_pool, block_table, local_lens, out, lse, workspace)
+    B, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_pool.shape
+    if tuple(v_pool.shape) != (NB, Hkv, D, bs):
+        raise ValueError(f"v_pool must be [NB, Hkv, D, block_size], got {tuple(v_pool.shape)}")
+    for t in (q, k_pool, v_pool, block_table, local_lens):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or local_lens.dtype != torch.int32:
+        raise TypeError("block_table and local_lens must be int32")
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise TypeError("decode q and pools must be bfloat16")
+    max_blocks = block_table.shape[1]
+    need = dcp_decode_workspace_size(B, Hq, D, bs, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _lib.call("dcp_decode_partial", _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(local_lens),
+              B, Hq, Hkv, D, bs, max_blocks, NB, _scale(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream))
+    return out, lse
+
+
+def kv_chunk_copy(dst_k, dst_v, src_k, src_v, stream=None):
+    """Asynchronous device copy of one K and one V chunk (the ring hop on one GPU)."""
+    _check_cuda(dst_k, dst_v, src_k, src_v)
+    nbytes = src_k.numel() * src_k.element_size()
+    for t in (dst_k, dst_v, src_v):
+        if t.numel() * t.element_size() != nbytes:
+            raise ValueError("chunk sizes differ")
+    for t in (dst_k, dst_v, src_k, src_v):
+        if not t.is_contiguous():
+            raise ValueError("chunks must be contiguous")
+    _lib.call("kv_chunk_copy", _ptr(dst_k), _ptr(dst_v), _ptr(src_k), _ptr(src_v), nbytes, _stream(stream))
+
+
+def version() -> str:
+    return _lib.load().ca_version().decode()

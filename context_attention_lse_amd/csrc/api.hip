@@ -1,0 +1,234 @@
+// C ABI of libctxattn: argument validation, then one launch sequence per call on the
+// caller's stream. No allocation, no state kept between calls (see include/ctxattn.h).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ca_status fail(ca_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ca_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) {
+    g_err[0] = 0;
+    return CA_OK;
+  }
+  return fail(CA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+float resolve_scale(float s, int D) { return s > 0.0f ? s : 1.0f / std::sqrt(float(D)); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a [B, S, H, D] strided input: D contiguous, every row start 16-byte aligned.
+ca_status check_bshd(const char* name, const void* p, const ca_strides& st, int dtype, int B, int S, int H, int D) {
+  if (B < 0 || S < 0 || H < 0 || D <= 0) return fail(CA_ERR_SHAPE, "%s: negative or zero size", name);
+  if (B == 0 || S == 0 || H == 0) return CA_OK;
+  if (!p) return fail(CA_ERR_NULL, "%s is NULL", name);
+  const int esz = dtype == CA_BF16 ? 2 : 4;
+  if (!aligned16(p)) return fail(CA_ERR_SHAPE, "%s must be 16-byte aligned", name);
+  if (st.b < 0 || st.s < 0 || st.h < 0) return fail(CA_ERR_SHAPE, "%s: negative stride", name);
+  if (((st.b * esz) & 15) || ((st.s * esz) & 15) || ((st.h * esz) & 15))
+    return fail(CA_ERR_SHAPE, "%s: strides must keep every row 16-byte aligned", name);
+  if (H > 1 && st.h < D) return fail(CA_ERR_SHAPE, "%s: head stride %lld < D", name, (long long)st.h);
+  return CA_OK;
+}
+
+ca_status check_dtype(int dtype) {
+  if (dtype != CA_BF16 && dtype != CA_FP32) return fail(CA_ERR_DTYPE, "unknown dtype code %d", dtype);
+  return CA_OK;
+}
+
+ca_status check_head_dim(int dtype, int D) {
+  if (dtype == CA_BF16 && D != 128)
+    return fail(CA_ERR_UNSUPPORTED, "bf16 attention supports head_dim 128 only (got %d)", D);
+  if (dtype == CA_FP32 && D != 64 && D != 128)
+    return fail(CA_ERR_UNSUPPORTED, "fp32 attention supports head_dim 64 or 128 (got %d)", D);
+  return CA_OK;
+}
+
+#define CA_TRY(expr)                 \
+  do {                               \
+    ca_status _st = (expr);          \
+    if (_st != CA_OK) return _st;    \
+  } while (0)
+
+ca_status attn_common(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype, int B,
+                      int H, int Sq, int Sk, int D) {
+  CA_TRY(check_dtype(dtype));
+  CA_TRY(check_head_dim(dtype, D));
+  if (Sq < 0 || Sk < 0) return fail(CA_ERR_SHAPE, "negative sequence length");
+  CA_TRY(check_bshd("q", q, qs, dtype, B, Sq, H, D));
+  CA_TRY(check_bshd("k", k, kvs, dtype, B, Sk, H, D));
+  CA_TRY(check_bshd("v", v, kvs, dtype, B, Sk, H, D));
+  return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ca_last_error(void) { return g_err; }
+
+const char* ca_version(void) { return "0.1.0"; }
+
+ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype, int B,
+                         int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o, float* lse,
+                         void* stream) {
+  CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
+  if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
+  if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
+  if (!o || !lse) return fail(CA_ERR_NULL, "o and lse are required");
+  if (!aligned16(o)) return fail(CA_ERR_SHAPE, "o must be 16-byte aligned");
+  ctxattn::AttnArgs a{};
+  a.q = q; a.qsb = qs.b; a.qss = qs.s; a.qsh = qs.h;
+  a.k = k; a.v = v; a.ksb = kvs.b; a.kss = kvs.s; a.ksh = kvs.h;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.D = D;
+  a.scale = resolve_scale(softmax_scale, D);
+  a.sl2e = a.scale * ctxattn::kLog2e;
+  a.mask = mask;
+  a.o = o; a.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
+  return hip_status(e, "ring_attn_step launch");
+}
+
+ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, int H, int D, float* kmax_sq,
+                         int accumulate, void* stream) {
+  CA_TRY(check_dtype(dtype));
+  if (D <= 0 || D % 8) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
+  CA_TRY(check_bshd("k", k, ks, dtype, B, S, H, D));
+  if (int64_t(B) * H == 0) return hip_status(hipSuccess, "");
+  if (!kmax_sq) return fail(CA_ERR_NULL, "kmax_sq is NULL");
+  if (H > 4096) return fail(CA_ERR_UNSUPPORTED, "at most 4096 heads");
+  hipError_t e = ctxattn::launch_key_sqnorm_max(k, ks.b, ks.s, ks.h, dtype == CA_BF16, B, S, H, D, kmax_sq,
+                                                accumulate != 0, static_cast<hipStream_t>(stream));
+  return hip_status(e, "key_sqnorm_max launch");
+}
+
+ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq, int H, int D, float softmax_scale,
+                          const float* kmax_sq, float* c, void* stream) {
+  CA_TRY(check_dtype(dtype));
+  if (D <= 0 || D % 8) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
+  CA_TRY(check_bshd("q", q, qs, dtype, B, Sq, H, D));
+  if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
+  if (!kmax_sq || !c) return fail(CA_ERR_NULL, "kmax_sq and c are required");
+  hipError_t e = ctxattn::launch_const_max_bound(q, qs.b, qs.s, qs.h, dtype == CA_BF16, B, Sq, H, D,
+                                                 resolve_scale(softmax_scale, D), kmax_sq, c,
+                                                 static_cast<hipStream_t>(stream));
+  return hip_status(e, "const_max_bound launch");
+}
+
+ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs,
+                                   int dtype, int B, int H, int Sq, int Sk, int D, float softmax_scale,
+                                   const float* c, float* acc, int phase, void* o, int o_dtype, float* lse,
+                                   void* stream) {
+  CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
+  if (phase < 0 || phase > (CA_PHASE_INIT | CA_PHASE_FINAL)) return fail(CA_ERR_SHAPE, "unknown phase %d", phase);
+  if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
+  if (!c) return fail(CA_ERR_NULL, "the bound c is required");
+  const bool init = phase & CA_PHASE_INIT, final_ = phase & CA_PHASE_FINAL;
+  if (!(init && final_) && !acc) return fail(CA_ERR_NULL, "acc is required unless phase is INIT|FINAL");
+  if (acc && !aligned16(acc)) return fail(CA_ERR_SHAPE, "acc must be 16-byte aligned");
+  if (final_) {
+    if (!o) return fail(CA_ERR_NULL, "o is required on the FINAL phase");
+    CA_TRY(check_dtype(o_dtype));
+    if (!aligned16(o)) return fail(CA_ERR_SHAPE, "o must be 16-byte aligned");
+  }
+  ctxattn::AttnArgs a{};
+  a.q = q; a.qsb = qs.b; a.qss = qs.s; a.qsh = qs.h;
+  a.k = k; a.v = v; a.ksb = kvs.b; a.kss = kvs.s; a.ksh = kvs.h;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = Sk; a.D = D;
+  a.scale = resolve_scale(softmax_scale, D);
+  a.sl2e = a.scale * ctxattn::kLog2e;
+  a.mask = CA_MASK_NONE;
+  a.c = c; a.acc = acc; a.phase = phase;
+  a.o_cm = o; a.o_cm_bf16 = (o_dtype == CA_BF16); a.lse_cm = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, s);
+  return hip_status(e, "ring_attn_const_max_step launch");
+}
+
+ca_status lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t rows, int D, void* o_out,
+                    int o_dtype, float* lse_out, void* stream) {
+  if (n < 1) return fail(CA_ERR_SHAPE, "n must be >= 1 (got %d)", n);
+  if (rows < 0) return fail(CA_ERR_SHAPE, "negative rows");
+  if (D != 64 && D != 128) return fail(CA_ERR_UNSUPPORTED, "lse_merge supports D 64 or 128 (got %d)", D);
+  CA_TRY(check_dtype(o_dtype));
+  if (rows == 0) return hip_status(hipSuccess, "");
+  if (!o_parts || !lse_parts || !o_out) return fail(CA_ERR_NULL, "o_parts, lse_parts and o_out are required");
+  if (!aligned16(o_parts) || !aligned16(o_out)) return fail(CA_ERR_SHAPE, "o_parts and o_out must be 16-byte aligned");
+  const char* op = static_cast<const char*>(static_cast<const void*>(o_parts));
+  const char* oo = static_cast<const char*>(o_out);
+  const size_t in_bytes = size_t(n) * size_t(rows) * D * sizeof(float);
+  const size_t out_bytes = size_t(rows) * D * (o_dtype == CA_BF16 ? 2 : 4);
+  if (oo < op + in_bytes && op < oo + out_bytes) return fail(CA_ERR_SHAPE, "o_out overlaps o_parts");
+  hipError_t e = ctxattn::launch_lse_merge(n, o_parts, lse_parts, rows, D, o_out, o_dtype == CA_BF16, lse_out,
+                                           static_cast<hipStream_t>(stream));
+  return hip_status(e, "lse_merge launch");
+}
+
+ca_status dcp_decode_workspace_size(int B, int Hq, int D, int block_size, int max_blocks, size_t* bytes) {
+  if (!bytes) return fail(CA_ERR_NULL, "bytes is NULL");
+  if (B < 0 || Hq < 0 || D <= 0 || block_size <= 0 || max_blocks < 0) return fail(CA_ERR_SHAPE, "bad sizes");
+  *bytes = ctxattn::decode_workspace_bytes(B, Hq, D, block_size, max_blocks);
+  g_err[0] = 0;
+  return CA_OK;
+}
+
+ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                             const int32_t* local_lens, int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                             int num_blocks, float softmax_scale, float* o, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_blocks < 0 || num_blocks < 0) return fail(CA_ERR_SHAPE, "bad sizes");
+  if (D != 128) return fail(CA_ERR_UNSUPPORTED, "decode supports head_dim 128 only (got %d)", D);
+  if (block_size != 16) return fail(CA_ERR_UNSUPPORTED, "decode supports block_size 16 only (got %d)", block_size);
+  if (Hq % Hkv) return fail(CA_ERR_UNSUPPORTED, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(CA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  if (B > 65535 || Hkv > 65535) return fail(CA_ERR_UNSUPPORTED, "at most 65535 sequences and KV heads");
+  if (B == 0) return hip_status(hipSuccess, "");
+  if (!q || !o || !lse || !local_lens) return fail(CA_ERR_NULL, "q, o, lse and local_lens are required");
+  if (max_blocks > 0 && num_blocks > 0 && (!k_pool || !v_pool || !block_table))
+    return fail(CA_ERR_NULL, "k_pool, v_pool and block_table are required");
+  if (!aligned16(q) || !aligned16(o) || (k_pool && !aligned16(k_pool)) || (v_pool && !aligned16(v_pool)))
+    return fail(CA_ERR_SHAPE, "q, o, k_pool and v_pool must be 16-byte aligned");
+  const size_t need = ctxattn::decode_workspace_bytes(B, Hq, D, block_size, max_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(CA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(CA_ERR_SHAPE, "workspace must be 16-byte aligned");
+  const int64_t max_tokens = int64_t(max_blocks) * block_size;
+  const int max_splits = int((max_tokens + ctxattn::kDecodeSplitTokens - 1) / ctxattn::kDecodeSplitTokens);
+  if (max_splits > 65535) return fail(CA_ERR_UNSUPPORTED, "too many blocks per sequence");
+  ctxattn::DecodeArgs a{};
+  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.block_table = block_table; a.local_lens = local_lens;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.sl2e = resolve_scale(softmax_scale, D) * ctxattn::kLog2e;
+  a.o = o; a.lse = lse;
+  a.max_splits = max_splits;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + int64_t(B) * Hq * (max_splits > 0 ? max_splits : 1) * D;
+  hipError_t e = ctxattn::launch_dcp_decode(a, static_cast<hipStream_t>(stream));
+  return hip_status(e, "dcp_decode_partial launch");
+}
+
+ca_status kv_chunk_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v, size_t bytes, void* stream) {
+  if (bytes == 0) return hip_status(hipSuccess, "");
+  if (!dst_k || !dst_v || !src_k || !src_v) return fail(CA_ERR_NULL, "all four chunk pointers are required");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst_k, src_k, bytes, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst_v, src_v, bytes, hipMemcpyDeviceToDevice, s);
+  return hip_status(e, "kv_chunk_copy");
+}
+
+}  // extern "C"

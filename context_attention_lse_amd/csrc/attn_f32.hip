@@ -1,0 +1,168 @@
+// fp32 attention step kernels (online-max and const-max) for fp32 inputs.
+//
+// Same two methods as the bf16 path (see attn_bf16.hip), computed with fp32 vector
+// FMAs and accurate expf/logf, for inputs that are fp32 end to end: a bf16 rounding of
+// fp32 inputs would be charged to the scores. Two lanes share one query row, each
+// holding half of the head dimension; keys stream through LDS in tiles of 32.
+#include "internal.hpp"
+
+namespace ctxattn {
+namespace {
+
+constexpr int NT = 256;        // threads per workgroup
+constexpr int ROWS = NT / 2;   // query rows per workgroup
+constexpr int TK = 32;         // keys per LDS tile
+
+enum { MODE_ONLINE = 0, MODE_CONSTMAX = 1 };
+
+template <int MODE, int MASK, int D>
+__global__ __launch_bounds__(NT) void attn_step_f32(const AttnArgs a, int nqb) {
+  constexpr int DH = D / 2;
+  __shared__ __attribute__((aligned(16))) float Ks[TK][D];
+  __shared__ __attribute__((aligned(16))) float Vs[TK][D];
+
+  const int bh = blockIdx.x / nqb;
+  const int qb = blockIdx.x - bh * nqb;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  const int tid = threadIdx.x;
+  const int half = tid & 1;
+  const int i = qb * ROWS + (tid >> 1);
+  const int Sq = a.Sq, Sk = a.Sk;
+  const bool live_row = i < Sq;
+
+  float q[DH], acc[DH];
+  const float* qrow = static_cast<const float*>(a.q) + b * a.qsb + int64_t(live_row ? i : 0) * a.qss + h * a.qsh + half * DH;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    q[d] = live_row ? qrow[d] : 0.0f;
+    acc[d] = 0.0f;
+  }
+  const float* kbase = static_cast<const float*>(a.k) + b * a.ksb + h * a.ksh;
+  const float* vbase = static_cast<const float*>(a.v) + b * a.ksb + h * a.ksh;
+
+  float m = -INFINITY, l = 0.0f, c = 0.0f;
+  if (MODE == MODE_CONSTMAX && live_row) c = a.c[int64_t(bh) * Sq + i];
+
+  int kend = Sk;
+  if (MASK != CA_MASK_NONE) kend = min(Sk, qb * ROWS + ROWS);
+
+  for (int key0 = 0; key0 < kend; key0 += TK) {
+    __syncthreads();
+    for (int e = tid; e < TK * D / 4; e += NT) {
+      const int row = e / (D / 4);
+      const int col = (e - row * (D / 4)) * 4;
+      const int key = key0 + row;
+      float4 kv = make_float4(0, 0, 0, 0), vv = kv;
+      if (key < Sk) {
+        kv = *reinterpret_cast<const float4*>(kbase + key * a.kss + col);
+        vv = *reinterpret_cast<const float4*>(vbase + key * a.kss + col);
+      }
+      *reinterpret_cast<float4*>(&Ks[row][col]) = kv;
+      *reinterpret_cast<float4*>(&Vs[row][col]) = vv;
+    }
+    __syncthreads();
+
+    float s[TK];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      float part = 0.0f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) part = fmaf(q[d], Ks[j][half * DH + d], part);
+      const float full = part + __shfl_xor(part, 1);
+      const int key = key0 + j;
+      bool ok = key < Sk;
+      if (MASK == CA_MASK_CAUSAL_INCL) ok &= key <= i;
+      if (MASK == CA_MASK_CAUSAL_STRICT) ok &= key < i;
+      s[j] = ok ? full * a.scale : -INFINITY;
+      tmax = fmaxf(tmax, s[j]);
+    }
+    float mu;
+    if (MODE == MODE_ONLINE) {
+      const float m_new = fmaxf(m, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : expf(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) acc[d] *= alpha;
+      m = m_new;
+      mu = (m == -INFINITY) ? 0.0f : m;
+    } else {
+      mu = c;
+    }
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      const float p = expf(s[j] - mu);
+      l += p;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, Vs[j][half * DH + d], acc[d]);
+    }
+  }
+
+  if (!live_row) return;
+  const int64_t rowidx = int64_t(bh) * Sq + i;
+  if (MODE == MODE_ONLINE) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* orow = a.o + rowidx * D + half * DH;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) orow[d] = acc[d] * inv;
+    if (half == 0) a.lse[rowidx] = l > 0.0f ? m + logf(l) : -INFINITY;
+  } else {
+    const int64_t rows = int64_t(a.B) * a.H * Sq;
+    float* arow = a.acc ? a.acc + rowidx * D + half * DH : nullptr;
+    float sum = l;
+    if (!(a.phase & CA_PHASE_INIT)) {
+#pragma unroll
+      for (int d = 0; d < DH; ++d) acc[d] += arow[d];
+      sum += a.acc[rows * D + rowidx];
+    }
+    if (!(a.phase & CA_PHASE_FINAL)) {
+#pragma unroll
+      for (int d = 0; d < DH; ++d) arow[d] = acc[d];
+      if (half == 0) a.acc[rows * D + rowidx] = sum;
+    } else {
+      const float z = fmaxf(sum, kSumClamp);
+      const float inv = 1.0f / z;
+      if (a.o_cm_bf16) {
+        uint16_t* orow = static_cast<uint16_t*>(a.o_cm) + rowidx * D + half * DH;
+#pragma unroll
+        for (int d = 0; d < DH; d += 2) {
+          const uint32_t pk = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
+          *reinterpret_cast<uint32_t*>(orow + d) = pk;
+        }
+      } else {
+        float* orow = static_cast<float*>(a.o_cm) + rowidx * D + half * DH;
+#pragma unroll
+        for (int d = 0; d < DH; ++d) orow[d] = acc[d] * inv;
+      }
+      if (half == 0 && a.lse_cm) a.lse_cm[rowidx] = c + logf(z);
+    }
+  }
+}
+
+template <int MODE, int MASK, int D>
+hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
+  const int nqb = (a.Sq + ROWS - 1) / ROWS;
+  const int64_t nblk = int64_t(a.B) * a.H * nqb;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_step_f32<MODE, MASK, D>), dim3(unsigned(nblk)), dim3(NT), 0, s, a, nqb);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch(const AttnArgs& a, bool const_max, hipStream_t s) {
+  if (const_max) return launch_one<MODE_CONSTMAX, CA_MASK_NONE, D>(a, s);
+  switch (a.mask) {
+    case CA_MASK_CAUSAL_INCL: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_INCL, D>(a, s);
+    case CA_MASK_CAUSAL_STRICT: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_STRICT, D>(a, s);
+    default: return launch_one<MODE_ONLINE, CA_MASK_NONE, D>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const AttnArgs& a, bool const_max, hipStream_t s) {
+  return a.D == 64 ? dispatch<64>(a, const_max, s) : dispatch<128>(a, const_max, s);
+}
+
+}  // namespace ctxattn

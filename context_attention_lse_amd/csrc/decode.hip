@@ -1,0 +1,250 @@
+// DCP decode: one shard's partial attention over its paged, interleaved KV cache
+// (DCP page, "DCP Decode" compute pattern steps 3-4: the gathered query heads attend
+// the local KV shard and produce a partial output with its LSE).
+//
+// Work decomposition (bandwidth-bound: every resident K/V byte is read once):
+//  * grid (split, kv head, sequence); a split is 1024 shard-local tokens (64 blocks);
+//  * a workgroup is 4 waves; wave w streams 16 blocks of the split, two blocks per step;
+//  * the GQA group's query heads (<= 16) share each K/V block: scores are
+//    S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows = 16 tokens, cols = heads), so
+//    a block is read once for all heads of its group;
+//  * V blocks are stored d-major ([D][16] per block and head), so the P.V product
+//    O^T = V^T P^T loads its A operand with 8-byte reads and P never leaves registers;
+//  * the four waves' partials fold in LDS into one (output, LSE) per split, and a
+//    second kernel folds the splits of each sequence by the LSE rule.
+#include "internal.hpp"
+
+namespace ctxattn {
+namespace {
+
+constexpr int D = 128;
+constexpr int BS = 16;                          // tokens per cache block
+constexpr int NT = 256;
+constexpr int WAVES = NT / 64;
+constexpr int SPLIT_BLOCKS = kDecodeSplitTokens / BS;   // 64
+constexpr int WAVE_BLOCKS = SPLIT_BLOCKS / WAVES;       // 16
+constexpr float kRescaleSlack = 8.0f;
+
+struct PairRegs {
+  uint4 k[2][4];   // [block][d chunk of 32]: 8 bf16 of row (token) c16
+  uint2 v[2][8];   // [block][d block of 16]: 4 bf16 (tokens 4g..4g+3) at d = 16*db + c16
+};
+
+__device__ __forceinline__ void load_pair(PairRegs& r, const uint16_t* kp, const uint16_t* vp, int hkv, int Hkv,
+                                          const int32_t* btab, int jb0, int nblk, int num_blocks, int g, int c16) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    const int j = jb0 + bi;
+    const int64_t blk = j < nblk ? btab[j] : -1;
+    if (blk >= 0 && blk < num_blocks) {
+      const uint16_t* kb = kp + ((blk * Hkv + hkv) * BS + c16) * D + 8 * g;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = *reinterpret_cast<const uint4*>(kb + 32 * cc);
+      const uint16_t* vb = vp + ((blk * Hkv + hkv) * D + c16) * BS + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) r.v[bi][db] = *reinterpret_cast<const uint2*>(vb + 16 * BS * db);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) r.v[bi][db] = make_uint2(0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArgs a) {
+  __shared__ float s_o[WAVES][16][D];
+  __shared__ float s_m[WAVES][16];
+  __shared__ float s_l[WAVES][16];
+
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int len = min(max(a.local_lens[b], 0), a.max_blocks * BS);
+  const int split_tok0 = split * kDecodeSplitTokens;
+  if (split_tok0 >= len) return;   // workgroup-uniform: nothing resident in this split
+  const int nblk = (len + BS - 1) / BS;
+  const int G = a.Hq / a.Hkv;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  // Q fragment: head c16 of the group (zero beyond G), d = 32*cc + 8*g .. +7.
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (int64_t(b) * a.Hq + hkv * G + min(c16, G - 1)) * D + 8 * g;
+  bf16x8 qf[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    uint4 t = c16 < G ? *reinterpret_cast<const uint4*>(qh + 32 * cc) : make_uint4(0, 0, 0, 0);
+    qf[cc] = *reinterpret_cast<bf16x8*>(&t);
+  }
+
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v_pool);
+  const int32_t* btab = a.block_table + int64_t(b) * a.max_blocks;
+  const int wave_blk0 = split * SPLIT_BLOCKS + w * WAVE_BLOCKS;
+
+  floatx4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;
+  float l_part = 0.0f;
+  const float sl2e = a.sl2e;
+
+  PairRegs cur, nxt;
+  load_pair(cur, kp, vp, hkv, a.Hkv, btab, wave_blk0, nblk, a.num_blocks, g, c16);
+  for (int it = 0; it < WAVE_BLOCKS / 2; ++it) {
+    const int jb0 = wave_blk0 + 2 * it;
+    if (jb0 >= nblk) break;   // wave-uniform
+    if (it + 1 < WAVE_BLOCKS / 2) load_pair(nxt, kp, vp, hkv, a.Hkv, btab, jb0 + 2, nblk, a.num_blocks, g, c16);
+
+    floatx4 s[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      s[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        bf16x8 kf = *reinterpret_cast<bf16x8*>(&cur.k[bi][cc]);
+        s[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], s[bi], 0, 0, 0);
+      }
+    }
+    // s[bi][r]: score of head c16 against token (jb0 + bi)*16 + 4g + r
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = (jb0 + bi) * BS + 4 * g + r;
+        s[bi][r] = t < len ? s[bi][r] : -INFINITY;
+        tmax = fmaxf(tmax, s[bi][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float t2 = tmax * sl2e;
+    const bool move = t2 > m_ref + kRescaleSlack;
+    if (__any(move)) {
+      const float m_new = move ? t2 : m_ref;
+      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      m_ref = m_new;
+    }
+    const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    float p[2][4];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[bi][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bi][r], sl2e, -mu));
+        l_part += p[bi][r];
+      }
+    uint4 pk = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                          pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
+    const bf16x8 pb = *reinterpret_cast<bf16x8*>(&pk);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      uint4 vv = make_uint4(cur.v[0][db].x, cur.v[0][db].y, cur.v[1][db].x, cur.v[1][db].y);
+      const bf16x8 vf = *reinterpret_cast<bf16x8*>(&vv);
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[db], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+
+  // Row sums per head: fold the 4 token groups (lanes c16, c16+16, c16+32, c16+48).
+  float l_head = l_part + __shfl_xor(l_part, 16);
+  l_head += __shfl_xor(l_head, 32);
+  // oacc[db][r]: O^T[d = 16*db + 4*g + r][head c16] (unnormalised, reference m_ref)
+  if (c16 < G) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[w][c16][16 * db + 4 * g + r] = oacc[db][r];
+    if (g == 0) {
+      s_m[w][c16] = m_ref;
+      s_l[w][c16] = l_head;
+    }
+  }
+  __syncthreads();
+
+  // Fold the 4 waves: G heads x 128 d outputs, 8 per thread.
+  const int64_t slot0 = (int64_t(b) * a.Hq + hkv * G) * a.max_splits + split;
+  for (int e = tid; e < G * D; e += NT) {
+    const int hh = e / D;
+    const int d = e - hh * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, s_l[ww][hh] > 0.0f ? s_m[ww][hh] : -INFINITY);
+    float o = 0.0f, l = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < WAVES; ++ww) {
+        if (s_l[ww][hh] > 0.0f) {
+          const float f = exp2f(s_m[ww][hh] - M);
+          o = fmaf(f, s_o[ww][hh][d], o);
+          l = fmaf(f, s_l[ww][hh], l);
+        }
+      }
+    }
+    const int64_t slot = slot0 + int64_t(hh) * a.max_splits;
+    a.ws_o[slot * D + d] = l > 0.0f ? o / l : 0.0f;
+    if (d == 0) a.ws_lse[slot] = l > 0.0f ? (M + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// One row (sequence, query head) per D/4 lanes: fold that sequence's splits.
+__global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs a) {
+  constexpr int LPR = D / 4;
+  constexpr int RPB = NT / LPR;
+  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / LPR;
+  const int col = (threadIdx.x % LPR) * 4;
+  if (row >= int64_t(a.B) * a.Hq) return;
+  const int b = int(row / a.Hq);
+  const int len = min(max(a.local_lens[b], 0), a.max_blocks * BS);
+  const int n = (len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+  const float* lp = a.ws_lse + row * a.max_splits;
+  const float* op = a.ws_o + row * a.max_splits * D + col;
+  float M = -INFINITY;
+  for (int s = 0; s < n; ++s) M = fmaxf(M, lp[s]);
+  float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
+  float gl = -INFINITY;
+  if (M != -INFINITY) {
+    float total = 0.0f;
+    for (int s = 0; s < n; ++s) total += __expf(lp[s] - M);
+    gl = M + __logf(total);
+    for (int s = 0; s < n; ++s) {
+      const float wt = __expf(lp[s] - gl);
+      const float4 v = *reinterpret_cast<const float4*>(op + int64_t(s) * D);
+      out.x = fmaf(wt, v.x, out.x); out.y = fmaf(wt, v.y, out.y);
+      out.z = fmaf(wt, v.z, out.z); out.w = fmaf(wt, v.w, out.w);
+    }
+  }
+  *reinterpret_cast<float4*>(a.o + row * D + col) = out;
+  if (col == 0) a.lse[row] = gl;
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int Hq, int D_, int block_size, int max_blocks) {
+  const int64_t max_tokens = int64_t(max_blocks) * block_size;
+  const int64_t splits = (max_tokens + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+  const int64_t rows = int64_t(B) * Hq * (splits > 0 ? splits : 1);
+  return size_t(rows) * (size_t(D_) + 1) * sizeof(float);
+}
+
+hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  if (a.max_splits > 0) {
+    hipLaunchKernelGGL(dcp_decode_split_kernel, dim3(a.max_splits, a.Hkv, a.B), dim3(NT), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  constexpr int RPB = NT / (D / 4);
+  const int64_t rows = int64_t(a.B) * a.Hq;
+  hipLaunchKernelGGL(dcp_decode_combine_kernel, dim3(unsigned((rows + RPB - 1) / RPB)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ctxattn

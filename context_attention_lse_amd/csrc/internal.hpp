@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP sources of libctxattn (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ctxattn.h"
+
+namespace ctxattn {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSumClamp = 1e-37f;   // row-sum floor of the const-max normalisation
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even pack of two floats into two bf16 (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  floatx2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return *reinterpret_cast<uint32_t*>(&b);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Maps a launch-order workgroup id to a logical work item so that consecutive
+// logical items land on the same XCD (workgroups are dealt round-robin over the
+// 8 XCDs). The grid is padded to a multiple of 8; padded ids return -1.
+__device__ __forceinline__ int xcd_logical_id(int wg, int grid, int nwork) {
+  const int per = grid >> 3;
+  const int logical = (wg & 7) * per + (wg >> 3);
+  return logical < nwork ? logical : -1;
+}
+
+__host__ __device__ inline int round_up8(int n) { return (n + 7) & ~7; }
+
+// ---------------------------------------------------------------- launch descriptors
+struct AttnArgs {
+  const void* q;
+  int64_t qsb, qss, qsh;
+  const void* k;
+  const void* v;
+  int64_t ksb, kss, ksh;
+  int B, H, Sq, Sk, D;
+  float scale;      // softmax scale
+  float sl2e;       // scale * log2(e)
+  int mask;         // ca_mask
+  // online-max outputs
+  float* o;
+  float* lse;
+  // const-max inputs/outputs
+  const float* c;
+  float* acc;
+  int phase;
+  void* o_cm;
+  int o_cm_bf16;
+  float* lse_cm;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, bool const_max, hipStream_t s);
+hipError_t launch_lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t rows,
+                            int D, void* o_out, int o_bf16, float* lse_out, hipStream_t s);
+hipError_t launch_key_sqnorm_max(const void* k, int64_t sb, int64_t ss, int64_t sh, bool bf16,
+                                 int B, int S, int H, int D, float* kmax_sq, bool accumulate,
+                                 hipStream_t s);
+hipError_t launch_const_max_bound(const void* q, int64_t sb, int64_t ss, int64_t sh, bool bf16,
+                                  int B, int Sq, int H, int D, float scale, const float* kmax_sq,
+                                  float* c, hipStream_t s);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* local_lens;
+  int B, Hq, Hkv, D, block_size, max_blocks, num_blocks;
+  float sl2e;
+  float* o;
+  float* lse;
+  float* ws_o;      // [B, Hq, max_splits, D]
+  float* ws_lse;    // [B, Hq, max_splits]
+  int max_splits;
+};
+
+constexpr int kDecodeSplitTokens = 1024;   // tokens per decode split (64 blocks of 16)
+size_t decode_workspace_bytes(int B, int Hq, int D, int block_size, int max_blocks);
+hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace ctxattn

@@ -1,0 +1,189 @@
+"""One rank's ring attention on one GPU: resident queries, K/V chunks delivered step by
+step, partials merged by LSE (or folded by the const-max rule).
+
+The ring schedule follows "Kernel reference: ring_attention_const_max_fwd" (Overview
+figure and Implementation, "The ring loop"): step 0 uses the rank's own K/V, step s
+uses the chunk of rank r - s (mod cp); the hop for step s + depth is launched before
+step s computes, into one of depth + 1 rotating buffers. On one GPU the other ranks'
+chunks sit in a pool in HBM and each hop is a device copy (kv_chunk_copy) on a copy
+stream, ordered against the compute stream by events.
+
+Striped sharding and its causal mask follow "Sharding the Input" (Striped Attention):
+token t lives on rank t mod cp at local index t div cp, so key (j, rank r') is visible
+to query (i, rank r) iff j*cp + r' <= i*cp + r, i.e. j <= i when r' <= r and j < i
+otherwise: one of two triangular masks per step.
+
+This module only orders library calls; every byte of arithmetic runs in libctxattn.
+"""
+
+import torch
+
+from . import api
+
+LAYOUTS = ("contiguous", "striped")
+
+
+def check_divisible(S: int, cp: int) -> None:
+    """Sequence length must divide by the ring size (context-parallelism page,
+    sequence sharding); the error names both numbers."""
+    if cp <= 0:
+        raise ValueError(f"cp must be positive, got {cp}")
+    if S % cp:
+        raise ValueError(f"Sequence length {S} is not divisible by cp_size {cp}.")
+
+
+def ring_source_rank(rank: int, step: int, cp: int) -> int:
+    """Rank whose K/V chunk rank ``rank`` holds at ring step ``step``."""
+    return (rank - step) % cp
+
+
+def shard(x: torch.Tensor, cp: int, rank: int, layout: str) -> torch.Tensor:
+    """Rank ``rank``'s tokens of a [B, S, H, D] tensor as a (possibly strided) view."""
+    check_divisible(x.shape[1], cp)
+    if layout == "contiguous":
+        n = x.shape[1] // cp
+        return x[:, rank * n:(rank + 1) * n]
+    if layout == "striped":
+        return x[:, rank::cp]
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def chunk_pool(x: torch.Tensor, cp: int, layout: str) -> torch.Tensor:
+    """Every rank's shard, each contiguous: [cp, B, S/cp, H, D] (the peers' HBM)."""
+    return torch.stack([shard(x, cp, r, layout).contiguous() for r in range(cp)], 0)
+
+
+def step_mask(layout: str, causal: bool, query_rank: int, source_rank: int):
+    """Mask of one step, or None when causality hides the whole chunk."""
+    if not causal:
+        return "none"
+    if layout == "striped":
+        return "causal_incl" if source_rank <= query_rank else "causal_strict"
+    # contiguous: earlier chunks fully visible, own chunk triangular, later chunks hidden
+    if source_rank < query_rank:
+        return "none"
+    if source_rank == query_rank:
+        return "causal_incl"
+    return None
+
+
+class RingPass:
+    """One rank's share of ring attention: q resident, cp chunks arriving one per step.
+
+    variant "online": every step emits a partial (o_s, lse_s) with ring_attn_step and
+                      the partials are merged once with lse_merge;
+    variant "constmax": the bound is built from every chunk's key norms (the ring's
+                      all_reduce(max) becomes a max-fold), then every step adds into one
+                      fp32 accumulator and the last step normalises.
+    """
+
+    def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
+                 scale=None, prefetch_depth=1, out_dtype=torch.float32, copy_stream=None):
+        if variant not in ("online", "constmax"):
+            raise ValueError(f"unknown variant {variant!r}")
+        if variant == "constmax" and causal:
+            raise ValueError("the const-max method is non-causal")
+        if layout not in LAYOUTS:
+            raise ValueError(f"unknown layout {layout!r}")
+        self.cp = k_pool.shape[0]
+        if not (0 <= rank < self.cp):
+            raise ValueError(f"rank {rank} outside ring of {self.cp}")
+        self.q, self.k_pool, self.v_pool = q, k_pool, v_pool
+        self.rank, self.layout, self.causal, self.variant = rank, layout, causal, variant
+        self.scale = scale
+        self.out_dtype = out_dtype
+        self.depth = max(1, min(int(prefetch_depth), max(1, self.cp - 1)))
+        self.nbuf = self.depth + 1
+        B, Sq, H, D = q.shape
+        chunk_shape = tuple(k_pool.shape[1:])
+        dev = q.device
+        self.kbuf = [torch.empty(chunk_shape, dtype=k_pool.dtype, device=dev) for _ in range(self.nbuf)]
+        self.vbuf = [torch.empty(chunk_shape, dtype=v_pool.dtype, device=dev) for _ in range(self.nbuf)]
+        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device=dev)
+        self.copied = [torch.cuda.Event() for _ in range(self.cp)]
+        self.consumed = [torch.cuda.Event() for _ in range(self.cp)]
+        self.masks = [step_mask(layout, causal, rank, ring_source_rank(rank, s, self.cp)) for s in range(self.cp)]
+        self.live_steps = [s for s in range(self.cp) if self.masks[s] is not None]
+        assert self.live_steps, "a rank always sees its own chunk"
+        if variant == "online":
+            n = len(self.live_steps)
+            self.o_parts = torch.empty((max(n, 1), B, H, Sq, D), dtype=torch.float32, device=dev)
+            self.lse_parts = torch.empty((max(n, 1), B, H, Sq), dtype=torch.float32, device=dev)
+        else:
+            self.kmax = torch.empty((B, H), dtype=torch.float32, device=dev)
+            self.c = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+            self.acc = torch.empty(api.const_max_acc_size(B, H, Sq, D), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        self.step_events = None
+
+    def _chunk(self, step):
+        if step == 0:
+            return self.k_pool[self.rank], self.v_pool[self.rank]
+        j = (step - 1) % self.nbuf
+        return self.kbuf[j], self.vbuf[j]
+
+    def _issue_copy(self, step):
+        src = ring_source_rank(self.rank, step, self.cp)
+        kd, vd = self._chunk(step)
+        with torch.cuda.stream(self.copy_stream):
+            api.kv_chunk_copy(kd, vd, self.k_pool[src], self.v_pool[src])
+            self.copied[step].record(self.copy_stream)
+
+    def prologue(self):
+        """const-max bound: per-head max key norm over the whole ring, then c per row."""
+        for r in range(self.cp):
+            api.key_sqnorm_max(self.k_pool[r], self.kmax, accumulate=r > 0)
+        api.const_max_bound(self.q, self.kmax, scale=self.scale, out=self.c)
+
+    def run(self, timing_events=None):
+        """Runs the ring on the current stream; returns (out [B,H,Sq,D], lse [B,H,Sq]).
+        ``timing_events``: optional list of cp (start, end) event pairs recorded around
+        each step's kernel on the compute stream."""
+        cs = torch.cuda.current_stream()
+        cp = self.cp
+        if self.variant == "constmax":
+            self.prologue()
+        self.copy_stream.wait_stream(cs)
+        for t in range(1, min(self.depth, cp - 1) + 1):
+            self._issue_copy(t)
+        slot = 0
+        for s in range(cp):
+            t = s + self.depth
+            if s >= 1 and t < cp:
+                self.copy_stream.wait_event(self.consumed[s - 1])
+                self._issue_copy(t)
+            if s >= 1:
+                cs.wait_event(self.copied[s])
+            k, v = self._chunk(s)
+            if timing_events is not None:
+                timing_events[s][0].record(cs)
+            if self.variant == "online":
+                if self.masks[s] is not None:
+                    api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s],
+                                       out=self.o_parts[slot], lse=self.lse_parts[slot])
+                    slot += 1
+            else:
+                phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
+                api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out, lse=self.lse,
+                                             scale=self.scale)
+            if timing_events is not None:
+                timing_events[s][1].record(cs)
+            self.consumed[s].record(cs)
+        if self.variant == "online":
+            api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
+        # the copy stream must not run ahead into the next call's buffers
+        cs.wait_stream(self.copy_stream)
+        return self.out, self.lse
+
+
+def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous", causal=False,
+                   variant="online", scale=None, prefetch_depth=1):
+    """Convenience: rank ``rank``'s output for global [B, S, H, D] inputs."""
+    check_divisible(q_global.shape[1], cp)
+    q = shard(q_global, cp, rank, layout)
+    kp = chunk_pool(k_global, cp, layout)
+    vp = chunk_pool(v_global, cp, layout)
+    rp = RingPass(q, kp, vp, rank, layout=layout, causal=causal, variant=variant, scale=scale,
+                  prefetch_depth=prefetch_depth)
+    return rp.run()

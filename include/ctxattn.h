@@ -1,0 +1,225 @@
+/*
+ * ctxattn.h -- C ABI of the MI355X (gfx950) context-parallel attention core.
+ *
+ * One rank's share of context-parallel attention: a resident query shard attends
+ * a sequence of K/V chunks as a ring delivers them, each step emitting a partial
+ * output plus per-row log-sum-exp (LSE), and partials are combined by the
+ * LSE-corrected merge. The same merge combines DCP decode shards.
+ *
+ * Sources (pages as published):
+ *  - "Kernel reference: ring_attention_const_max_fwd const-max ring attention"
+ *    (AWS Neuron docs): Overview (ring schedule), Design (bound, pure-addition
+ *    fold), Implementation (norms, global key max, accumulate then normalise,
+ *    1e-37 clamp), Interface (q/k/v token-major [b, seqlen, h, d], o [b, h, seqlen, d],
+ *    softmax_scale default 1/sqrt(d), lse = c + log(sum_exp)).
+ *  - "DCP (Decode Context Parallelism)" (AWS Neuron docs): DCP Decode compute
+ *    pattern (local attention, partial LSE, weight = exp(local_lse - global_lse)),
+ *    local_filled computation, slot mapping (position -> (pos // I) % W).
+ *  - "Sharding the Input" (iop.systems): ring attention, striped attention.
+ *
+ * Conventions for every entry point:
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them, and keeps no state between calls.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *    Only argument validation and the launch are synchronous; kernel faults
+ *    surface at the caller's next synchronisation.
+ *  - Return CA_OK or an error status. On error nothing is launched, and
+ *    ca_last_error() returns a message for the calling thread.
+ *  - Unsupported shapes or types return CA_ERR_UNSUPPORTED; there is no silent
+ *    fallback to another path (the kernel reference page, Best practices: the
+ *    only correct path gets no selector, violations fail loudly).
+ *  - softmax_scale <= 0 selects 1/sqrt(D).
+ *  - LSE values are natural logarithms; a row that sees no key has
+ *    lse = -inf and output 0.
+ *  - A [B, S, H, D] input is described by element strides (b, s, h); the D axis
+ *    must be contiguous and every row 16-byte aligned.
+ */
+#ifndef CTXATTN_H
+#define CTXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CA_OK = 0,
+  CA_ERR_NULL = 1,         /* a required pointer is NULL */
+  CA_ERR_SHAPE = 2,        /* sizes or strides are inconsistent */
+  CA_ERR_DTYPE = 3,        /* unknown dtype code */
+  CA_ERR_UNSUPPORTED = 4,  /* valid request this library does not implement */
+  CA_ERR_WORKSPACE = 5,    /* workspace missing or too small */
+  CA_ERR_HIP = 6           /* the HIP runtime reported an error */
+} ca_status;
+
+typedef enum { CA_BF16 = 0, CA_FP32 = 1 } ca_dtype;
+
+/* Key visibility inside one step, on LOCAL indices i (query) and j (key). Under a
+ * striped ring (token t on rank t mod cp, local index t div cp), global causality
+ * reduces per step to INCL when the chunk's source rank <= the query rank, and to
+ * STRICT otherwise. */
+typedef enum {
+  CA_MASK_NONE = 0,
+  CA_MASK_CAUSAL_INCL = 1,   /* key j visible iff j <= i */
+  CA_MASK_CAUSAL_STRICT = 2  /* key j visible iff j <  i */
+} ca_mask;
+
+/* Phase bits of the const-max step. */
+enum { CA_PHASE_ACCUMULATE = 0, CA_PHASE_INIT = 1, CA_PHASE_FINAL = 2 };
+
+/* Element strides of a [B, S, H, D] tensor (D stride is 1). */
+typedef struct {
+  int64_t b;
+  int64_t s;
+  int64_t h;
+} ca_strides;
+
+/*
+ * ring_attn_step -- online-max (flash-style) attention of the resident query shard
+ * against ONE K/V chunk, emitting the chunk's partial output and per-row LSE.
+ * Source: kernel reference page, Design "Dropping the online max buys a better
+ * layout" (the online-max path keeps a running row max, row sum and a rescaled
+ * accumulator); "Sharding the Input", ring attention (blockwise attention per
+ * K/V block).
+ *
+ *   q      [B, Sq, H, D] bf16 or fp32 (dtype), strides q_strides
+ *   k, v   [B, Sk, H, D] same dtype, strides kv_strides (shared by k and v)
+ *   mask   ca_mask on local indices
+ *   o      OUT [B, H, Sq, D] fp32, contiguous: softmax(s) @ v over visible keys
+ *   lse    OUT [B, H, Sq] fp32, contiguous: log sum_j exp(scale * q_i . k_j)
+ * Supported: D in {64, 128} (fp32), D == 128 (bf16); MHA (same H for q and kv).
+ * Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
+ * CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+ca_status ring_attn_step(const void* q, ca_strides q_strides,
+                         const void* k, const void* v, ca_strides kv_strides,
+                         int dtype, int B, int H, int Sq, int Sk, int D,
+                         float softmax_scale, int mask,
+                         float* o, float* lse, void* stream);
+
+/*
+ * key_sqnorm_max -- per (b, h) maximum over the chunk's keys of |k_j|^2.
+ * Source: kernel reference page, Implementation "Transpose prologue with fused
+ * norms" (K folds per-token |k|^2 into a running max, one value per head) and
+ * "Global key max" (all_reduce(max) across the ring). On one device the
+ * all-reduce is the max-fold over chunks: accumulate = 0 overwrites kmax_sq with
+ * this chunk's maxima, accumulate = 1 folds them into kmax_sq by max.
+ *   k        [B, S, H, D], strides ks
+ *   kmax_sq  IN/OUT [B, H] fp32
+ */
+ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, int H, int D,
+                         float* kmax_sq, int accumulate, void* stream);
+
+/*
+ * const_max_bound -- per query row bound c_i = scale * |q_i| * sqrt(kmax_sq[b, h]).
+ * Source: kernel reference page, Design "Picking a max that is safe without
+ * measuring it" (Cauchy-Schwarz: c_i >= every score of row i) and Implementation
+ * "Assembling the bound" (one square root of scale^2 * kmax_sq * |q_i|^2).
+ *   q        [B, Sq, H, D], strides qs
+ *   kmax_sq  [B, H] fp32 (from key_sqnorm_max over every chunk of the ring)
+ *   c        OUT [B, H, Sq] fp32
+ */
+ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq, int H, int D,
+                          float softmax_scale, const float* kmax_sq, float* c, void* stream);
+
+/*
+ * ring_attn_const_max_step -- one ring step of const-max attention: p = exp(s - c_i)
+ * with the fixed per-row bound, folded into a running unnormalised accumulator by
+ * pure addition; the FINAL step normalises once.
+ * Source: kernel reference page, Design "A static bound makes the ring reduction
+ * pure addition", Implementation "Accumulate, then normalize once" (fp32
+ * accumulator, row sum clamped to 1e-37 before the single division), Interface
+ * (lse = c + log(sum_exp); non-causal, MHA).
+ *
+ *   q, k, v   as ring_attn_step (no mask: the method is non-causal)
+ *   c         [B, H, Sq] fp32 bound from const_max_bound (identical for every step)
+ *   acc       IN/OUT fp32 accumulator: [B, H, Sq, D] unnormalised output followed
+ *             by [B, H, Sq] row sums (B*H*Sq*(D+1) floats). May be NULL when
+ *             phase == INIT|FINAL (a single chunk).
+ *   phase     CA_PHASE_INIT: first chunk (acc is overwritten, not read);
+ *             CA_PHASE_FINAL: last chunk (o and lse are written, acc is not);
+ *             CA_PHASE_ACCUMULATE (0): any middle chunk.
+ *   o         OUT (FINAL only) [B, H, Sq, D], o_dtype CA_FP32 or CA_BF16:
+ *             acc_o / max(acc_sum, 1e-37)
+ *   lse       OUT (FINAL only, nullable) [B, H, Sq] fp32: c + log(max(acc_sum, 1e-37))
+ * Supported: as ring_attn_step.
+ */
+ca_status ring_attn_const_max_step(const void* q, ca_strides q_strides,
+                                   const void* k, const void* v, ca_strides kv_strides,
+                                   int dtype, int B, int H, int Sq, int Sk, int D,
+                                   float softmax_scale, const float* c, float* acc, int phase,
+                                   void* o, int o_dtype, float* lse, void* stream);
+
+/*
+ * lse_merge -- LSE-corrected merge of n partial attention results.
+ * Source: DCP page, DCP Decode compute pattern steps 4-7: gather the partial LSEs,
+ * global_lse = log sum_s exp(lse_s), weight_s = exp(lse_s - global_lse), output =
+ * sum_s weight_s * o_s. Also the fold of ring-step partials ("Sharding the Input",
+ * ring attention; kernel reference page, Design: online-softmax ring bookkeeping).
+ *
+ *   o_parts    [n, rows, D] fp32, contiguous (partial s at o_parts + s*rows*D)
+ *   lse_parts  [n, rows] fp32 (-inf marks an empty partial; it weighs 0)
+ *   o_out      OUT [rows, D], o_dtype CA_FP32 or CA_BF16 (may not alias o_parts)
+ *   lse_out    OUT [rows] fp32 global LSE, nullable
+ * All partials -inf -> output 0 and lse -inf. Requires n >= 1, D % 4 == 0.
+ */
+ca_status lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t rows, int D,
+                    void* o_out, int o_dtype, float* lse_out, void* stream);
+
+/*
+ * dcp_decode_partial -- one DCP shard's decode attention: every query head of every
+ * sequence attends the tokens resident in this shard's paged KV cache, giving the
+ * shard's partial output and LSE (to be merged across shards with lse_merge).
+ * Source: DCP page, DCP Decode compute pattern steps 3-4 (gathered Q against the
+ * local KV shard, partial LSE), local_filled computation (tokens resident per
+ * shard), slot mapping (blocks of interleave_size tokens dealt round-robin).
+ *
+ *   q            [B, Hq, D] bf16 contiguous (one decode token per sequence)
+ *   k_pool       [num_blocks, Hkv, block_size, D] bf16: token-major blocks
+ *   v_pool       [num_blocks, Hkv, D, block_size] bf16: d-major blocks (this
+ *                library's V cache layout: each block's values stored transposed
+ *                so that a block feeds the P.V matrix product without a shuffle)
+ *   block_table  [B, max_blocks] int32: physical block of the sequence's shard-local
+ *                block j (shard-local token t is slot t % block_size of block
+ *                t / block_size); entries past the sequence's blocks are ignored;
+ *                an id outside [0, num_blocks) reads as an all-zero block
+ *   num_blocks   blocks in k_pool and v_pool
+ *   local_lens   [B] int32: tokens of each sequence resident on this shard
+ *                (local_filled); values are clamped to [0, max_blocks * block_size]
+ *   o            OUT [B, Hq, D] fp32 partial output; lse OUT [B, Hq] fp32
+ *   workspace    device scratch of at least dcp_decode_workspace_size() bytes
+ * Query head h uses KV head h / (Hq / Hkv). Supported: D == 128, block_size == 16,
+ * Hq % Hkv == 0, Hq / Hkv <= 16. A sequence with local_lens 0 yields o = 0, lse = -inf.
+ */
+ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, const int32_t* local_lens,
+                             int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                             int num_blocks, float softmax_scale, float* o, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace dcp_decode_partial needs for these sizes. */
+ca_status dcp_decode_workspace_size(int B, int Hq, int D, int block_size, int max_blocks,
+                                    size_t* bytes);
+
+/*
+ * kv_chunk_copy -- the ring's K/V hop on one device: asynchronous device-to-device
+ * copies of one K chunk and one V chunk (bytes each) on `stream`.
+ * Source: kernel reference page, Implementation "The ring loop" (rotating K/V
+ * buffers, the next hop launched while the current step computes).
+ */
+ca_status kv_chunk_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                        size_t bytes, void* stream);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* ca_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* ca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CTXATTN_H */

@@ -1,0 +1,73 @@
+"""The C ABI without a GPU: the built library loads, exports every entry point that
+include/ctxattn.h declares, and rejects bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from context_attention_lse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ctxattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libctxattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_error_string():
+    lib = _lib.load()
+    assert lib.ca_version().decode() == "0.1.0"
+    assert isinstance(lib.ca_last_error(), bytes)
+
+
+def _fake(n=0x1000):
+    return ctypes.c_void_p(n)   # never dereferenced: validation fails first
+
+
+def test_rejections_without_gpu():
+    lib = _lib.load()
+    st = _lib.ca_strides(0, 128, 0)
+    # unknown dtype
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, 9, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_DTYPE
+    # bf16 head_dim other than 128
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 96, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_UNSUPPORTED
+    assert b"128" in lib.ca_last_error()
+    # unknown mask
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 7, _fake(), _fake(), None) == _lib.CA_ERR_UNSUPPORTED
+    # NULL inputs
+    assert lib.ring_attn_step(None, st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_NULL
+    # misaligned q
+    assert lib.ring_attn_step(_fake(0x1002), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_SHAPE
+    # empty query shard is a no-op success
+    assert lib.ring_attn_step(None, st, None, None, st, _lib.CA_BF16, 1, 1, 0, 0, 128, 0.0, 0, None, None, None) == _lib.CA_OK
+    # const-max: middle phase without an accumulator
+    assert lib.ring_attn_const_max_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, _fake(), None, 0, None, 0, None, None) == _lib.CA_ERR_NULL
+    # merge: n = 0, unsupported D, overlapping output
+    assert lib.lse_merge(0, _fake(), _fake(), 4, 128, _fake(0x9000), 1, None, None) == _lib.CA_ERR_SHAPE
+    assert lib.lse_merge(2, _fake(), _fake(), 4, 96, _fake(0x9000), 1, None, None) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.lse_merge(2, _fake(0x1000), _fake(), 4, 128, _fake(0x1400), 1, None, None) == _lib.CA_ERR_SHAPE
+    # decode: GQA group above 16, wrong block size, small workspace
+    args = (_fake(), _fake(), _fake(), _fake(), _fake())
+    assert lib.dcp_decode_partial(*args, 2, 64, 2, 128, 16, 8, 100, 0.0, _fake(), _fake(), _fake(), 1 << 30, None) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.dcp_decode_partial(*args, 2, 64, 8, 128, 32, 8, 100, 0.0, _fake(), _fake(), _fake(), 1 << 30, None) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.dcp_decode_partial(*args, 2, 64, 8, 128, 16, 8, 100, 0.0, _fake(), _fake(), _fake(), 16, None) == _lib.CA_ERR_WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert lib.dcp_decode_workspace_size(32, 64, 128, 16, 4096, ctypes.byref(n)) == _lib.CA_OK
+    assert n.value == 32 * 64 * 64 * 129 * 4   # 64 splits of 1024 tokens

@@ -1,0 +1,321 @@
+"""HIP path vs the fp64 oracle, element by element, at sizes that span several tiles
+and ragged tails; plus the edge cases (empty chunks, empty shards, fully masked rows,
+const-max clamp collapse). All calls go through the C ABI via the binding."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL_LSE, TOL_O, check, max_err, say, to_np
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import context_attention_lse_amd as ca
+    ca._lib.load()   # loud failure if the library is missing
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+def _ca():
+    import context_attention_lse_amd as ca
+    return ca
+
+
+def _inputs(dev, B, S, H, D, dtype, seed, extra_heads=1):
+    """Token-major [B, S, H, D] views with a non-trivial head stride (H+extra heads stored)."""
+    dt = gen.torch_dtype(dtype)
+    full = [gen.normal((B, S, H + extra_heads, D), seed + i, dev, dt) for i in range(3)]
+    return [f[:, :, :H] for f in full]
+
+
+def _allowed(mask, Sq, Sk):
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    if mask == "causal_incl":
+        return j <= i
+    if mask == "causal_strict":
+        return j < i
+    return None
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64), ("fp32", 128)])
+@pytest.mark.parametrize("mask,Sq,Sk", [("none", 300, 200), ("none", 129, 1), ("causal_incl", 300, 300),
+                                        ("causal_strict", 300, 300)])
+def test_step_partial_matches_oracle(dev, dtype, D, mask, Sq, Sk):
+    ca = _ca()
+    B, H = 2, 3
+    say(f"step dtype={dtype} D={D} mask={mask} Sq={Sq} Sk={Sk}")
+    q, _, _ = _inputs(dev, B, Sq, H, D, dtype, 100)
+    _, k, v = _inputs(dev, B, Sk, H, D, dtype, 200)
+    o, l = ca.ring_attn_step(q, k, v, mask=mask)
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(D)
+    ro, rl = oracle.attention_heads(q, k, v, scale, allowed=_allowed(mask, Sq, Sk))
+    check("step", o, l, ro, rl)
+    if mask == "causal_strict":
+        assert np.all(to_np(l)[:, :, 0] == -np.inf) and np.all(to_np(o)[:, :, 0] == 0)
+
+
+def test_step_explicit_scale_and_empty_chunk(dev):
+    ca = _ca()
+    q, k, v = _inputs(dev, 1, 70, 2, 128, "bf16", 300)
+    o, l = ca.ring_attn_step(q, k, v, scale=0.05)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_heads(q, k, v, 0.05)
+    check("scale=0.05", o, l, ro, rl)
+    o, l = ca.ring_attn_step(q, k[:, :0], v[:, :0])
+    torch.cuda.synchronize()
+    assert np.all(to_np(l) == -np.inf) and np.all(to_np(o) == 0)
+
+
+def test_step_rejects_bad_arguments(dev):
+    ca = _ca()
+    q, k, v = _inputs(dev, 1, 16, 2, 128, "bf16", 310)
+    with pytest.raises(ca.CtxAttnError):
+        ca.ring_attn_step(q[..., :64].contiguous(), k[..., :64].contiguous(), v[..., :64].contiguous())
+    with pytest.raises(ca.CtxAttnError):
+        ca.ring_attn_step(q, k, v, mask=5)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_const_max_bound_matches_oracle(dev, dtype, D):
+    ca = _ca()
+    q, k, _ = _inputs(dev, 2, 150, 3, D, dtype, 400)
+    chunks = [k[:, :40], k[:, 40:41], k[:, 41:]]
+    km = None
+    for r, kc in enumerate(chunks):
+        km = ca.key_sqnorm_max(kc, km, accumulate=r > 0)
+    c = ca.const_max_bound(q, km)
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(D)
+    for b in range(2):
+        for h in range(3):
+            rc, rk = oracle.const_max_bound(q[b, :, h], [kc[b, :, h] for kc in chunks], scale)
+            assert abs(float(km[b, h]) - rk) <= 1e-5 * rk
+            assert np.allclose(to_np(c[b, h]), rc, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_const_max_steps_match_oracle(dev, dtype, D, out_dtype):
+    ca = _ca()
+    say(f"const-max steps dtype={dtype} D={D} out={out_dtype}")
+    B, H, Sq = 1, 3, 260
+    q, _, _ = _inputs(dev, B, Sq, H, D, dtype, 500)
+    _, k, v = _inputs(dev, B, 405, H, D, dtype, 600)
+    cuts = [0, 200, 277, 405]
+    ks = [k[:, a:b] for a, b in zip(cuts, cuts[1:])]
+    vs = [v[:, a:b] for a, b in zip(cuts, cuts[1:])]
+    km = None
+    for r, kc in enumerate(ks):
+        km = ca.key_sqnorm_max(kc, km, accumulate=r > 0)
+    c = ca.const_max_bound(q, km)
+    acc = torch.empty(ca.const_max_acc_size(B, H, Sq, D), dtype=torch.float32, device=dev)
+    odt = gen.torch_dtype(out_dtype)
+    o = l = None
+    for s in range(3):
+        phase = (1 if s == 0 else 0) | (2 if s == 2 else 0)
+        res = ca.ring_attn_const_max_step(q, ks[s], vs[s], c, acc, phase, out_dtype=odt)
+        if res is not None:
+            o, l = res
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(D)
+    ro = np.zeros((B, H, Sq, D)); rl = np.zeros((B, H, Sq))
+    eo_ = np.zeros((B, H, Sq, D)); el_ = np.zeros((B, H, Sq))
+    for h in range(H):
+        ro[0, h], rl[0, h], _ = oracle.const_max(q[0, :, h], [x[0, :, h] for x in ks], [x[0, :, h] for x in vs], scale)
+        eo_[0, h], el_[0, h] = oracle.attention(q[0, :, h], k[0, :, h], v[0, :, h], scale)
+    check("const-max vs oracle const_max", o, l, ro, rl)
+    check("const-max vs exact attention", o, l, eo_, el_)
+
+
+def test_const_max_single_chunk_without_accumulator(dev):
+    ca = _ca()
+    q, k, v = _inputs(dev, 1, 100, 2, 128, "bf16", 700)
+    km = ca.key_sqnorm_max(k)
+    c = ca.const_max_bound(q, km)
+    o, l = ca.ring_attn_const_max_step(q, k, v, c, None, 3)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_heads(q, k, v, oracle.default_scale(128))
+    check("const-max INIT|FINAL", o, l, ro, rl)
+
+
+def test_const_max_sink_collapse_follows_the_clamp(dev):
+    """A planted key sink inflates max|k|: rows whose bound overshoots by ~100+ nats
+    collapse onto the 1e-37 clamp exactly as the oracle's const-max emulation predicts
+    (the page's documented failure), while rows under ~60 nats stay exact."""
+    ca = _ca()
+    D, Sq, Sk = 128, 64, 256
+    scale = oracle.default_scale(D)
+    g = torch.Generator().manual_seed(9)
+    q = torch.zeros((1, Sq, 1, D))
+    alpha = torch.cat([torch.linspace(2.0, 6.0, Sq // 2), torch.linspace(22.0, 30.0, Sq // 2)])
+    q[0, :, 0, 0] = alpha
+    k = torch.randn((1, Sk, 1, D), generator=g) * 0.5
+    k[0, 7, 0, :] = 0.0
+    k[0, 7, 0, 1] = 64.0                        # the sink: orthogonal to every query
+    v = torch.randn((1, Sk, 1, D), generator=g)
+    q, k, v = (x.to(torch.bfloat16).to(dev) for x in (q, k, v))
+    km = ca.key_sqnorm_max(k)
+    c = ca.const_max_bound(q, km)
+    o, l = ca.ring_attn_const_max_step(q, k, v, c, None, 3)
+    torch.cuda.synchronize()
+    ro, rl, rc = oracle.const_max(q[0, :, 0], [k[0, :, 0]], [v[0, :, 0]], scale)
+    eo, el = oracle.attention(q[0, :, 0], k[0, :, 0], v[0, :, 0], scale)
+    overshoot = rc - el + np.log(Sk)   # >= c - max score
+    check("sink: gpu vs oracle const_max", o[0, 0], l[0, 0], ro, rl)
+    collapsed = np.abs(rl - el) > 1.0       # clamped rows: lse = c - 85.2, far from exact
+    assert collapsed[Sq // 2:].all() and not collapsed[: Sq // 2].any(), overshoot
+    assert max_err(o[0, 0, : Sq // 2], eo[: Sq // 2]) <= TOL_O
+
+
+def test_lse_merge_matches_oracle(dev):
+    ca = _ca()
+    n, rows, D = 5, 1000, 128
+    g = torch.Generator().manual_seed(3)
+    o = torch.randn((n, rows, D), generator=g)
+    lse = torch.randn((n, rows), generator=g) * 4 + 2
+    lse[1, ::7] = -math.inf
+    lse[:, 5] = -math.inf          # a row with no partial at all
+    lse[2, 9] = 900.0              # huge values must not overflow
+    lse[3, 9] = 899.0
+    ro, rl = oracle.merge_lse(list(o.double().numpy()), list(lse.double().numpy()))
+    og, lg = ca.lse_merge(o.to(dev), lse.to(dev))
+    torch.cuda.synchronize()
+    check("merge fp32", og, lg, ro, rl, tol_o=2e-5, tol_lse=2e-5)
+    ob, lb = ca.lse_merge(o.to(dev), lse.to(dev), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check("merge bf16 out", ob, lb, ro, rl)
+    o1, l1 = ca.lse_merge(o[:1].to(dev), lse[:1].to(dev))
+    torch.cuda.synchronize()
+    check("merge n=1", o1, l1, *oracle.merge_lse([o[0].double().numpy()], [lse[0].double().numpy()]),
+          tol_o=1e-6, tol_lse=1e-6)
+
+
+# ---------------------------------------------------------------- ring passes
+
+def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=None):
+    ca = _ca()
+    wl = wl.scaled(S=S, **({"H": H} if H else {}))
+    layout = layout or wl.layout
+    causal = wl.causal if causal is None else causal
+    t = gen.ring_inputs(wl, dev)
+    scale = oracle.default_scale(wl.D)
+    S_all = np.arange(S)
+    for r in ranks:
+        say(f"ring {wl.name} S={S} cp={wl.cp} rank={r} variant={variant} layout={layout} causal={causal} depth={depth}")
+        o, l = ca.ring.ring_attention(t["q"], t["k"], t["v"], wl.cp, r, layout=layout, causal=causal,
+                                      variant=variant, prefetch_depth=depth)
+        torch.cuda.synchronize()
+        rows = (oracle.contiguous_tokens if layout == "contiguous" else oracle.striped_tokens)(S, wl.cp, r)
+        allowed = oracle.causal_allowed(rows, S_all) if causal else None
+        ro, rl = oracle.attention_heads(t["q"][:, rows], t["k"], t["v"], scale, allowed=allowed)
+        check(f"rank {r}", o, l, ro, rl)
+
+
+def test_tiny_fp32_ring_full_config(dev):
+    wl = workloads.workload("tiny_ring_fp32")
+    for variant in ("online", "constmax"):
+        _ring_case(dev, wl, wl.S, ranks=(0, 3), variant=variant)
+
+
+def test_wan22_online_ring_scaled(dev):
+    wl = workloads.workload("wan22_cp8_online")
+    _ring_case(dev, wl, 8 * 328, ranks=(0, 5), variant="online")
+
+
+@pytest.mark.parametrize("variant", ["constmax", "online"])
+def test_wan22_720p_ring_scaled(dev, variant):
+    wl = workloads.workload("wan22_720p_constmax")
+    _ring_case(dev, wl, 8 * 300, ranks=(0,), variant=variant, H=4)
+
+
+def test_striped_causal_ring_scaled_all_ranks(dev):
+    wl = workloads.workload("striped_causal_128k")
+    _ring_case(dev, wl, 8 * 200, ranks=tuple(range(8)), variant="online", H=2)
+
+
+def test_contiguous_causal_ring_scaled(dev):
+    wl = workloads.workload("striped_causal_128k")
+    _ring_case(dev, wl, 8 * 136, ranks=(0, 3, 7), variant="online", layout="contiguous", causal=True, H=2)
+
+
+@pytest.mark.parametrize("depth", [2, 3])
+def test_ring_prefetch_depth(dev, depth):
+    wl = workloads.workload("wan22_cp8_online")
+    _ring_case(dev, wl, 8 * 64, ranks=(2,), variant="online", depth=depth, H=2)
+
+
+def test_ring_pass_is_repeatable(dev):
+    ca = _ca()
+    wl = workloads.workload("wan22_cp8_online").scaled(S=8 * 256, H=2)
+    t = gen.ring_inputs(wl, dev)
+    q = ca.ring.shard(t["q"], 8, 1, "contiguous")
+    kp = ca.ring.chunk_pool(t["k"], 8, "contiguous")
+    vp = ca.ring.chunk_pool(t["v"], 8, "contiguous")
+    for variant in ("online", "constmax"):
+        rp = ca.ring.RingPass(q, kp, vp, 1, variant=variant)
+        o1, l1 = (x.clone() for x in rp.run())
+        for _ in range(3):
+            o2, l2 = rp.run()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), variant
+
+
+def test_ring_rejects_indivisible_length(dev):
+    ca = _ca()
+    x = torch.zeros((1, 3645, 1, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="3645"):
+        ca.ring.shard(x, 8, 0, "contiguous")
+
+
+# ---------------------------------------------------------------- DCP decode
+
+def _decode_case(dev, B, Hq, Hkv, ctx, world=2, interleave=16, seed=4):
+    ca = _ca()
+    wl = workloads.workload("dcp_decode_gqa").scaled(B=B, Hq=Hq, Hkv=Hkv, ctx_override=tuple(ctx), seed=seed,
+                                                     shards=world, interleave=interleave)
+    say(f"decode B={B} Hq={Hq} Hkv={Hkv} ctx={ctx} world={world}")
+    d = gen.decode_inputs(wl, dev)
+    shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], d["ctx"], r, world, interleave, 16,
+                                       d["block_rand"]) for r in range(world)]
+    run = ca.dcp.DcpDecode(d["q"], shards)
+    o, l = run.run()
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(wl.D)
+    for b in range(B):
+        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
+        kb, vb = d["k_seq"][s0:s1], d["v_seq"][s0:s1]
+        for r in range(world):
+            po, pl = oracle.decode_shard_partial(d["q"][b], kb, vb, r, interleave, world, scale)
+            check(f"seq {b} shard {r} partial", run.o_parts[r, b], run.lse_parts[r, b], po, pl)
+        fo, fl = oracle.decode_full(d["q"][b], kb, vb, scale)
+        check(f"seq {b} merged", o[b], l[b], fo, fl)
+    return run
+
+
+def test_decode_mixed_lengths(dev):
+    _decode_case(dev, 5, 64, 8, (1, 15, 17, 1000, 3000))
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (32, 8), (32, 2)])
+def test_decode_gqa_groups(dev, Hq, Hkv):
+    _decode_case(dev, 3, Hq, Hkv, (33, 2049, 700))
+
+
+def test_decode_four_shards_and_empty_shard(dev):
+    run = _decode_case(dev, 2, 16, 4, (5, 1100), world=4)
+    # a 5-token context lives entirely on shard 0: the others are empty for it
+    for r in (1, 2, 3):
+        assert np.all(to_np(run.lse_parts[r, 0]) == -np.inf) and np.all(to_np(run.o_parts[r, 0]) == 0)
+
