@@ -192,7 +192,8 @@ def test_lse_merge_matches_oracle(dev):
     ro, rl = oracle.merge_lse(list(o.double().numpy()), list(lse.double().numpy()))
     og, lg = ca.lse_merge(o.to(dev), lse.to(dev))
     torch.cuda.synchronize()
-    check("merge fp32", og, lg, ro, rl, tol_o=2e-5, tol_lse=2e-5)
+    # fp32 LSE inputs near 900 carry an ulp of 6e-5, which bounds the weights' accuracy
+    check("merge fp32", og, lg, ro, rl, tol_o=2e-4, tol_lse=1e-4)
     ob, lb = ca.lse_merge(o.to(dev), lse.to(dev), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     check("merge bf16 out", ob, lb, ro, rl)
