@@ -8,102 +8,247 @@
 // Design "A static bound makes the ring reduction pure addition", Implementation
 // "Accumulate, then normalize once").
 //
-// Layout of the work (gfx950, wave64):
-//  * a workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32 rows;
-//  * keys stream through LDS in tiles of 64 (double-buffered, one barrier per tile);
-//  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so a
-//    lane holds 32 scores of ONE query row: the row max / row sum need one cross-half
-//    exchange (lane l <-> l^32) per tile and no other cross-lane traffic;
-//  * O^T = V^T P^T reuses the score registers directly as the B operand (no LDS round
-//    trip for P); V is transposed once per tile while it is staged into LDS, with its
-//    keys permuted so that each lane's 8 contiguous LDS values match the 8 score
-//    registers it already holds;
+// Work layout (gfx950, wave64, two workgroups of four waves per CU):
+//  * a workgroup is 2 waves and 128 query rows of one (batch, head); a wave owns 64
+//    rows as two groups of 32, so every K and V fragment read from LDS feeds two
+//    MFMAs (64 flops per LDS byte: LDS reads stay below the matrix-core time);
+//  * keys stream through LDS in tiles of 32, triple-buffered: tile t+2 is copied from
+//    HBM straight into LDS (global_load_lds_dwordx4, no staging registers) while tile t
+//    computes, with one barrier per tile. LDS rows are dense (256 B) and their 16-byte
+//    chunks are XOR-swizzled so that every read pattern below is bank-conflict free:
+//    K chunk c of row r sits at c ^ (r & 7) (8-lane 16 B reads over 8 rows), V chunk c
+//    of row r at c ^ 2(r & 3) (16-lane transposed reads over 4 rows x 32 B);
+//  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each
+//    lane holds 16 scores of one query row per group: the row max and row sum need
+//    one exchange between lanes l and l^32 per tile and nothing else;
+//  * the QK^T product of tile t+1 is issued before the softmax of tile t, so the
+//    matrix cores work while the VALU does exp/max/sum;
+//  * O^T = V^T P^T takes P straight from the score registers (B operand); V stays in
+//    natural [key][d] order in LDS and ds_read_b64_tr_b16 transposes it on the read
+//    (within 16 lanes, lane i element t <- lane i/4 + 4t's element i%4), fetching the
+//    keys in exactly the order the score registers hold them;
 //  * softmax uses exp2 with scale*log2(e) folded into one FMA per score; the running
-//    max is moved only when a tile's max exceeds it by more than 8 (log2 units), so
-//    the accumulator rescale is rare (probabilities stay <= 256, exact in fp32/bf16).
+//    max moves only when a tile's max exceeds it by more than 8 (log2 units), so the
+//    accumulator rescale is rare and probabilities stay <= 256.
 #include "internal.hpp"
 
 namespace ctxattn {
 namespace {
 
-constexpr int D = 128;        // head dim of the bf16 path
-constexpr int BQ = 128;       // query rows per workgroup
-constexpr int BK = 64;        // keys per LDS tile
-constexpr int NT = 256;       // threads per workgroup
-constexpr int KS = D + 8;     // LDS row stride (bf16) of a K row:   272 B
-constexpr int VS = BK + 8;    // LDS row stride (bf16) of a V^T row: 144 B
-constexpr int K_TILE = BK * KS;
-constexpr int V_TILE = D * VS;
-constexpr size_t LDS_BYTES = size_t(2) * (K_TILE + V_TILE) * sizeof(uint16_t);
-constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may lag the true max
+constexpr int D = 128;         // head dim of the bf16 path
+constexpr int NW = 4;          // waves per workgroup
+constexpr int NT = 64 * NW;    // threads per workgroup
+constexpr int BQ = 32 * NW;    // query rows per workgroup (32 per wave)
+constexpr int BK = 32;         // keys per LDS tile
+constexpr int NBUF = 3;        // LDS tile buffers
+constexpr int ROW = D;                    // bf16 per LDS row (dense, swizzled)
+constexpr int TILE = BK * ROW;            // bf16 per tile and tensor (8 KB)
+constexpr size_t LDS_BYTES = size_t(NBUF) * 2 * TILE * sizeof(uint16_t);
+constexpr int COPIES = BK * D / 8 / NT;   // 16-byte copies per lane per tile and tensor (2)
+constexpr float kRescaleSlack = 8.0f;
 
 enum { MODE_ONLINE = 0, MODE_CONSTMAX = 1 };
 
-struct Stage {
-  uint4 k[4];
-  uint4 v[4];
-};
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
 
-__device__ __forceinline__ void load_stage(Stage& st, const uint16_t* kbase, const uint16_t* vbase,
-                                           int64_t kss, int key0, int Sk, int tid) {
-  // K: 64 rows x 16 chunks of 16 B; thread tid takes chunks tid, tid+256, ...
+// Makes the compiler wait for a value's load here (an empty asm that reads it), so no wait
+// for it is left inside the tile loop, where it would also wait for in-flight tile copies.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) { asm volatile("" :: "v"(x)); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((__attribute__((address_space(3))) const char*)(p)));
+}
+
+// One 16-byte-per-lane copy HBM -> LDS (global_load_lds_dwordx4): lane l's 16 bytes land at
+// LDS byte m0 + 16*l. Issued as inline asm so that the compiler neither waits for it before
+// unrelated LDS reads nor before barriers: the kernel places every wait for these copies.
+__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_byte), "v"(g) : "memory", "m0");
+}
+
+// Copies one 32-key tile of K and V from HBM into LDS. Copy u of wave w fills LDS rows
+// (COPIES*w+u)*4 .. +3 (1 KB, lane l -> row + l/16, physical chunk l%16) and so reads the
+// logical chunk that the swizzle places there. Rows past the chunk's end re-read the
+// last key (their scores are masked, their values meet p = 0).
+__device__ __forceinline__ void issue_tile(uint16_t* Kt, uint16_t* Vt, const uint16_t* kbase,
+                                           const uint16_t* vbase, int64_t kss, int key0, int Sk, int w,
+                                           int lane) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int ci = tid + NT * u;
-    const int row = ci >> 4;
-    const int col = (ci & 15) * 8;
-    const int key = key0 + row;
-    st.k[u] = key < Sk ? *reinterpret_cast<const uint4*>(kbase + key * kss + col) : make_uint4(0, 0, 0, 0);
-  }
-  // V: thread (dg = tid % 16, kg = tid / 16) loads keys 4kg..4kg+3 at d = 8dg..8dg+7.
-  const int dg = tid & 15;
-  const int kg = tid >> 4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int key = key0 + 4 * kg + e;
-    st.v[e] = key < Sk ? *reinterpret_cast<const uint4*>(vbase + key * kss + dg * 8) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < COPIES; ++u) {
+    const int blk = w * COPIES + u;
+    const int row = blk * 4 + (lane >> 4);
+    const int p = lane & 15;
+    const int64_t key = min(key0 + row, Sk - 1);
+    const uint16_t* kg = kbase + key * kss + ((p ^ (row & 7)) << 3);
+    const uint16_t* vg = vbase + key * kss + ((p ^ ((row & 3) << 1)) << 3);
+    copy16_to_lds(kg, __builtin_amdgcn_readfirstlane(lds_addr(Kt + blk * 512)));
+    copy16_to_lds(vg, __builtin_amdgcn_readfirstlane(lds_addr(Vt + blk * 512)));
   }
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& x, int w) {
-  return w == 0 ? x.x : w == 1 ? x.y : w == 2 ? x.z : x.w;
+// Barrier after this wave's copies of the current tile have landed: with another tile's
+// batch (2*COPIES copies) issued later, vmcnt(2*COPIES) leaves exactly that batch in flight.
+__device__ __forceinline__ void wait_tile_and_barrier(bool newer_batch_in_flight) {
+  static_assert(2 * COPIES == 4, "vmcnt immediate below assumes 4 copies per batch");
+  if (newer_batch_in_flight) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ void store_stage(const Stage& st, uint16_t* Ks, uint16_t* Vt, int tid) {
+__device__ __forceinline__ bf16x8 tr16_pair(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) short4v* lds_ptr;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p + 8 * ROW));
+  const short4v both[2] = {lo, hi};
+  return *reinterpret_cast<const bf16x8*>(both);
+}
+
+// S^T for 32 keys x 32 rows. kr[j] is this lane's read offset for d-chunks c with
+// c % 4 == j (row li, swizzled); chunks 4..7 add 64 elements.
+__device__ __forceinline__ void qk_tile(const uint16_t* Kt, const int (&kr)[4], const bf16x8 (&q)[8], floatx16& s) {
+  bf16x8 ka[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int ci = tid + NT * u;
-    const int row = ci >> 4;
-    const int col = (ci & 15) * 8;
-    *reinterpret_cast<uint4*>(Ks + row * KS + col) = st.k[u];
+  for (int c = 0; c < 8; ++c) ka[c] = *reinterpret_cast<const bf16x8*>(Kt + kr[c & 3] + (c >> 2) * 64);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
+}
+
+// Softmax numerators of one 32-row group: p = exp2(s*sl2e - mu) packed to bf16 in
+// P.V operand order (kc = 0: registers 0..7, kc = 1: registers 8..15). Returns sum p.
+__device__ __forceinline__ float exp_pack(const floatx16& s, float sl2e, float mu, bf16x8 (&pb)[2]) {
+  float sum = 0.0f;
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = kc * 8 + 2 * t;
+      const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2e, -mu));
+      const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2e, -mu));
+      sum += x0 + x1;
+      w[t] = pack_bf16x2(x0, x1);
+    }
+    uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
+    pb[kc] = *reinterpret_cast<bf16x8*>(&u);
   }
-  // Transpose the 4 (key) x 8 (d) block to 8 rows of V^T holding 4 keys each. Within each
-  // 16-key chunk the keys are stored with bits 2 and 3 of their index swapped, so LDS
-  // positions 0..7 hold keys {0-3, 8-11} and positions 8..15 keys {4-7, 12-15}: the
-  // order of the score registers a lane feeds to the P.V product.
-  const int dg = tid & 15;
-  const int kg = tid >> 4;
-  const int pos = (kg >> 2) * 16 + (((kg & 1) << 3) | ((kg & 2) << 1));
+  return sum;
+}
+
+// Online-max bookkeeping of one group for one tile; returns the exp2 offset mu.
+__device__ __forceinline__ float online_update(const floatx16& s, float sl2e, float& m_ref, float& l_part,
+                                               floatx16 (&o)[4]) {
+  float tmax = s[0];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a0 = word(st.v[0], w), a1 = word(st.v[1], w);
-    const uint32_t a2 = word(st.v[2], w), a3 = word(st.v[3], w);
-    uint2 lo, hi;
-    lo.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);   // d even: keys 0,1
-    lo.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);   //         keys 2,3
-    hi.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);   // d odd
-    hi.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-    const int d = dg * 8 + 2 * w;
-    *reinterpret_cast<uint2*>(Vt + d * VS + pos) = lo;
-    *reinterpret_cast<uint2*>(Vt + (d + 1) * VS + pos) = hi;
+  for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float t2 = tmax * sl2e;
+  const bool move = t2 > m_ref + kRescaleSlack;
+  if (__any(move)) {
+    const float m_new = move ? t2 : m_ref;
+    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    m_ref = m_new;
+  }
+  return (m_ref == -INFINITY) ? 0.0f : m_ref;
+}
+
+template <int MASK>
+__device__ __forceinline__ void apply_mask(floatx16& s, int key0, int hl, int row, int Sk) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+    bool ok = j < Sk;
+    if (MASK == CA_MASK_CAUSAL_INCL) ok &= j <= row;
+    if (MASK == CA_MASK_CAUSAL_STRICT) ok &= j < row;
+    s[r] = ok ? s[r] : -INFINITY;
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_rows(const AttnArgs& a, int64_t bh, int Sq, int row, int hl,
+                                           floatx16 (&o)[4], float l_part, float m_ref, float c2) {
+  const float lrow = l_part + __shfl_xor(l_part, 32);
+  if (row >= Sq) return;
+  const int64_t rowidx = bh * Sq + row;
+  // o[db][r] is O[row][d] for d = 32*db + 8*(r/4) + 4*hl + r%4: four consecutive d per float4.
+  if (MODE == MODE_ONLINE) {
+    const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
+    float* orow = a.o + rowidx * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * hl) =
+            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+    if (hl == 0) a.lse[rowidx] = lrow > 0.0f ? (m_ref + __log2f(lrow)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t rows = int64_t(a.B) * a.H * Sq;
+    float sum = lrow;
+    if (!(a.phase & CA_PHASE_INIT)) {
+      const float* arow = a.acc + rowidx * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 p4 = *reinterpret_cast<const float4*>(arow + db * 32 + 8 * g + 4 * hl);
+          o[db][4 * g] += p4.x; o[db][4 * g + 1] += p4.y;
+          o[db][4 * g + 2] += p4.z; o[db][4 * g + 3] += p4.w;
+        }
+      sum += a.acc[rows * D + rowidx];
+    }
+    if (!(a.phase & CA_PHASE_FINAL)) {
+      float* arow = a.acc + rowidx * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(arow + db * 32 + 8 * g + 4 * hl) =
+              make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+      if (hl == 0) a.acc[rows * D + rowidx] = sum;
+    } else {
+      const float z = fmaxf(sum, kSumClamp);
+      const float inv = 1.0f / z;
+      if (a.o_cm_bf16) {
+        uint16_t* orow = static_cast<uint16_t*>(a.o_cm) + rowidx * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint2 u;
+            u.x = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+            u.y = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * hl) = u;
+          }
+      } else {
+        float* orow = static_cast<float*>(a.o_cm) + rowidx * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * hl) =
+                make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                            o[db][4 * g + 3] * inv);
+      }
+      if (hl == 0 && a.lse_cm) a.lse_cm[rowidx] = c2 * kLn2 + __logf(z);
+    }
   }
 }
 
 template <int MODE, int MASK>
-__global__ __launch_bounds__(NT, 2) void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
+__global__ __launch_bounds__(NT, 2)
+void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* Ks0 = lds;
-  uint16_t* Vt0 = lds + 2 * K_TILE;
+  uint16_t* Kb = lds;
+  uint16_t* Vb = lds + NBUF * TILE;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x, nwork);
   if (logical < 0) return;
@@ -119,16 +264,19 @@ __global__ __launch_bounds__(NT, 2) void attn_step_bf16(const AttnArgs a, int nq
   const int li = lane & 31;
   const int hl = lane >> 5;
   const int row_w0 = qb * BQ + w * 32;   // first query row of this wave
-  const int i = row_w0 + li;             // this lane's query row
+  const int row = row_w0 + li;           // this lane's query row
   const int Sq = a.Sq, Sk = a.Sk;
 
-  // Q fragment: row i, d = c*16 + 8*hl .. +7 for c = 0..7 (B operand of S^T = K Q^T).
-  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + b * a.qsb + int64_t(i) * a.qss + h * a.qsh;
-  bf16x8 qf[8];
+  // Q fragment: row, d = c*16 + 8*hl .. +7 (B operand of S^T = K Q^T). Rows past Sq re-read
+  // the last row; their outputs are never stored.
+  bf16x8 q[8];
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh + hl * 8 +
+                         int64_t(min(row, Sq - 1)) * a.qss;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint4 t = i < Sq ? *reinterpret_cast<const uint4*>(qrow + c * 16 + hl * 8) : make_uint4(0, 0, 0, 0);
-    qf[c] = *reinterpret_cast<bf16x8*>(&t);
+    for (int c = 0; c < 8; ++c) q[c] = *reinterpret_cast<const bf16x8*>(qr + c * 16);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) settle(q[c]);
   }
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh;
@@ -138,200 +286,96 @@ __global__ __launch_bounds__(NT, 2) void attn_step_bf16(const AttnArgs a, int nq
   if (MASK != CA_MASK_NONE) kend = min(Sk, qb * BQ + BQ);
   const int nkt = (kend + BK - 1) / BK;
 
-  floatx16 oacc[4];
+  floatx16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
 
   float m_ref = -INFINITY;   // running reference max (log2 units), online mode
   float l_part = 0.0f;       // this lane's share of the row sum
   float c2 = 0.0f;           // const-max bound in log2 units
   if (MODE == MODE_CONSTMAX) {
-    if (i < Sq) c2 = a.c[int64_t(bh) * Sq + i] * kLog2e;
+    c2 = a.c[int64_t(bh) * Sq + min(row, Sq - 1)] * kLog2e;
+    settle(c2);
   }
   const float sl2e = a.sl2e;
 
-  Stage st;
-  if (nkt > 0) {
-    load_stage(st, kbase, vbase, a.kss, 0, Sk, tid);
-    store_stage(st, Ks0, Vt0, tid);
+  // Per-lane LDS read offsets (elements, within a tile).
+  // K: row li, logical chunk 2c+hl at physical chunk (2c+hl) ^ (li & 7).
+  int kr[4];
+  {
+    const int kx = li & 7;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kr[j] = li * ROW + (((2 * j + hl) ^ kx) << 3);
   }
-  __syncthreads();
+  // V (transposed reads): lane i16 of 16-lane group G reads row 4*hl + t (t = i16/4; +16 kc,
+  // +8 for the second half), logical element 32*db + 16*(G&1) + 4*(i16&3), i.e. chunk
+  // 4*db + 2*(G&1) + (i16&3)/2, swizzled by 2t: physical chunk 4*(db ^ (t>>1)) +
+  // ((2*(G&1) + (i16&3)/2) ^ 2*(t&1)).
+  int vr_even, vr_odd;
+  {
+    const int i16 = lane & 15;
+    const int t = i16 >> 2;
+    const int clow = (2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1)) ^ (2 * (t & 1));
+    const int base = (4 * hl + t) * ROW + (clow << 3) + 4 * (i16 & 1);
+    const int tb = t >> 1;
+    vr_even = base + 32 * tb;    // db even: chunk block db + tb
+    vr_odd = base - 32 * tb;     // db odd:  chunk block db - tb
+  }
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const uint16_t* Ks = Ks0 + buf * K_TILE;
-    const uint16_t* Vt = Vt0 + buf * V_TILE;
-    const int key0 = kt * BK;
-    if (kt + 1 < nkt) load_stage(st, kbase, vbase, a.kss, key0 + BK, Sk, tid);
+  // A tile is skipped by a wave when causality hides all of its keys from all 32 rows.
+  auto skip_tile = [&](int t) -> bool {
+    if (MASK == CA_MASK_CAUSAL_INCL) return t * BK > row_w0 + 31;
+    if (MASK == CA_MASK_CAUSAL_STRICT) return t * BK >= row_w0 + 31;
+    return false;
+  };
 
-    // Is any key of this tile visible to any row of this wave?
-    bool skip = false;
-    bool need_mask = key0 + BK > Sk;
-    if (MASK == CA_MASK_CAUSAL_INCL) {
-      skip = key0 > row_w0 + 31;
-      need_mask |= key0 + BK - 1 > row_w0;
-    } else if (MASK == CA_MASK_CAUSAL_STRICT) {
-      skip = key0 >= row_w0 + 31;
-      need_mask |= key0 + BK - 1 >= row_w0;
-    }
+  if (nkt > 0) issue_tile(Kb, Vb, kbase, vbase, a.kss, 0, Sk, w, lane);
+  if (nkt > 1) issue_tile(Kb + TILE, Vb + TILE, kbase, vbase, a.kss, BK, Sk, w, lane);
 
-    if (!skip) {
-      floatx16 s0, s1;
+  int buf = 0;
+  for (int t = 0; t < nkt; ++t) {
+    const int key0 = t * BK;
+    const int nb1 = buf == NBUF - 1 ? 0 : buf + 1;
+    const int nb2 = nb1 == NBUF - 1 ? 0 : nb1 + 1;
+    // tile t's copies (issued two iterations ago, or in the prologue) must have landed;
+    // tile t+1's batch may stay in flight
+    wait_tile_and_barrier(t + 1 < nkt);
+    // tile t+2 goes into the buffer that tile t-1 used (free: every wave passed the barrier)
+    if (t + 2 < nkt) issue_tile(Kb + nb2 * TILE, Vb + nb2 * TILE, kbase, vbase, a.kss, key0 + 2 * BK, Sk, w, lane);
+
+    if (!skip_tile(t)) {
+      // V fragments first: their LDS latency hides behind QK^T and the softmax
+      const uint16_t* vt = Vb + buf * TILE;
+      bf16x8 va[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
-      const uint16_t* kr0 = Ks + li * KS + hl * 8;
-      const uint16_t* kr1 = Ks + (32 + li) * KS + hl * 8;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kr0 + c * 16);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kr1 + c * 16);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s1, 0, 0, 0);
-      }
-      // s{jb}[r] is the raw score q_i . k_j for key j = key0 + 32*jb + 8*(r/4) + 4*hl + r%4.
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j0 = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const int j1 = j0 + 32;
-          bool ok0 = j0 < Sk, ok1 = j1 < Sk;
-          if (MASK == CA_MASK_CAUSAL_INCL) { ok0 &= j0 <= i; ok1 &= j1 <= i; }
-          if (MASK == CA_MASK_CAUSAL_STRICT) { ok0 &= j0 < i; ok1 &= j1 < i; }
-          s0[r] = ok0 ? s0[r] : -INFINITY;
-          s1[r] = ok1 ? s1[r] : -INFINITY;
-        }
-      }
-
+        for (int kc = 0; kc < 2; ++kc)
+          va[db * 2 + kc] = tr16_pair(vt + ((db & 1) ? vr_odd : vr_even) + kc * 16 * ROW + db * 32);
+      floatx16 s;
+      qk_tile(Kb + buf * TILE, kr, q, s);
+      bool need_mask = key0 + BK > Sk;
+      if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
+      if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
+      if (need_mask) apply_mask<MASK>(s, key0, hl, row, Sk);
       float mu;
-      if (MODE == MODE_ONLINE) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float t2 = tmax * sl2e;
-        const bool move = t2 > m_ref + kRescaleSlack;
-        if (__any(move)) {
-          const float m_new = move ? t2 : m_ref;
-          const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
-          l_part *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-          m_ref = m_new;
-        }
-        mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
-      } else {
-        mu = c2;
-      }
+      if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
+      else mu = c2;
+      bf16x8 p[2];
+      l_part += exp_pack(s, sl2e, mu, p);
 
-      // p = exp2(s * scale*log2e - mu), packed to bf16 in the order the P.V product reads.
-      bf16x8 pb[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        uint32_t wds[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = (kc & 1) * 8 + 2 * t;
-          float x0 = (kc < 2 ? s0[r] : s1[r]);
-          float x1 = (kc < 2 ? s0[r + 1] : s1[r + 1]);
-          x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, sl2e, -mu));
-          x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, sl2e, -mu));
-          psum += x0 + x1;
-          wds[t] = pack_bf16x2(x0, x1);
-        }
-        uint4 u4 = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-        pb[kc] = *reinterpret_cast<bf16x8*>(&u4);
-      }
-      l_part += psum;
-
-      // O^T[d][i] += sum_j V^T[d][j] P^T[j][i]
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vr = Vt + (db * 32 + li) * VS + hl * 8;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vr + kc * 16);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc], oacc[db], 0, 0, 0);
-        }
-      }
-    }
-
-    if (kt + 1 < nkt) store_stage(st, Ks0 + (buf ^ 1) * K_TILE, Vt0 + (buf ^ 1) * V_TILE, tid);
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------ epilogue
-  const float lrow = l_part + __shfl_xor(l_part, 32);
-  if (i >= Sq) return;
-  const int64_t rowidx = int64_t(bh) * Sq + i;
-  // oacc[db][r] is O[i][d] for d = 32*db + 8*(r/4) + 4*hl + r%4: four consecutive d per float4.
-  if (MODE == MODE_ONLINE) {
-    const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
-    float* orow = a.o + rowidx * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 v4 = make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                                oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        *reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * hl) = v4;
-      }
-    if (hl == 0) a.lse[rowidx] = lrow > 0.0f ? (m_ref + __log2f(lrow)) * kLn2 : -INFINITY;
-  } else {
-    const int64_t rows = int64_t(a.B) * a.H * Sq;
-    float sum = lrow;
-    if (!(a.phase & CA_PHASE_INIT)) {
-      const float* arow = a.acc + rowidx * D;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 p4 = *reinterpret_cast<const float4*>(arow + db * 32 + 8 * g + 4 * hl);
-          oacc[db][4 * g] += p4.x; oacc[db][4 * g + 1] += p4.y;
-          oacc[db][4 * g + 2] += p4.z; oacc[db][4 * g + 3] += p4.w;
-        }
-      sum += a.acc[rows * D + rowidx];
+        for (int kc = 0; kc < 2; ++kc)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
     }
-    if (!(a.phase & CA_PHASE_FINAL)) {
-      float* arow = a.acc + rowidx * D;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(arow + db * 32 + 8 * g + 4 * hl) =
-              make_float4(oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]);
-      if (hl == 0) a.acc[rows * D + rowidx] = sum;
-    } else {
-      const float z = fmaxf(sum, kSumClamp);
-      const float inv = 1.0f / z;
-      if (a.o_cm_bf16) {
-        uint16_t* orow = static_cast<uint16_t*>(a.o_cm) + rowidx * D;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint2 u;
-            u.x = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-            u.y = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + db * 32 + 8 * g + 4 * hl) = u;
-          }
-      } else {
-        float* orow = static_cast<float*>(a.o_cm) + rowidx * D;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * hl) =
-                make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                            oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-      }
-      if (hl == 0 && a.lse_cm) a.lse_cm[rowidx] = c2 * kLn2 + __logf(z);
-    }
+    buf = nb1;
   }
+
+  store_rows<MODE>(a, bh, Sq, row, hl, o, l_part, m_ref, c2);
 }
 
 template <int MODE, int MASK>
