@@ -9,27 +9,29 @@
 // "Accumulate, then normalize once").
 //
 // Work layout (gfx950, wave64, two workgroups of four waves per CU):
-//  * a workgroup is 2 waves and 128 query rows of one (batch, head); a wave owns 64
-//    rows as two groups of 32, so every K and V fragment read from LDS feeds two
-//    MFMAs (64 flops per LDS byte: LDS reads stay below the matrix-core time);
+//  * a workgroup is 4 waves and 128 query rows of one (batch, head); each wave owns
+//    32 rows and keeps Q, the output accumulator and the scores in VGPRs;
 //  * keys stream through LDS in tiles of 32, triple-buffered: tile t+2 is copied from
-//    HBM straight into LDS (global_load_lds_dwordx4, no staging registers) while tile t
-//    computes, with one barrier per tile. LDS rows are dense (256 B) and their 16-byte
-//    chunks are XOR-swizzled so that every read pattern below is bank-conflict free:
-//    K chunk c of row r sits at c ^ (r & 7) (8-lane 16 B reads over 8 rows), V chunk c
-//    of row r at c ^ 2(r & 3) (16-lane transposed reads over 4 rows x 32 B);
+//    HBM straight into LDS (global_load_lds_dwordx4: no staging registers, one scalar
+//    base per tile plus a fixed per-lane offset) while tile t computes; one barrier per
+//    tile; the tile loop is unrolled by three so every LDS buffer offset is an
+//    instruction immediate;
+//  * LDS rows are dense (256 B) with XOR-swizzled 16-byte chunks so that both read
+//    patterns are bank-conflict free whether the hardware serves 8 or 16 lanes of a
+//    16-byte read (32 or 64 banks) per cycle: K chunk c of row r sits at c ^ (r & 15),
+//    V chunk c at c ^ (4(r & 3) + 2((r >> 1) & 1));
 //  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each
-//    lane holds 16 scores of one query row per group: the row max and row sum need
-//    one exchange between lanes l and l^32 per tile and nothing else;
-//  * the QK^T product of tile t+1 is issued before the softmax of tile t, so the
-//    matrix cores work while the VALU does exp/max/sum;
+//    lane holds 16 scores of one query row: the row max needs one exchange between
+//    lanes l and l^32 per tile and nothing else;
 //  * O^T = V^T P^T takes P straight from the score registers (B operand); V stays in
 //    natural [key][d] order in LDS and ds_read_b64_tr_b16 transposes it on the read
 //    (within 16 lanes, lane i element t <- lane i/4 + 4t's element i%4), fetching the
 //    keys in exactly the order the score registers hold them;
-//  * softmax uses exp2 with scale*log2(e) folded into one FMA per score; the running
-//    max moves only when a tile's max exceeds it by more than 8 (log2 units), so the
+//  * softmax uses exp2 with scale*log2(e) folded into one FMA per score; the running max
+//    moves only when a tile's max exceeds it by more than 8 (log2 units), so the
 //    accumulator rescale is rare and probabilities stay <= 256.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace ctxattn {
@@ -43,15 +45,18 @@ constexpr int BK = 32;         // keys per LDS tile
 constexpr int NBUF = 3;        // LDS tile buffers
 constexpr int ROW = D;                    // bf16 per LDS row (dense, swizzled)
 constexpr int TILE = BK * ROW;            // bf16 per tile and tensor (8 KB)
-constexpr size_t LDS_BYTES = size_t(NBUF) * 2 * TILE * sizeof(uint16_t);
+constexpr int TILE_BYTES = TILE * 2;
+constexpr int V_OFF = NBUF * TILE_BYTES;  // byte offset of the V buffers
+constexpr size_t LDS_BYTES = size_t(NBUF) * 2 * TILE_BYTES;
 constexpr int COPIES = BK * D / 8 / NT;   // 16-byte copies per lane per tile and tensor (2)
 constexpr float kRescaleSlack = 8.0f;
 
 enum { MODE_ONLINE = 0, MODE_CONSTMAX = 1 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+__host__ __device__ constexpr int k_swz(int r) { return r & 15; }
+__host__ __device__ constexpr int v_swz(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
 
 // Makes the compiler wait for a value's load here (an empty asm that reads it), so no wait
 // for it is left inside the tile loop, where it would also wait for in-flight tile copies.
@@ -62,32 +67,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(uintptr_t((__attribute__((address_space(3))) const char*)(p)));
 }
 
-// One 16-byte-per-lane copy HBM -> LDS (global_load_lds_dwordx4): lane l's 16 bytes land at
-// LDS byte m0 + 16*l. Issued as inline asm so that the compiler neither waits for it before
-// unrelated LDS reads nor before barriers: the kernel places every wait for these copies.
-__device__ __forceinline__ void copy16_to_lds(const void* g, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_byte), "v"(g) : "memory", "m0");
-}
-
-// Copies one 32-key tile of K and V from HBM into LDS. Copy u of wave w fills LDS rows
-// (COPIES*w+u)*4 .. +3 (1 KB, lane l -> row + l/16, physical chunk l%16) and so reads the
-// logical chunk that the swizzle places there. Rows past the chunk's end re-read the
-// last key (their scores are masked, their values meet p = 0).
-__device__ __forceinline__ void issue_tile(uint16_t* Kt, uint16_t* Vt, const uint16_t* kbase,
-                                           const uint16_t* vbase, int64_t kss, int key0, int Sk, int w,
-                                           int lane) {
-#pragma unroll
-  for (int u = 0; u < COPIES; ++u) {
-    const int blk = w * COPIES + u;
-    const int row = blk * 4 + (lane >> 4);
-    const int p = lane & 15;
-    const int64_t key = min(key0 + row, Sk - 1);
-    const uint16_t* kg = kbase + key * kss + ((p ^ (row & 7)) << 3);
-    const uint16_t* vg = vbase + key * kss + ((p ^ ((row & 3) << 1)) << 3);
-    copy16_to_lds(kg, __builtin_amdgcn_readfirstlane(lds_addr(Kt + blk * 512)));
-    copy16_to_lds(vg, __builtin_amdgcn_readfirstlane(lds_addr(Vt + blk * 512)));
-  }
+// One 16-byte-per-lane copy HBM -> LDS: lane l reads base + off and its 16 bytes land at LDS
+// byte m0 + 16*l. Inline asm, so that the compiler neither waits for it before unrelated LDS
+// reads nor before barriers: the kernel places every wait for these copies itself.
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_byte), "v"(off), "s"(base) : "memory", "m0");
 }
 
 // Barrier after this wave's copies of the current tile have landed: with another tile's
@@ -98,30 +83,26 @@ __device__ __forceinline__ void wait_tile_and_barrier(bool newer_batch_in_flight
   else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ bf16x8 tr16_pair(const uint16_t* p) {
+template <int IMM>
+__device__ __forceinline__ bf16x8 lds_read16(const uint16_t* lds0, int off_el) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(lds0) + IMM + 2 * off_el);
+}
+
+template <int IMM>
+__device__ __forceinline__ bf16x8 lds_read_tr(const uint16_t* lds0, int off_el) {
   typedef __attribute__((address_space(3))) short4v* lds_ptr;
-  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
-  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p + 8 * ROW));
+  const char* p = reinterpret_cast<const char*>(lds0) + 2 * off_el;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p + IMM));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p + IMM + 8 * ROW * 2));
   const short4v both[2] = {lo, hi};
   return *reinterpret_cast<const bf16x8*>(both);
 }
 
-// S^T for 32 keys x 32 rows. kr[j] is this lane's read offset for d-chunks c with
-// c % 4 == j (row li, swizzled); chunks 4..7 add 64 elements.
-__device__ __forceinline__ void qk_tile(const uint16_t* Kt, const int (&kr)[4], const bf16x8 (&q)[8], floatx16& s) {
-  bf16x8 ka[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) ka[c] = *reinterpret_cast<const bf16x8*>(Kt + kr[c & 3] + (c >> 2) * 64);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
-}
-
-// Softmax numerators of one 32-row group: p = exp2(s*sl2e - mu) packed to bf16 in
-// P.V operand order (kc = 0: registers 0..7, kc = 1: registers 8..15). Returns sum p.
-__device__ __forceinline__ float exp_pack(const floatx16& s, float sl2e, float mu, bf16x8 (&pb)[2]) {
-  float sum = 0.0f;
+// Softmax numerators of the 16 scores a lane holds: p = exp2(s*sl2e - mu), packed to bf16 in
+// P.V operand order (kc = 0: registers 0..7, kc = 1: registers 8..15). The row-sum share of
+// the lane adds the fp32 values: summing the bf16-rounded ones instead would leave an LSE
+// error up to 2^-9 on rows that see only one or two keys.
+__device__ __forceinline__ void exp_pack(const floatx16& s, float sl2e, float mu, bf16x8 (&pb)[2], float& lsum) {
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
     uint32_t w[4];
@@ -130,21 +111,20 @@ __device__ __forceinline__ float exp_pack(const floatx16& s, float sl2e, float m
       const int r = kc * 8 + 2 * t;
       const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2e, -mu));
       const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2e, -mu));
-      sum += x0 + x1;
       w[t] = pack_bf16x2(x0, x1);
+      lsum += x0 + x1;
     }
     uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
     pb[kc] = *reinterpret_cast<bf16x8*>(&u);
   }
-  return sum;
 }
 
-// Online-max bookkeeping of one group for one tile; returns the exp2 offset mu.
+// Online-max bookkeeping for one tile; returns the exp2 offset mu.
 __device__ __forceinline__ float online_update(const floatx16& s, float sl2e, float& m_ref, float& l_part,
                                                floatx16 (&o)[4]) {
-  float tmax = s[0];
+  float tmax = fmaxf(s[0], s[1]);
 #pragma unroll
-  for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+  for (int r = 2; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[r], s[r + 1]));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const float t2 = tmax * sl2e;
   const bool move = t2 > m_ref + kRescaleSlack;
@@ -247,8 +227,6 @@ template <int MODE, int MASK>
 __global__ __launch_bounds__(NT, 2)
 void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* Kb = lds;
-  uint16_t* Vb = lds + NBUF * TILE;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x, nwork);
   if (logical < 0) return;
@@ -279,8 +257,9 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
     for (int c = 0; c < 8; ++c) settle(q[c]);
   }
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.ksb + h * a.ksh;
+  const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh);
+  const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + h * a.ksh);
+  const int64_t kss_bytes = a.kss * 2;
 
   int kend = Sk;
   if (MASK != CA_MASK_NONE) kend = min(Sk, qb * BQ + BQ);
@@ -301,27 +280,38 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
   }
   const float sl2e = a.sl2e;
 
-  // Per-lane LDS read offsets (elements, within a tile).
-  // K: row li, logical chunk 2c+hl at physical chunk (2c+hl) ^ (li & 7).
-  int kr[4];
-  {
-    const int kx = li & 7;
+  // Per-lane copy offsets (bytes from the tile's first key): copy u of this wave fills LDS
+  // rows (COPIES*w+u)*4 + lane/16 at physical chunk lane%16, i.e. reads that row's logical
+  // chunk (lane%16) ^ swizzle(row).
+  uint32_t koff[COPIES], voff[COPIES];
+  int crow[COPIES];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kr[j] = li * ROW + (((2 * j + hl) ^ kx) << 3);
+  for (int u = 0; u < COPIES; ++u) {
+    const int r = (w * COPIES + u) * 4 + (lane >> 4);
+    const int p = lane & 15;
+    crow[u] = r;
+    koff[u] = uint32_t(r * kss_bytes) + uint32_t((p ^ k_swz(r)) << 4);
+    voff[u] = uint32_t(r * kss_bytes) + uint32_t((p ^ v_swz(r)) << 4);
   }
-  // V (transposed reads): lane i16 of 16-lane group G reads row 4*hl + t (t = i16/4; +16 kc,
-  // +8 for the second half), logical element 32*db + 16*(G&1) + 4*(i16&3), i.e. chunk
-  // 4*db + 2*(G&1) + (i16&3)/2, swizzled by 2t: physical chunk 4*(db ^ (t>>1)) +
-  // ((2*(G&1) + (i16&3)/2) ^ 2*(t&1)).
-  int vr_even, vr_odd;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+
+  // Per-lane LDS read offsets (elements; buffer offsets are added as immediates).
+  // K: row li, logical chunk 2c+hl.
+  int kr[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kr[c] = li * ROW + (((2 * c + hl) ^ k_swz(li)) << 3);
+  // V (transposed reads): lane i16 of 16-lane group G reads row 4*hl + t (t = i16/4; +16 kc
+  // and +8 for the second half are immediates), logical element 32*db + 16*(G&1) + 4*(i16&3),
+  // i.e. chunk 4*db + 2*(G&1) + (i16&3)/2, physically at chunk ^ v_swz(t) =
+  // 4*(db ^ t) + ((2*(G&1) + (i16&3)/2) ^ 2*(t>>1)).
+  int vr[4];
   {
     const int i16 = lane & 15;
     const int t = i16 >> 2;
-    const int clow = (2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1)) ^ (2 * (t & 1));
+    const int clow = (2 * ((lane >> 4) & 1) + ((i16 & 3) >> 1)) ^ (2 * (t >> 1));
     const int base = (4 * hl + t) * ROW + (clow << 3) + 4 * (i16 & 1);
-    const int tb = t >> 1;
-    vr_even = base + 32 * tb;    // db even: chunk block db + tb
-    vr_odd = base - 32 * tb;     // db odd:  chunk block db - tb
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vr[db] = base + 32 * (db ^ t);
   }
 
   // A tile is skipped by a wave when causality hides all of its keys from all 32 rows.
@@ -331,48 +321,77 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
     return false;
   };
 
-  if (nkt > 0) issue_tile(Kb, Vb, kbase, vbase, a.kss, 0, Sk, w, lane);
-  if (nkt > 1) issue_tile(Kb + TILE, Vb + TILE, kbase, vbase, a.kss, BK, Sk, w, lane);
-
-  int buf = 0;
-  for (int t = 0; t < nkt; ++t) {
+  // Issues the copies of tile t into LDS buffer BUF. The last tile of a chunk clamps its rows
+  // to the last key (their scores are masked, their values meet p = 0).
+  auto issue = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
     const int key0 = t * BK;
-    const int nb1 = buf == NBUF - 1 ? 0 : buf + 1;
-    const int nb2 = nb1 == NBUF - 1 ? 0 : nb1 + 1;
-    // tile t's copies (issued two iterations ago, or in the prologue) must have landed;
-    // tile t+1's batch may stay in flight
-    wait_tile_and_barrier(t + 1 < nkt);
-    // tile t+2 goes into the buffer that tile t-1 used (free: every wave passed the barrier)
-    if (t + 2 < nkt) issue_tile(Kb + nb2 * TILE, Vb + nb2 * TILE, kbase, vbase, a.kss, key0 + 2 * BK, Sk, w, lane);
-
-    if (!skip_tile(t)) {
-      // V fragments first: their LDS latency hides behind QK^T and the softmax
-      const uint16_t* vt = Vb + buf * TILE;
-      bf16x8 va[8];
+    const char* kt = kbase + key0 * kss_bytes;
+    const char* vt = vbase + key0 * kss_bytes;
+    const bool full = key0 + BK <= Sk;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-          va[db * 2 + kc] = tr16_pair(vt + ((db & 1) ? vr_odd : vr_even) + kc * 16 * ROW + db * 32);
-      floatx16 s;
-      qk_tile(Kb + buf * TILE, kr, q, s);
-      bool need_mask = key0 + BK > Sk;
-      if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
-      if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
-      if (need_mask) apply_mask<MASK>(s, key0, hl, row, Sk);
-      float mu;
-      if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
-      else mu = c2;
-      bf16x8 p[2];
-      l_part += exp_pack(s, sl2e, mu, p);
-
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
+    for (int u = 0; u < COPIES; ++u) {
+      uint32_t ko = koff[u], vo = voff[u];
+      if (!full) {
+        const int rr = min(crow[u], Sk - 1 - key0);
+        const int p = lane & 15;
+        ko = uint32_t(rr * kss_bytes) + uint32_t((p ^ k_swz(crow[u])) << 4);
+        vo = uint32_t(rr * kss_bytes) + uint32_t((p ^ v_swz(crow[u])) << 4);
+      }
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + BUF * TILE_BYTES + (w * COPIES + u) * 1024);
+      copy16_to_lds(kt, ko, dst);
+      copy16_to_lds(vt, vo, dst + V_OFF);
     }
-    buf = nb1;
+  };
+
+  // One tile: wait for its copies, launch tile t+2's copies, compute.
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int BUF2 = (BUF + 2) % NBUF;
+    wait_tile_and_barrier(t + 1 < nkt);
+    if (t + 2 < nkt) issue(std::integral_constant<int, BUF2>{}, t + 2);
+    if (skip_tile(t)) return;
+    const int key0 = t * BK;
+    // All fragment reads up front: K first (QK^T waits for those only), then V, whose
+    // latency hides behind QK^T and the softmax.
+    bf16x8 ka[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ka[c] = lds_read16<BUF * TILE_BYTES>(lds, kr[c]);
+    bf16x8 va[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      va[db * 2] = lds_read_tr<V_OFF + BUF * TILE_BYTES>(lds, vr[db]);
+      va[db * 2 + 1] = lds_read_tr<V_OFF + BUF * TILE_BYTES + 16 * ROW * 2>(lds, vr[db]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every fragment read is issued before the first MFMA
+    floatx16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
+    // s[r] is the raw score q_row . k_j for key j = key0 + 8*(r/4) + 4*hl + r%4
+    bool need_mask = key0 + BK > Sk;
+    if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
+    if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
+    if (need_mask) apply_mask<MASK>(s, key0, hl, row, Sk);
+    float mu;
+    if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
+    else mu = c2;
+    bf16x8 p[2];
+    exp_pack(s, sl2e, mu, p, l_part);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
+  };
+
+  if (nkt > 0) issue(std::integral_constant<int, 0>{}, 0);
+  if (nkt > 1) issue(std::integral_constant<int, 1>{}, 1);
+  for (int t = 0; t < nkt; t += NBUF) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < nkt) step(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 < nkt) step(std::integral_constant<int, 2>{}, t + 2);
   }
 
   store_rows<MODE>(a, bh, Sq, row, hl, o, l_part, m_ref, c2);

@@ -71,14 +71,17 @@ class RingPass:
     """One rank's share of ring attention: q resident, cp chunks arriving one per step.
 
     variant "online": every step emits a partial (o_s, lse_s) with ring_attn_step and
-                      the partials are merged once with lse_merge;
+                      the partials are merged once with lse_merge; steps alternate between
+                      two compute streams, so a step can start as soon as its chunk has
+                      arrived and fill the GPU while the previous step drains;
     variant "constmax": the bound is built from every chunk's key norms (the ring's
                       all_reduce(max) becomes a max-fold), then every step adds into one
                       fp32 accumulator and the last step normalises.
     """
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
-                 scale=None, prefetch_depth=1, out_dtype=torch.float32, copy_stream=None):
+                 scale=None, prefetch_depth=2, out_dtype=torch.float32, copy_stream=None,
+                 compute_streams=None):
         if variant not in ("online", "constmax"):
             raise ValueError(f"unknown variant {variant!r}")
         if variant == "constmax" and causal:
@@ -100,6 +103,9 @@ class RingPass:
         self.kbuf = [torch.empty(chunk_shape, dtype=k_pool.dtype, device=dev) for _ in range(self.nbuf)]
         self.vbuf = [torch.empty(chunk_shape, dtype=v_pool.dtype, device=dev) for _ in range(self.nbuf)]
         self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device=dev)
+        if compute_streams is None:
+            compute_streams = 2 if variant == "online" else 1   # const-max steps fold in order
+        self.aux_stream = torch.cuda.Stream(device=dev) if compute_streams > 1 else None
         self.copied = [torch.cuda.Event() for _ in range(self.cp)]
         self.consumed = [torch.cuda.Event() for _ in range(self.cp)]
         self.masks = [step_mask(layout, causal, rank, ring_source_rank(rank, s, self.cp)) for s in range(self.cp)]
@@ -139,37 +145,44 @@ class RingPass:
     def run(self, timing_events=None):
         """Runs the ring on the current stream; returns (out [B,H,Sq,D], lse [B,H,Sq]).
         ``timing_events``: optional list of cp (start, end) event pairs recorded around
-        each step's kernel on the compute stream."""
+        each step's kernel on the stream that runs it."""
         cs = torch.cuda.current_stream()
         cp = self.cp
         if self.variant == "constmax":
             self.prologue()
         self.copy_stream.wait_stream(cs)
+        if self.aux_stream is not None:
+            self.aux_stream.wait_stream(cs)
         for t in range(1, min(self.depth, cp - 1) + 1):
             self._issue_copy(t)
         slot = 0
         for s in range(cp):
             t = s + self.depth
             if s >= 1 and t < cp:
+                # the buffer of step t was last read by step t - nbuf = s - 1
                 self.copy_stream.wait_event(self.consumed[s - 1])
                 self._issue_copy(t)
+            st = self.aux_stream if (self.aux_stream is not None and s % 2 == 1) else cs
             if s >= 1:
-                cs.wait_event(self.copied[s])
+                st.wait_event(self.copied[s])
             k, v = self._chunk(s)
-            if timing_events is not None:
-                timing_events[s][0].record(cs)
-            if self.variant == "online":
-                if self.masks[s] is not None:
-                    api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s],
-                                       out=self.o_parts[slot], lse=self.lse_parts[slot])
-                    slot += 1
-            else:
-                phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
-                api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out, lse=self.lse,
-                                             scale=self.scale)
-            if timing_events is not None:
-                timing_events[s][1].record(cs)
-            self.consumed[s].record(cs)
+            with torch.cuda.stream(st):
+                if timing_events is not None:
+                    timing_events[s][0].record(st)
+                if self.variant == "online":
+                    if self.masks[s] is not None:
+                        api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s],
+                                           out=self.o_parts[slot], lse=self.lse_parts[slot])
+                        slot += 1
+                else:
+                    phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
+                    api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out,
+                                                 lse=self.lse, scale=self.scale)
+                if timing_events is not None:
+                    timing_events[s][1].record(st)
+            self.consumed[s].record(st)
+        if self.aux_stream is not None:
+            cs.wait_stream(self.aux_stream)
         if self.variant == "online":
             api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
         # the copy stream must not run ahead into the next call's buffers
@@ -178,7 +191,7 @@ class RingPass:
 
 
 def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous", causal=False,
-                   variant="online", scale=None, prefetch_depth=1):
+                   variant="online", scale=None, prefetch_depth=2):
     """Convenience: rank ``rank``'s output for global [B, S, H, D] inputs."""
     check_divisible(q_global.shape[1], cp)
     q = shard(q_global, cp, rank, layout)
