@@ -378,11 +378,15 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
     if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
     else mu = c2;
     bf16x8 p[2];
+    // The softmax runs at raised wave priority: the two waves sharing a SIMD then tend to
+    // alternate, one on the VALU while the other keeps the matrix core busy.
+    __builtin_amdgcn_s_setprio(2);
     exp_pack(s, sl2e, mu, p, l_part);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int kc = 0; kc < 2; ++kc)   // kc outer: consecutive MFMAs hit different accumulators
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+      for (int db = 0; db < 4; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
   };
 
