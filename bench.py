@@ -13,6 +13,11 @@ over two interleaved paged shards (KV GB/s), and the tiny fp32 ring.
 is launched on; ``cpu_baseline`` times the fp64 oracle on a bounded row sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+                       [--only constmax,striped,decode,tiny,copy]
+
+``--only`` runs the headline plus the named extra workloads; ``copy`` times a plain device
+copy of 1 GiB through the library (kv_chunk_copy), the reference used to scale the
+FETCH_SIZE / WRITE_SIZE hardware counters into bytes.
 """
 
 import argparse
@@ -30,6 +35,30 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch),
+# scaled by the plain-copy calibration: the copy kernel moving 2 GiB in and 2 GiB out read
+# FETCH_SIZE = 1048599.6 KiB and WRITE_SIZE = 2097263.8 KiB, so fetch x 2.0, write x 1.0.
+# Each entry holds for the kernel source whose sha256 prefix it names; after an edit of that
+# source the figure no longer describes the kernel and traffic is reported as null.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+TRAFFIC = {
+    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "7ca660989a7f787f",
+                                        "fetch_kib": 21570.0, "write_kib": 20640.1},
+    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "a4babf5203842dce",
+                                  "fetch_kib": 2773545.7 + 22174.5, "write_kib": 46925.6 + 1032.0},
+}
+
+
+def traffic(key):
+    import hashlib
+    t = TRAFFIC[key]
+    path = os.path.join(ROOT, "context_attention_lse_amd", "csrc", t["source"])
+    with open(path, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != t["sha256"]:
+            return None
+    return round((t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -38,8 +67,9 @@ def ring_flops(H, Sq, Sk, D):
     return 4.0 * H * Sq * Sk * D
 
 
-def time_ring(rp, steps, warmup, torch):
-    """Runs warmup + timed ring passes; returns (ms per pass, mean step-kernel ms, per-step ms)."""
+def time_ring(rp, steps, warmup, torch, union=None):
+    """Runs warmup + timed ring passes; returns (ms per pass, per-step mean kernel ms). If ``union``
+    is a list, the mean time from the first step's start to the last step's end is appended."""
     cp = rp.cp
     for _ in range(warmup):
         rp.run()
@@ -56,6 +86,9 @@ def time_ring(rp, steps, warmup, torch):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     per_step = [sum(ev[k][s][0].elapsed_time(ev[k][s][1]) for k in range(steps)) / steps for s in range(cp)]
+    if union is not None:
+        union.append(sum(max(ev[k][s][0].elapsed_time(ev[k][j][1]) for j in range(cp)) for k in range(steps)
+                         for s in [0]) / steps)
     return ms, per_step
 
 
@@ -69,7 +102,9 @@ def headline(args, torch, ca, workloads, gen, dev):
     del t
     rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online")
     log("[bench] timing ring pass")
-    ms, per_step = time_ring(rp, args.steps, args.warmup, torch)
+    union = []
+    ms, per_step = time_ring(rp, args.steps, args.warmup, torch, union)
+    union_ms = union[0]
     Sq = wl.local_S
     flops_pass = ring_flops(wl.H, Sq, wl.S, wl.D)
     flops_step = ring_flops(wl.H, Sq, wl.local_S, wl.D)
@@ -79,9 +114,14 @@ def headline(args, torch, ca, workloads, gen, dev):
         "wl": wl, "ms": ms, "tflops": flops_pass / (ms * 1e-3) / 1e12, "step_ms": step_ms,
         "per_step_ms": per_step,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic("attn_step_bf16/wan22_cp8_online"),
                      "kernel": "attn_step_bf16 (ring_attn_step)",
-                     "per_launch": f"{flops_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128"},
+                     "per_launch": f"{flops_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
+                     "note": "consecutive ring steps run on two compute streams and overlap, so each "
+                             "launch's duration includes sharing the GPU with its neighbour step; "
+                             "steps_union_tflops is the step kernels' throughput over their union"},
+        "steps_union_tflops": round(8 * flops_step / (union_ms * 1e-3) / 1e12, 2),
         "inputs": (q, kp, vp),
     }
 
@@ -127,15 +167,45 @@ def run_constmax(args, torch, ca, workloads, gen, dev):
     out = {}
     for variant in ("constmax", "online"):
         rp = ca.ring.RingPass(q, kp, vp, 0, variant=variant)
-        ms, per_step = time_ring(rp, max(2, args.steps // 4), 1, torch)
+        union = []
+        ms, per_step = time_ring(rp, max(2, args.steps // 4), 1, torch, union)
         fl = ring_flops(wl.H, wl.local_S, wl.S, wl.D)
         step_ms = sum(per_step) / len(per_step)
-        ach = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D) / (step_ms * 1e-3) / 1e12
+        step_fl = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D)
+        ach = step_fl / (step_ms * 1e-3) / 1e12
         out[variant] = {"ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                         "step_kernel_ms": round(step_ms, 4), "step_tflops": round(ach, 2),
-                        "frac_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
+                        "frac_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4),
+                        "steps_union_tflops": round(wl.cp * step_fl / (union[0] * 1e-3) / 1e12, 2),
+                        "compute_streams": 1 if rp.aux_stream is None else 2}
+        if variant == "constmax":
+            # bound prologue: |k|^2 max over all 8 chunks + c for every query row (HBM-bound)
+            ms_b = time_calls(rp.prologue, 10, torch)
+            nbytes = (kp.numel() + q.numel()) * kp.element_size() + q.shape[1] * wl.H * 4
+            out["bound"] = {"ms": round(ms_b, 4), "bytes": nbytes, "GBps": round(nbytes / (ms_b * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(nbytes / (ms_b * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        else:
+            # the 8-way merge of the online partials (HBM-bound: 8 x 193.5 MB in, 195 MB out)
+            parts_o, parts_l = rp.o_parts[:wl.cp], rp.lse_parts[:wl.cp]
+            ms_m = time_calls(lambda: ca.lse_merge(parts_o, parts_l, out=rp.out, lse_out=rp.lse), 10, torch)
+            nbytes = (parts_o.numel() + parts_l.numel()) * 4 + (rp.out.numel() + rp.lse.numel()) * 4
+            out["merge"] = {"ms": round(ms_m, 4), "bytes": nbytes, "GBps": round(nbytes / (ms_m * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(nbytes / (ms_m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del rp
     return {"workload": wl.name, "config": f"B=1 H=40 D=128 S=75600 cp=8 local=9450 bf16", **out}
+
+
+def time_calls(fn, reps, torch):
+    """Mean ms per call of ``fn`` (launches on the current stream), after one warm-up call."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def run_striped(args, torch, ca, workloads, gen, dev):
@@ -203,7 +273,7 @@ def run_decode(args, torch, ca, workloads, gen, dev):
             "kv_bytes": kv_bytes, "ms_per_step": round(ms, 4), "kv_GBps": round(gbs, 1),
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic("dcp_decode/dcp_decode_gqa"),
                          "kernel": "dcp_decode_split_kernel + combine (dcp_decode_partial)",
                          "per_launch": "one shard's resident K+V bytes = local tokens * Hkv * D * 2 * 2"}}
 
@@ -222,6 +292,31 @@ def run_tiny(args, torch, ca, workloads, gen, dev):
     return res
 
 
+def run_copy(args, torch, ca, workloads, gen, dev):
+    n = 1 << 29                      # 2**29 bf16 = 1 GiB per tensor
+    src_k = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    src_v = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    dst_k = torch.empty_like(src_k)
+    dst_v = torch.empty_like(src_v)
+    src_k.zero_(); src_v.zero_()
+    ca.kv_chunk_copy(dst_k, dst_v, src_k, src_v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        ca.kv_chunk_copy(dst_k, dst_v, src_k, src_v)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    nbytes = 4 * n * 2                # read 2 GiB + write 2 GiB per call
+    return {"workload": "device copy 2 x 1 GiB", "ms_per_call": round(ms, 4),
+            "bytes_read_per_call": 2 * n * 2, "bytes_written_per_call": 2 * n * 2,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+EXTRAS = {"constmax": run_constmax, "striped": run_striped, "decode": run_decode, "tiny": run_tiny, "copy": run_copy}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="constmax,striped,decode,tiny",
+                    help="comma-separated extra workloads to run after the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share only: the ring's other ranks are simulated on the same "
@@ -264,15 +361,16 @@ def main():
                    "flops_per_pass": ring_flops(wl.H, wl.local_S, wl.S, wl.D)},
         "roofline": h["roofline"],
         "step_kernel_ms": round(h["step_ms"], 4),
+        "steps_union_tflops": h["steps_union_tflops"],
     }
     extra = {}
     if not args.headline_only:
         q, kp, vp = h.pop("inputs")
-        for fn in (run_constmax, run_striped, run_decode, run_tiny):
+        for name in [x for x in args.only.split(",") if x]:
             try:
-                extra[fn.__name__[4:]] = fn(args, torch, ca, workloads, gen, dev)
+                extra[name] = EXTRAS[name](args, torch, ca, workloads, gen, dev)
             except Exception as e:  # report, do not hide
-                extra[fn.__name__[4:]] = {"error": repr(e)}
+                extra[name] = {"error": repr(e)}
             torch.cuda.empty_cache()
         line["workloads"] = extra
     if not args.no_cpu_baseline:

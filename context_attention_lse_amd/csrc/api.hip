@@ -225,10 +225,10 @@ ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_po
 ca_status kv_chunk_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v, size_t bytes, void* stream) {
   if (bytes == 0) return hip_status(hipSuccess, "");
   if (!dst_k || !dst_v || !src_k || !src_v) return fail(CA_ERR_NULL, "all four chunk pointers are required");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(dst_k, src_k, bytes, hipMemcpyDeviceToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(dst_v, src_v, bytes, hipMemcpyDeviceToDevice, s);
-  return hip_status(e, "kv_chunk_copy");
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v) || (bytes & 15))
+    return fail(CA_ERR_SHAPE, "kv_chunk_copy: pointers must be 16-byte aligned and bytes a multiple of 16");
+  return hip_status(ctxattn::launch_kv_copy(dst_k, dst_v, src_k, src_v, bytes, static_cast<hipStream_t>(stream)),
+                    "kv_chunk_copy");
 }
 
 }  // extern "C"

@@ -106,5 +106,6 @@ struct DecodeArgs {
 constexpr int kDecodeSplitTokens = 1024;   // tokens per decode split (64 blocks of 16)
 size_t decode_workspace_bytes(int B, int Hq, int D, int block_size, int max_blocks);
 hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_kv_copy(void* dk, void* dv, const void* sk, const void* sv, size_t bytes, hipStream_t s);
 
 }  // namespace ctxattn

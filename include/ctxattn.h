@@ -204,8 +204,11 @@ ca_status dcp_decode_workspace_size(int B, int Hq, int D, int block_size, int ma
                                     size_t* bytes);
 
 /*
- * kv_chunk_copy -- the ring's K/V hop on one device: asynchronous device-to-device
- * copies of one K chunk and one V chunk (bytes each) on `stream`.
+ * kv_chunk_copy -- the ring's K/V hop on one device: one asynchronous copy kernel
+ * on `stream` moves one K chunk (src_k -> dst_k) and one V chunk (src_v -> dst_v),
+ * `bytes` each. All four pointers must be 16-byte aligned and bytes a multiple of
+ * 16 (CA_ERR_SHAPE otherwise); bytes == 0 is a no-op. Source and destination must
+ * not overlap.
  * Source: kernel reference page, Implementation "The ring loop" (rotating K/V
  * buffers, the next hop launched while the current step computes).
  */

@@ -1,0 +1,97 @@
+"""HIP path vs the fp64 oracle at the workloads' full sizes, in the launch configuration the
+benchmark times (RingPass / DcpDecode with their defaults), on sampled output rows that the
+oracle computes one by one against the full key range.
+
+Rows are sampled per head with a fixed seed and always include the first rows, the ragged
+last 128-row tile and the last row; every sampled row is checked element by element."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import check, say
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ca():
+    import context_attention_lse_amd as ca
+    ca._lib.load()
+    torch.cuda.set_device(0)
+    return ca
+
+
+def _rows(n, seed, k=24):
+    last_tile = (n - 1) // 128 * 128
+    return gen.sample_rows(n, k, seed, include=(0, 1, 127, 128, last_tile, n - 2, n - 1))
+
+
+def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q):
+    wl = workloads.workload(name)
+    dev = torch.device("cuda:0")
+    say(f"full-size {name} variant={variant} rank={rank} S={wl.S} cp={wl.cp} H={wl.H}")
+    t = gen.ring_inputs(wl, dev)
+    q = ca.ring.shard(t["q"], wl.cp, rank, wl.layout)
+    if contiguous_q:
+        q = q.contiguous()
+    kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
+    vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
+    rp = ca.ring.RingPass(q, kp, vp, rank, layout=wl.layout, causal=wl.causal, variant=variant)
+    o, lse = rp.run()
+    torch.cuda.synchronize()
+    tok = (oracle.contiguous_tokens if wl.layout == "contiguous" else oracle.striped_tokens)(wl.S, wl.cp, rank)
+    scale = oracle.default_scale(wl.D)
+    for h in heads:
+        rows = _rows(wl.local_S, 17 * h + rank)
+        qh = oracle.to_f64(t["q"][0, tok[rows], h])
+        kh = oracle.to_f64(t["k"][0, :, h])
+        vh = oracle.to_f64(t["v"][0, :, h])
+        allowed = oracle.causal_allowed(tok[rows], np.arange(wl.S)) if wl.causal else None
+        ro, rl = oracle.attention(qh, kh, vh, scale, allowed)
+        check(f"{name} {variant} rank {rank} head {h} ({len(rows)} rows)", o[0, h, rows], lse[0, h, rows], ro, rl)
+    del t, q, kp, vp, rp
+    torch.cuda.empty_cache()
+
+
+def test_wan22_cp8_online_fullsize(ca):
+    _ring_fullsize(ca, "wan22_cp8_online", "online", 0, heads=(0, 4, 9), contiguous_q=False)
+
+
+@pytest.mark.parametrize("variant", ["constmax", "online"])
+def test_wan22_720p_fullsize(ca, variant):
+    _ring_fullsize(ca, "wan22_720p_constmax", variant, 0, heads=(0, 21, 39), contiguous_q=True)
+
+
+@pytest.mark.parametrize("rank", [0, 3, 7])
+def test_striped_causal_128k_fullsize(ca, rank):
+    _ring_fullsize(ca, "striped_causal_128k", "online", rank, heads=(0, 31), contiguous_q=True)
+
+
+def test_dcp_decode_fullsize(ca):
+    wl = workloads.workload("dcp_decode_gqa")
+    dev = torch.device("cuda:0")
+    say(f"full-size {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} shards={wl.shards}")
+    d = gen.decode_inputs(wl, dev)
+    shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], d["ctx"], r, wl.shards,
+                                       wl.interleave, wl.block_size, d["block_rand"]) for r in range(wl.shards)]
+    run = ca.dcp.DcpDecode(d["q"], shards)
+    o, lse = run.run()
+    torch.cuda.synchronize()
+    ctx = d["ctx"]
+    picks = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 13})
+    scale = oracle.default_scale(wl.D)
+    for b in picks:
+        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
+        kb, vb = d["k_seq"][s0:s1].cpu(), d["v_seq"][s0:s1].cpu()
+        for r in range(wl.shards):
+            po, pl = oracle.decode_shard_partial(d["q"][b].cpu(), kb, vb, r, wl.interleave, wl.shards, scale)
+            check(f"seq {b} (ctx {s1 - s0}) shard {r}", run.o_parts[r, b], run.lse_parts[r, b], po, pl)
+        fo, fl = oracle.decode_full(d["q"][b].cpu(), kb, vb, scale)
+        check(f"seq {b} (ctx {s1 - s0}) merged", o[b], lse[b], fo, fl)
+    del d, shards, run
+    torch.cuda.empty_cache()

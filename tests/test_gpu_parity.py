@@ -273,6 +273,23 @@ def test_ring_pass_is_repeatable(dev):
         assert torch.equal(o1, o2) and torch.equal(l1, l2), variant
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, (1 << 22) + 16 * 1000])
+def test_kv_chunk_copy_is_exact(dev, nbytes):
+    """The hop copies both chunks byte for byte, including a ragged last workgroup."""
+    ca = _ca()
+    say(f"kv_chunk_copy bytes={nbytes}")
+    n = nbytes // 2
+    src_k = gen.normal((n,), 31, dev, torch.bfloat16)
+    src_v = gen.normal((n,), 32, dev, torch.bfloat16)
+    full_k = torch.full((n + 64,), 7.0, dtype=torch.bfloat16, device=dev)
+    full_v = torch.full((n + 64,), 7.0, dtype=torch.bfloat16, device=dev)
+    ca.kv_chunk_copy(full_k[:n], full_v[:n], src_k, src_v)
+    torch.cuda.synchronize()
+    assert torch.equal(full_k[:n].view(torch.int16), src_k.view(torch.int16))
+    assert torch.equal(full_v[:n].view(torch.int16), src_v.view(torch.int16))
+    assert bool((full_k[n:] == 7.0).all()) and bool((full_v[n:] == 7.0).all())   # nothing written past the end
+
+
 def test_ring_rejects_indivisible_length(dev):
     ca = _ca()
     x = torch.zeros((1, 3645, 1, 128), dtype=torch.bfloat16, device=dev)
