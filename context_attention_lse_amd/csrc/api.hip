@@ -106,7 +106,7 @@ ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void
 ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, int H, int D, float* kmax_sq,
                          int accumulate, void* stream) {
   CA_TRY(check_dtype(dtype));
-  if (D <= 0 || D % 8) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
+  if (D <= 0 || D % 8 || D > 128) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 128]");
   CA_TRY(check_bshd("k", k, ks, dtype, B, S, H, D));
   if (int64_t(B) * H == 0) return hip_status(hipSuccess, "");
   if (!kmax_sq) return fail(CA_ERR_NULL, "kmax_sq is NULL");
@@ -119,7 +119,7 @@ ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, 
 ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq, int H, int D, float softmax_scale,
                           const float* kmax_sq, float* c, void* stream) {
   CA_TRY(check_dtype(dtype));
-  if (D <= 0 || D % 8) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
+  if (D <= 0 || D % 8 || D > 128) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 128]");
   CA_TRY(check_bshd("q", q, qs, dtype, B, Sq, H, D));
   if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
   if (!kmax_sq || !c) return fail(CA_ERR_NULL, "kmax_sq and c are required");

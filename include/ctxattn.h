@@ -106,7 +106,7 @@ ca_status ring_attn_step(const void* q, ca_strides q_strides,
  * "Global key max" (all_reduce(max) across the ring). On one device the
  * all-reduce is the max-fold over chunks: accumulate = 0 overwrites kmax_sq with
  * this chunk's maxima, accumulate = 1 folds them into kmax_sq by max.
- *   k        [B, S, H, D], strides ks
+ *   k        [B, S, H, D], strides ks; D a multiple of 8 in [8, 128]
  *   kmax_sq  IN/OUT [B, H] fp32
  */
 ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, int H, int D,
@@ -117,7 +117,7 @@ ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, 
  * Source: kernel reference page, Design "Picking a max that is safe without
  * measuring it" (Cauchy-Schwarz: c_i >= every score of row i) and Implementation
  * "Assembling the bound" (one square root of scale^2 * kmax_sq * |q_i|^2).
- *   q        [B, Sq, H, D], strides qs
+ *   q        [B, Sq, H, D], strides qs; D a multiple of 8 in [8, 128]
  *   kmax_sq  [B, H] fp32 (from key_sqnorm_max over every chunk of the ring)
  *   c        OUT [B, H, Sq] fp32
  */

@@ -87,10 +87,12 @@ def test_step_rejects_bad_arguments(dev):
         ca.ring_attn_step(q, k, v, mask=5)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
-def test_const_max_bound_matches_oracle(dev, dtype, D):
+@pytest.mark.parametrize("dtype,D,S,H", [("bf16", 128, 150, 3), ("fp32", 64, 150, 3), ("bf16", 128, 2001, 5),
+                                         ("fp32", 128, 1203, 3)])
+def test_const_max_bound_matches_oracle(dev, dtype, D, S, H):
     ca = _ca()
-    q, k, _ = _inputs(dev, 2, 150, 3, D, dtype, 400)
+    say(f"bound dtype={dtype} D={D} S={S} H={H}")
+    q, k, _ = _inputs(dev, 2, S, H, D, dtype, 400)
     chunks = [k[:, :40], k[:, 40:41], k[:, 41:]]
     km = None
     for r, kc in enumerate(chunks):
@@ -99,7 +101,7 @@ def test_const_max_bound_matches_oracle(dev, dtype, D):
     torch.cuda.synchronize()
     scale = oracle.default_scale(D)
     for b in range(2):
-        for h in range(3):
+        for h in range(H):
             rc, rk = oracle.const_max_bound(q[b, :, h], [kc[b, :, h] for kc in chunks], scale)
             assert abs(float(km[b, h]) - rk) <= 1e-5 * rk
             assert np.allclose(to_np(c[b, h]), rc, rtol=2e-6, atol=1e-6)
