@@ -118,9 +118,11 @@ def headline(args, torch, ca, workloads, gen, dev):
                      "traffic": traffic("attn_step_bf16/wan22_cp8_online"),
                      "kernel": "attn_step_bf16 (ring_attn_step)",
                      "per_launch": f"{flops_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
-                     "note": "consecutive ring steps run on two compute streams and overlap, so each "
-                             "launch's duration includes sharing the GPU with its neighbour step; "
-                             "steps_union_tflops is the step kernels' throughput over their union"},
+                     "note": ("steps run one after another on one compute stream, each on a key-split "
+                              "grid that fills the device" if rp.aux_stream is None else
+                              "consecutive ring steps run on two compute streams and overlap, so each "
+                              "launch's duration includes sharing the GPU with its neighbour step; "
+                              "steps_union_tflops is the step kernels' throughput over their union")},
         "steps_union_tflops": round(8 * flops_step / (union_ms * 1e-3) / 1e12, 2),
         "inputs": (q, kp, vp),
     }

@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 # Every symbol include/ctxattn.h declares.
 EXPORTS = (
-    "ring_attn_step", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "lse_merge",
+    "ring_attn_step", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "lse_merge",
     "dcp_decode_partial", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error", "ca_version",
 )
 
@@ -38,11 +38,13 @@ _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
 
 SIGNATURES = {
-    "ring_attn_step": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp],
+    "ring_attn_step": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _sz,
+                       _vp],
+    "ring_attn_workspace_size": [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
     "key_sqnorm_max": [_vp, ca_strides, _i, _i, _i, _i, _i, _vp, _i, _vp],
     "const_max_bound": [_vp, ca_strides, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp],
     "ring_attn_const_max_step": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
-                                 _vp, _i, _vp, _vp],
+                                 _vp, _i, _vp, _vp, _sz, _vp],
     "lse_merge": [_i, _vp, _vp, _i64, _i, _vp, _i, _vp, _vp],
     "dcp_decode_partial": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp],
     "dcp_decode_workspace_size": [_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],

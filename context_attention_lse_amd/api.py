@@ -54,10 +54,36 @@ def _scale(scale):
     return 0.0 if scale is None else float(scale)
 
 
-def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, stream=None):
+def ring_attn_workspace_size(dtype, B, H, Sq, Sk, D, mask="none") -> int:
+    """Bytes of key-split workspace a step of these sizes needs on the current device (0: none)."""
+    n = ctypes.c_size_t(0)
+    code = _DT[dtype] if not isinstance(dtype, int) else dtype
+    _lib.call("ring_attn_workspace_size", code, B, H, Sq, Sk, D, MASKS[mask] if isinstance(mask, str) else int(mask),
+              ctypes.byref(n))
+    return int(n.value)
+
+
+def step_workspace(q, k, mask="none"):
+    """A zeroed key-split workspace for steps of q's and k's shapes, or None if they never split.
+    Reusable by any number of such steps in stream order; concurrent steps need their own."""
+    B, Sq, H, D = q.shape
+    n = ring_attn_workspace_size(q.dtype, B, H, Sq, k.shape[1], D, mask)
+    return torch.zeros(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if not (workspace.is_contiguous() and workspace.dtype == torch.uint8):
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return _ptr(workspace), workspace.numel()
+
+
+def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspace=None, stream=None):
     """Online-max attention of q [B, Sq, H, D] against one K/V chunk [B, Sk, H, D].
-    Returns (o [B, H, Sq, D] fp32, lse [B, H, Sq] fp32)."""
-    _check_cuda(q, k, v, out, lse)
+    Returns (o [B, H, Sq, D] fp32, lse [B, H, Sq] fp32). With ``workspace`` (from
+    step_workspace) the key range is split over a grid that fills the device."""
+    _check_cuda(q, k, v, out, lse, workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
@@ -72,7 +98,7 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, stream=
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     _lib.call("ring_attn_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
               B, H, Sq, Sk, D, _scale(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
-              _ptr(out), _ptr(lse), _stream(stream))
+              _ptr(out), _ptr(lse), *_ws(workspace), _stream(stream))
     return out, lse
 
 
@@ -106,10 +132,11 @@ def const_max_acc_size(B, H, Sq, D) -> int:
 
 
 def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dtype=torch.float32,
-                             scale=None, stream=None):
+                             scale=None, workspace=None, stream=None):
     """One const-max ring step. acc: fp32 tensor of const_max_acc_size floats (None allowed
-    when phase == INIT|FINAL). On the FINAL phase returns (o [B, H, Sq, D], lse [B, H, Sq])."""
-    _check_cuda(q, k, v, c, acc, out, lse)
+    when phase == INIT|FINAL). On the FINAL phase returns (o [B, H, Sq, D], lse [B, H, Sq]).
+    ``workspace`` as for ring_attn_step."""
+    _check_cuda(q, k, v, c, acc, out, lse, workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
@@ -127,7 +154,7 @@ def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dty
     _lib.call("ring_attn_const_max_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
               B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase),
               _ptr(out) if final else None, _DT.get(out.dtype, CA_FP32) if final else CA_FP32,
-              _ptr(lse) if final else None, _stream(stream))
+              _ptr(lse) if final else None, *_ws(workspace), _stream(stream))
     return (out, lse) if final else None
 
 

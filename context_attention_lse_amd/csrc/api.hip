@@ -74,6 +74,20 @@ ca_status attn_common(const void* q, ca_strides qs, const void* k, const void* v
   return CA_OK;
 }
 
+// Hands a caller workspace to the bf16 step, which then splits key ranges across a grid
+// that fills the device. NULL keeps one workgroup per query tile; the fp32 step never splits.
+ca_status attach_workspace(ctxattn::AttnArgs& a, int dtype, void* ws, size_t ws_bytes) {
+  if (!ws || dtype != CA_BF16) return CA_OK;
+  const size_t need = ctxattn::attn_bf16_workspace_bytes(a.B, a.H, a.Sq, a.Sk, a.mask);
+  if (need == 0) return CA_OK;
+  if (ws_bytes < need)
+    return fail(CA_ERR_WORKSPACE, "step workspace has %zu bytes, the call needs %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(CA_ERR_SHAPE, "step workspace must be 256-byte aligned");
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return CA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,7 +98,7 @@ const char* ca_version(void) { return "0.1.0"; }
 
 ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype, int B,
                          int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o, float* lse,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
   CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
   if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
   if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
@@ -98,9 +112,21 @@ ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void
   a.sl2e = a.scale * ctxattn::kLog2e;
   a.mask = mask;
   a.o = o; a.lse = lse;
+  CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
   return hip_status(e, "ring_attn_step launch");
+}
+
+ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask, size_t* bytes) {
+  if (!bytes) return fail(CA_ERR_NULL, "bytes is NULL");
+  *bytes = 0;
+  CA_TRY(check_dtype(dtype));
+  CA_TRY(check_head_dim(dtype, D));
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(CA_ERR_SHAPE, "negative size");
+  if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
+  if (dtype == CA_BF16) *bytes = ctxattn::attn_bf16_workspace_bytes(B, H, Sq, Sk, mask);
+  return hip_status(hipSuccess, "");
 }
 
 ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, int H, int D, float* kmax_sq,
@@ -132,7 +158,7 @@ ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq
 ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs,
                                    int dtype, int B, int H, int Sq, int Sk, int D, float softmax_scale,
                                    const float* c, float* acc, int phase, void* o, int o_dtype, float* lse,
-                                   void* stream) {
+                                   void* workspace, size_t workspace_bytes, void* stream) {
   CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
   if (phase < 0 || phase > (CA_PHASE_INIT | CA_PHASE_FINAL)) return fail(CA_ERR_SHAPE, "unknown phase %d", phase);
   if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
@@ -154,6 +180,7 @@ ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, 
   a.mask = CA_MASK_NONE;
   a.c = c; a.acc = acc; a.phase = phase;
   a.o_cm = o; a.o_cm_bf16 = (o_dtype == CA_BF16); a.lse_cm = lse;
+  CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, s);
   return hip_status(e, "ring_attn_const_max_step launch");

@@ -30,6 +30,18 @@
 //  * softmax uses exp2 with scale*log2(e) folded into one FMA per score; the running max
 //    moves only when a tile's max exceeds it by more than 8 (log2 units), so the
 //    accumulator rescale is rare and probabilities stay <= 256.
+//
+// Key-split schedule (when the caller passes a workspace and one workgroup per query tile
+// would leave over a tenth of the device's workgroup slots idle, e.g. 320 tiles on 512
+// slots): the (query tile, key tile) iterations of the whole call are laid end to end and
+// cut into G equal ranges, G = the number of workgroups the device holds at once (or fewer
+// for small calls), so every workgroup does the same work and the grid fills the machine.
+// A query tile whose keys fall into several ranges is computed in segments; each segment
+// leaves its unnormalised partial (rows' output, running max and row sum) in the workspace
+// and bumps the tile's counter, and the workgroup that brings the counter to the segment
+// count combines the segments in key order and writes the result. No workgroup ever waits
+// for another. The combiner resets the counter, so a workspace is ready for the next call.
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -153,10 +165,11 @@ __device__ __forceinline__ void apply_mask(floatx16& s, int key0, int hl, int ro
   }
 }
 
+// Final output of one lane's half row: o (unnormalised), the full row sum lrow, the running
+// max m_ref (online) or the bound c2 (const-max), both in log2 units.
 template <int MODE>
 __device__ __forceinline__ void store_rows(const AttnArgs& a, int64_t bh, int Sq, int row, int hl,
-                                           floatx16 (&o)[4], float l_part, float m_ref, float c2) {
-  const float lrow = l_part + __shfl_xor(l_part, 32);
+                                           floatx16 (&o)[4], float lrow, float m_ref, float c2) {
   if (row >= Sq) return;
   const int64_t rowidx = bh * Sq + row;
   // o[db][r] is O[row][d] for d = 32*db + 8*(r/4) + 4*hl + r%4: four consecutive d per float4.
@@ -223,61 +236,59 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int64_t bh, int Sq
   }
 }
 
-template <int MODE, int MASK>
+// Key tiles that query tile qb iterates over: every tile of the chunk, or under a causal
+// mask every tile up to the diagonal block (keys below (qb + 1) * BQ).
+__host__ __device__ inline int tile_iters(int mask, int qb, int nkt) {
+  if (mask == CA_MASK_NONE) return nkt;
+  return min(nkt, (BQ / BK) * (qb + 1));
+}
+
+// Iterations of query tiles [0, qb) of one (batch, head). Causal: the first nkt / (BQ/BK)
+// tiles grow by BQ/BK key tiles each, the rest see the whole chunk.
+__host__ __device__ inline int64_t tiles_prefix(int mask, int qb, int nkt) {
+  if (mask == CA_MASK_NONE) return int64_t(qb) * nkt;
+  constexpr int R = BQ / BK;
+  const int64_t m = min(qb, nkt / R);
+  return R * m * (m + 1) / 2 + int64_t(nkt) * (qb - m);
+}
+
+// Key-split schedule and its workspace (see the file comment).
+struct Split {
+  int* cnt;        // [B*H*nqb][NW] arrivals per (query tile, wave); zero between calls
+  float* po;       // [2G][NW][64 values][64 lanes] unnormalised partial outputs, one record per
+                   // segment and wave, lane-interleaved so every access is one contiguous 256 B
+  float* pml;      // [2G][NW][2][64 lanes] partial running max (log2 units) and full row sum
+  int G;           // logical workgroups
+  int64_t T;       // iterations (query tile x key tile) of the whole call
+  int64_t per_bh;  // iterations of one (batch, head)
+};
+
+__device__ __forceinline__ int64_t range_begin(const Split& sp, int w) { return sp.T * w / sp.G; }
+// The workgroup whose range holds iteration x: the largest w with range_begin(w) <= x.
+__device__ __forceinline__ int range_owner(const Split& sp, int64_t x) {
+  return int((int64_t(sp.G) * (x + 1) + sp.T - 1) / sp.T) - 1;
+}
+// Record of workgroup w's segment of the tile starting at iteration tile_start: its first
+// segment (slot 2w) unless the tile began before w's range (then its last, 2w + 1).
+__device__ __forceinline__ int64_t segment_slot(const Split& sp, int w, int64_t tile_start) {
+  return 2 * int64_t(w) + (range_begin(sp, w) >= tile_start ? 0 : 1);
+}
+
+template <int MODE, int MASK, bool SPLIT>
 __global__ __launch_bounds__(NT, 2)
-void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
+void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x, nwork);
   if (logical < 0) return;
-  const int bh = logical / nqb;
-  int qb = logical - bh * nqb;
-  if (MASK != CA_MASK_NONE) qb = nqb - 1 - qb;   // heavy (late) query blocks first
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int li = lane & 31;
   const int hl = lane >> 5;
-  const int row_w0 = qb * BQ + w * 32;   // first query row of this wave
-  const int row = row_w0 + li;           // this lane's query row
   const int Sq = a.Sq, Sk = a.Sk;
-
-  // Q fragment: row, d = c*16 + 8*hl .. +7 (B operand of S^T = K Q^T). Rows past Sq re-read
-  // the last row; their outputs are never stored.
-  bf16x8 q[8];
-  {
-    const uint16_t* qr = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh + hl * 8 +
-                         int64_t(min(row, Sq - 1)) * a.qss;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) q[c] = *reinterpret_cast<const bf16x8*>(qr + c * 16);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) settle(q[c]);
-  }
-
-  const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh);
-  const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + h * a.ksh);
   const int64_t kss_bytes = a.kss * 2;
-
-  int kend = Sk;
-  if (MASK != CA_MASK_NONE) kend = min(Sk, qb * BQ + BQ);
-  const int nkt = (kend + BK - 1) / BK;
-
-  floatx16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-
-  float m_ref = -INFINITY;   // running reference max (log2 units), online mode
-  float l_part = 0.0f;       // this lane's share of the row sum
-  float c2 = 0.0f;           // const-max bound in log2 units
-  if (MODE == MODE_CONSTMAX) {
-    c2 = a.c[int64_t(bh) * Sq + min(row, Sq - 1)] * kLog2e;
-    settle(c2);
-  }
   const float sl2e = a.sl2e;
 
   // Per-lane copy offsets (bytes from the tile's first key): copy u of this wave fills LDS
@@ -314,118 +325,325 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nwork) {
     for (int db = 0; db < 4; ++db) vr[db] = base + 32 * (db ^ t);
   }
 
-  // A tile is skipped by a wave when causality hides all of its keys from all 32 rows.
-  auto skip_tile = [&](int t) -> bool {
-    if (MASK == CA_MASK_CAUSAL_INCL) return t * BK > row_w0 + 31;
-    if (MASK == CA_MASK_CAUSAL_STRICT) return t * BK >= row_w0 + 31;
-    return false;
-  };
-
-  // Issues the copies of tile t into LDS buffer BUF. The last tile of a chunk clamps its rows
-  // to the last key (their scores are masked, their values meet p = 0).
-  auto issue = [&](auto bufc, int t) {
-    constexpr int BUF = decltype(bufc)::value;
-    const int key0 = t * BK;
-    const char* kt = kbase + key0 * kss_bytes;
-    const char* vt = vbase + key0 * kss_bytes;
-    const bool full = key0 + BK <= Sk;
-#pragma unroll
-    for (int u = 0; u < COPIES; ++u) {
-      uint32_t ko = koff[u], vo = voff[u];
-      if (!full) {
-        const int rr = min(crow[u], Sk - 1 - key0);
-        const int p = lane & 15;
-        ko = uint32_t(rr * kss_bytes) + uint32_t((p ^ k_swz(crow[u])) << 4);
-        vo = uint32_t(rr * kss_bytes) + uint32_t((p ^ v_swz(crow[u])) << 4);
+  int64_t it = 0, it_end = 1;
+  if (SPLIT) {
+    it = range_begin(sp, logical);
+    it_end = range_begin(sp, logical + 1);
+  }
+  bool first_segment = true;
+  while (it < it_end) {
+    // ---- which query tile, and which of its key tiles, this segment covers
+    int bh, qb, k0, k1;
+    int64_t tile_start = 0;
+    if (SPLIT) {
+      bh = int(it / sp.per_bh);
+      const int64_t r = it - int64_t(bh) * sp.per_bh;
+      if (MASK == CA_MASK_NONE) {
+        qb = int(r / nkt);
+      } else {
+        int lo = 0, hi = nqb - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (tiles_prefix(MASK, mid, nkt) <= r) lo = mid; else hi = mid - 1;
+        }
+        qb = lo;
       }
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + BUF * TILE_BYTES + (w * COPIES + u) * 1024);
-      copy16_to_lds(kt, ko, dst);
-      copy16_to_lds(vt, vo, dst + V_OFF);
+      tile_start = int64_t(bh) * sp.per_bh + tiles_prefix(MASK, qb, nkt);
+      const int64_t seg_end = min(it_end, tile_start + tile_iters(MASK, qb, nkt));
+      k0 = int(it - tile_start);
+      k1 = int(seg_end - tile_start);
+      it = seg_end;
+    } else {
+      bh = logical / nqb;
+      qb = logical - bh * nqb;
+      if (MASK != CA_MASK_NONE) qb = nqb - 1 - qb;   // heavy (late) query blocks first
+      k0 = 0;
+      k1 = tile_iters(MASK, qb, nkt);
+      it = it_end;
     }
-  };
+    if (!first_segment) __syncthreads();   // every wave is done with the LDS buffers and stores
+    first_segment = false;
 
-  // One tile: wait for its copies, launch tile t+2's copies, compute.
-  auto step = [&](auto bufc, int t) {
-    constexpr int BUF = decltype(bufc)::value;
-    constexpr int BUF2 = (BUF + 2) % NBUF;
-    wait_tile_and_barrier(t + 1 < nkt);
-    if (t + 2 < nkt) issue(std::integral_constant<int, BUF2>{}, t + 2);
-    if (skip_tile(t)) return;
-    const int key0 = t * BK;
-    // All fragment reads up front: K first (QK^T waits for those only), then V, whose
-    // latency hides behind QK^T and the softmax.
-    bf16x8 ka[8];
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const int row_w0 = qb * BQ + w * 32;   // first query row of this wave
+    const int row = row_w0 + li;           // this lane's query row
+
+    // Q fragment: row, d = c*16 + 8*hl .. +7 (B operand of S^T = K Q^T). Rows past Sq re-read
+    // the last row; their outputs are never stored.
+    bf16x8 q[8];
+    {
+      const uint16_t* qr = static_cast<const uint16_t*>(a.q) + b * a.qsb + h * a.qsh + hl * 8 +
+                           int64_t(min(row, Sq - 1)) * a.qss;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) ka[c] = lds_read16<BUF * TILE_BYTES>(lds, kr[c]);
-    bf16x8 va[8];
+      for (int c = 0; c < 8; ++c) q[c] = *reinterpret_cast<const bf16x8*>(qr + c * 16);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      va[db * 2] = lds_read_tr<V_OFF + BUF * TILE_BYTES>(lds, vr[db]);
-      va[db * 2 + 1] = lds_read_tr<V_OFF + BUF * TILE_BYTES + 16 * ROW * 2>(lds, vr[db]);
+      for (int c = 0; c < 8; ++c) settle(q[c]);
     }
-    __builtin_amdgcn_sched_barrier(0);   // every fragment read is issued before the first MFMA
-    floatx16 s;
+
+    const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh);
+    const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + h * a.ksh);
+    const int nk = k1 - k0;   // key tiles of this segment
+
+    floatx16 o[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
-    // s[r] is the raw score q_row . k_j for key j = key0 + 8*(r/4) + 4*hl + r%4
-    bool need_mask = key0 + BK > Sk;
-    if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
-    if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
-    if (need_mask) apply_mask<MASK>(s, key0, hl, row, Sk);
-    float mu;
-    if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
-    else mu = c2;
-    bf16x8 p[2];
-    // The softmax runs at raised wave priority: the two waves sharing a SIMD then tend to
-    // alternate, one on the VALU while the other keeps the matrix core busy.
-    __builtin_amdgcn_s_setprio(2);
-    exp_pack(s, sl2e, mu, p, l_part);
-    __builtin_amdgcn_s_setprio(0);
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+
+    float m_ref = -INFINITY;   // running reference max (log2 units), online mode
+    float l_part = 0.0f;       // this lane's share of the row sum
+    float c2 = 0.0f;           // const-max bound in log2 units
+    if (MODE == MODE_CONSTMAX) {
+      c2 = a.c[int64_t(bh) * Sq + min(row, Sq - 1)] * kLog2e;
+      settle(c2);
+    }
+
+    // A tile is skipped by a wave when causality hides all of its keys from all 32 rows.
+    auto skip_tile = [&](int t) -> bool {
+      if (MASK == CA_MASK_CAUSAL_INCL) return t * BK > row_w0 + 31;
+      if (MASK == CA_MASK_CAUSAL_STRICT) return t * BK >= row_w0 + 31;
+      return false;
+    };
+
+    // Issues the copies of key tile t into LDS buffer BUF. The last tile of a chunk clamps its
+    // rows to the last key (their scores are masked, their values meet p = 0).
+    auto issue = [&](auto bufc, int t) {
+      constexpr int BUF = decltype(bufc)::value;
+      const int key0 = t * BK;
+      const char* kt = kbase + key0 * kss_bytes;
+      const char* vt = vbase + key0 * kss_bytes;
+      const bool full = key0 + BK <= Sk;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)   // kc outer: consecutive MFMAs hit different accumulators
+      for (int u = 0; u < COPIES; ++u) {
+        uint32_t ko = koff[u], vo = voff[u];
+        if (!full) {
+          const int rr = min(crow[u], Sk - 1 - key0);
+          const int p = lane & 15;
+          ko = uint32_t(rr * kss_bytes) + uint32_t((p ^ k_swz(crow[u])) << 4);
+          vo = uint32_t(rr * kss_bytes) + uint32_t((p ^ v_swz(crow[u])) << 4);
+        }
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + BUF * TILE_BYTES + (w * COPIES + u) * 1024);
+        copy16_to_lds(kt, ko, dst);
+        copy16_to_lds(vt, vo, dst + V_OFF);
+      }
+    };
+
+    // The segment's i-th key tile (key tile k0 + i): wait for its copies, launch the copies
+    // of tile i+2, compute.
+    auto step = [&](auto bufc, int i) {
+      constexpr int BUF = decltype(bufc)::value;
+      constexpr int BUF2 = (BUF + 2) % NBUF;
+      wait_tile_and_barrier(i + 1 < nk);
+      if (i + 2 < nk) issue(std::integral_constant<int, BUF2>{}, k0 + i + 2);
+      const int t = k0 + i;
+      if (skip_tile(t)) return;
+      const int key0 = t * BK;
+      // All fragment reads up front: K first (QK^T waits for those only), then V, whose
+      // latency hides behind QK^T and the softmax.
+      bf16x8 ka[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ka[c] = lds_read16<BUF * TILE_BYTES>(lds, kr[c]);
+      bf16x8 va[8];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        va[db * 2] = lds_read_tr<V_OFF + BUF * TILE_BYTES>(lds, vr[db]);
+        va[db * 2 + 1] = lds_read_tr<V_OFF + BUF * TILE_BYTES + 16 * ROW * 2>(lds, vr[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // every fragment read is issued before the first MFMA
+      floatx16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
+      // s[r] is the raw score q_row . k_j for key j = key0 + 8*(r/4) + 4*hl + r%4
+      bool need_mask = key0 + BK > Sk;
+      if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
+      if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
+      if (need_mask) apply_mask<MASK>(s, key0, hl, row, Sk);
+      float mu;
+      if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
+      else mu = c2;
+      bf16x8 p[2];
+      // The softmax runs at raised wave priority: the two waves sharing a SIMD then tend to
+      // alternate, one on the VALU while the other keeps the matrix core busy.
+      __builtin_amdgcn_s_setprio(2);
+      exp_pack(s, sl2e, mu, p, l_part);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)   // kc outer: consecutive MFMAs hit different accumulators
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
+    };
+
+    if (nk > 0) issue(std::integral_constant<int, 0>{}, k0);
+    if (nk > 1) issue(std::integral_constant<int, 1>{}, k0 + 1);
+    for (int i = 0; i < nk; i += NBUF) {
+      step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < nk) step(std::integral_constant<int, 1>{}, i + 1);
+      if (i + 2 < nk) step(std::integral_constant<int, 2>{}, i + 2);
+    }
+
+    const float lrow = l_part + __shfl_xor(l_part, 32);
+    if (!SPLIT) {
+      store_rows<MODE>(a, bh, Sq, row, hl, o, lrow, m_ref, c2);
+      continue;
+    }
+    const int tile_iters_n = tile_iters(MASK, qb, nkt);
+    const int w_first = range_owner(sp, tile_start);
+    const int w_last = range_owner(sp, tile_start + tile_iters_n - 1);
+    if (w_first == w_last) {   // the whole tile lies in this workgroup's range
+      store_rows<MODE>(a, bh, Sq, row, hl, o, lrow, m_ref, c2);
+      continue;
+    }
+
+    // ---- publish this segment's partial, count it; the last arrival combines all of them.
+    // Records move through agent-coherent accesses (relaxed agent-scope atomic stores and
+    // loads), so no L2 write-back or invalidation is needed: the stores have completed
+    // (vmcnt 0) before the counter moves, and the combiner loads only after it has seen the
+    // final count.
+    {
+      const int64_t rec = segment_slot(sp, logical, tile_start) * NW + w;
+      float* po = sp.po + rec * (64 * 64) + lane;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
-  };
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(po + (db * 16 + r) * 64, o[db][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sp.pml + rec * 128 + lane, m_ref, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sp.pml + rec * 128 + 64 + lane, lrow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int* ctr = sp.cnt + (int64_t(bh) * nqb + qb) * NW + w;
+    int seen = 0;
+    if (lane == 0) seen = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    seen = __shfl(seen, 0);
+    if (seen != w_last - w_first) continue;   // another segment is still running
 
-  if (nkt > 0) issue(std::integral_constant<int, 0>{}, 0);
-  if (nkt > 1) issue(std::integral_constant<int, 1>{}, 1);
-  for (int t = 0; t < nkt; t += NBUF) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < nkt) step(std::integral_constant<int, 1>{}, t + 1);
-    if (t + 2 < nkt) step(std::integral_constant<int, 2>{}, t + 2);
+    if (lane == 0) __hip_atomic_exchange(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+    float M = -INFINITY;
+    if (MODE == MODE_ONLINE)
+      for (int wq = w_first; wq <= w_last; ++wq)
+        M = fmaxf(M, __hip_atomic_load(sp.pml + (segment_slot(sp, wq, tile_start) * NW + w) * 128 + lane,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float L = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    for (int wq = w_first; wq <= w_last; ++wq) {   // key order: deterministic sums
+      const int64_t rec = segment_slot(sp, wq, tile_start) * NW + w;
+      float wt = 1.0f;
+      if (MODE == MODE_ONLINE) {
+        const float mq = __hip_atomic_load(sp.pml + rec * 128 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wt = mq == -INFINITY ? 0.0f : exp2f(mq - M);
+      }
+      L += wt * __hip_atomic_load(sp.pml + rec * 128 + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float* po = sp.po + rec * (64 * 64) + lane;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[db][r] += wt * __hip_atomic_load(po + (db * 16 + r) * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store_rows<MODE>(a, bh, Sq, row, hl, o, L, M, c2);
   }
-
-  store_rows<MODE>(a, bh, Sq, row, hl, o, l_part, m_ref, c2);
 }
 
-template <int MODE, int MASK>
-hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
+// Workgroups resident at once on the current device (two per CU).
+int resident_workgroups() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cache[dev] = 2 * cus;
+  }
+  return cache[dev];
+}
+
+constexpr int64_t kMinItersPerWorkgroup = 8;
+// Splitting pays where one workgroup per query tile would leave more than this share of the
+// device's workgroup slots idle over the call (the last, partly filled round of tiles).
+constexpr double kMaxIdleShare = 0.10;
+
+struct Plan {
+  int nqb, nkt, G;
+  int64_t per_bh, T;
+  bool split;      // key-split schedule chosen (needs a workspace)
+  size_t cnt_bytes, po_bytes, pml_bytes;
+  size_t bytes() const { return split ? cnt_bytes + po_bytes + pml_bytes : 0; }
+};
+
+Plan make_plan(int B, int H, int Sq, int Sk, int mask) {
+  Plan p{};
+  p.nqb = (Sq + BQ - 1) / BQ;
+  p.nkt = (Sk + BK - 1) / BK;
+  p.per_bh = tiles_prefix(mask, p.nqb, p.nkt);
+  p.T = int64_t(B) * H * p.per_bh;
+  if (p.T == 0) return p;
+  const int64_t slots = resident_workgroups();
+  const int64_t tiles = int64_t(B) * H * p.nqb;
+  const int64_t rounds = (tiles + slots - 1) / slots;
+  p.split = double(rounds * slots - tiles) > kMaxIdleShare * double(rounds * slots);
+  if (!p.split) return p;
+  const int64_t g = std::min<int64_t>(slots, (p.T + kMinItersPerWorkgroup - 1) / kMinItersPerWorkgroup);
+  p.G = int(std::max<int64_t>(1, g));
+  p.cnt_bytes = (size_t(B) * H * p.nqb * NW * sizeof(int) + 255) & ~size_t(255);
+  p.po_bytes = size_t(2) * p.G * NW * 64 * 64 * sizeof(float);
+  p.pml_bytes = size_t(2) * p.G * NW * 128 * sizeof(float);
+  return p;
+}
+
+template <int MODE, int MASK, bool SPLIT>
+hipError_t launch_one(const AttnArgs& a, const Plan& p, hipStream_t s) {
   static bool attr_set = false;   // dynamic LDS above 64 KB must be allowed once
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_step_bf16<MODE, MASK>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_step_bf16<MODE, MASK, SPLIT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(LDS_BYTES));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int nqb = (a.Sq + BQ - 1) / BQ;
-  const int nwork = a.B * a.H * nqb;
+  Split sp{};
+  int nwork = a.B * a.H * p.nqb;
+  if (SPLIT) {
+    char* ws = static_cast<char*>(a.ws);
+    sp.cnt = reinterpret_cast<int*>(ws);
+    sp.po = reinterpret_cast<float*>(ws + p.cnt_bytes);
+    sp.pml = reinterpret_cast<float*>(ws + p.cnt_bytes + p.po_bytes);
+    sp.G = p.G;
+    sp.T = p.T;
+    sp.per_bh = p.per_bh;
+    nwork = p.G;
+  }
   if (nwork == 0) return hipSuccess;
   const int grid = round_up8(nwork);
-  hipLaunchKernelGGL((attn_step_bf16<MODE, MASK>), dim3(grid), dim3(NT), LDS_BYTES, s, a, nqb, nwork);
+  hipLaunchKernelGGL((attn_step_bf16<MODE, MASK, SPLIT>), dim3(grid), dim3(NT), LDS_BYTES, s, a, p.nqb, p.nkt,
+                     nwork, sp);
   return hipGetLastError();
+}
+
+template <int MODE, int MASK>
+hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
+  const Plan p = make_plan(a.B, a.H, a.Sq, a.Sk, MASK);
+  if (a.ws != nullptr && p.split) return launch_one<MODE, MASK, true>(a, p, s);
+  return launch_one<MODE, MASK, false>(a, p, s);
 }
 
 }  // namespace
 
+size_t attn_bf16_workspace_bytes(int B, int H, int Sq, int Sk, int mask) {
+  return make_plan(B, H, Sq, Sk, mask).bytes();
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s) {
-  if (const_max) return launch_one<MODE_CONSTMAX, CA_MASK_NONE>(a, s);
+  if (const_max) return launch_mode<MODE_CONSTMAX, CA_MASK_NONE>(a, s);
   switch (a.mask) {
-    case CA_MASK_CAUSAL_INCL: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_INCL>(a, s);
-    case CA_MASK_CAUSAL_STRICT: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_STRICT>(a, s);
-    default: return launch_one<MODE_ONLINE, CA_MASK_NONE>(a, s);
+    case CA_MASK_CAUSAL_INCL: return launch_mode<MODE_ONLINE, CA_MASK_CAUSAL_INCL>(a, s);
+    case CA_MASK_CAUSAL_STRICT: return launch_mode<MODE_ONLINE, CA_MASK_CAUSAL_STRICT>(a, s);
+    default: return launch_mode<MODE_ONLINE, CA_MASK_NONE>(a, s);
   }
 }
 

@@ -71,17 +71,22 @@ class RingPass:
     """One rank's share of ring attention: q resident, cp chunks arriving one per step.
 
     variant "online": every step emits a partial (o_s, lse_s) with ring_attn_step and
-                      the partials are merged once with lse_merge; steps alternate between
-                      two compute streams, so a step can start as soon as its chunk has
-                      arrived and fill the GPU while the previous step drains;
+                      the partials are merged once with lse_merge;
     variant "constmax": the bound is built from every chunk's key norms (the ring's
                       all_reduce(max) becomes a max-fold), then every step adds into one
                       fp32 accumulator and the last step normalises.
+
+    split=True gives the steps a key-split workspace where the library would split (query
+    tiles too few to fill the device), so each step's grid fills it; such steps run on one
+    compute stream by default. Otherwise steps keep one workgroup per query tile and online
+    steps alternate two compute streams, so a step can fill the CUs the previous one leaves
+    idle as it drains. On the Wan2.2 share (320 query tiles per step) the second form gives
+    the faster pass: the split kernel alone is faster, but the steps' overlap hides more.
     """
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
                  scale=None, prefetch_depth=2, out_dtype=torch.float32, copy_stream=None,
-                 compute_streams=None):
+                 compute_streams=None, split=False):
         if variant not in ("online", "constmax"):
             raise ValueError(f"unknown variant {variant!r}")
         if variant == "constmax" and causal:
@@ -103,12 +108,25 @@ class RingPass:
         self.kbuf = [torch.empty(chunk_shape, dtype=k_pool.dtype, device=dev) for _ in range(self.nbuf)]
         self.vbuf = [torch.empty(chunk_shape, dtype=v_pool.dtype, device=dev) for _ in range(self.nbuf)]
         self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device=dev)
-        if compute_streams is None:
-            compute_streams = 2 if variant == "online" else 1   # const-max steps fold in order
-        self.aux_stream = torch.cuda.Stream(device=dev) if compute_streams > 1 else None
         self.copied = [torch.cuda.Event() for _ in range(self.cp)]
         self.consumed = [torch.cuda.Event() for _ in range(self.cp)]
         self.masks = [step_mask(layout, causal, rank, ring_source_rank(rank, s, self.cp)) for s in range(self.cp)]
+        # the library splits key ranges only where query tiles alone would underfill the device
+        nbytes = 0
+        if split:
+            nbytes = max(api.ring_attn_workspace_size(q.dtype, B, H, Sq, chunk_shape[1], D, m)
+                         for m in set(x for x in self.masks if x is not None))
+        if compute_streams is None:
+            # const-max steps fold in order; split steps already fill the device
+            compute_streams = 2 if (variant == "online" and not nbytes) else 1
+        if variant == "constmax" and compute_streams > 1:
+            raise ValueError("const-max steps add into one accumulator and run on one stream")
+        self.aux_stream = torch.cuda.Stream(device=dev) if compute_streams > 1 else None
+        # one workspace per compute stream (concurrent steps may not share one)
+        self.ws = [None, None]
+        if nbytes:
+            self.ws = [torch.zeros(nbytes, dtype=torch.uint8, device=dev) for _ in range(compute_streams)]
+            self.ws += [self.ws[0]] * (2 - len(self.ws))
         self.live_steps = [s for s in range(self.cp) if self.masks[s] is not None]
         assert self.live_steps, "a rank always sees its own chunk"
         if variant == "online":
@@ -162,7 +180,9 @@ class RingPass:
                 # the buffer of step t was last read by step t - nbuf = s - 1
                 self.copy_stream.wait_event(self.consumed[s - 1])
                 self._issue_copy(t)
-            st = self.aux_stream if (self.aux_stream is not None and s % 2 == 1) else cs
+            second = self.aux_stream is not None and s % 2 == 1
+            st = self.aux_stream if second else cs
+            ws = self.ws[1 if second else 0]
             if s >= 1:
                 st.wait_event(self.copied[s])
             k, v = self._chunk(s)
@@ -172,12 +192,12 @@ class RingPass:
                 if self.variant == "online":
                     if self.masks[s] is not None:
                         api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s],
-                                           out=self.o_parts[slot], lse=self.lse_parts[slot])
+                                           out=self.o_parts[slot], lse=self.lse_parts[slot], workspace=ws)
                         slot += 1
                 else:
                     phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
                     api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out,
-                                                 lse=self.lse, scale=self.scale)
+                                                 lse=self.lse, scale=self.scale, workspace=ws)
                 if timing_events is not None:
                     timing_events[s][1].record(st)
             self.consumed[s].record(st)
@@ -191,12 +211,12 @@ class RingPass:
 
 
 def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous", causal=False,
-                   variant="online", scale=None, prefetch_depth=2):
+                   variant="online", scale=None, prefetch_depth=2, split=False):
     """Convenience: rank ``rank``'s output for global [B, S, H, D] inputs."""
     check_divisible(q_global.shape[1], cp)
     q = shard(q_global, cp, rank, layout)
     kp = chunk_pool(k_global, cp, layout)
     vp = chunk_pool(v_global, cp, layout)
     rp = RingPass(q, kp, vp, rank, layout=layout, causal=causal, variant=variant, scale=scale,
-                  prefetch_depth=prefetch_depth)
+                  prefetch_depth=prefetch_depth, split=split)
     return rp.run()

@@ -89,15 +89,37 @@ typedef struct {
  *   mask   ca_mask on local indices
  *   o      OUT [B, H, Sq, D] fp32, contiguous: softmax(s) @ v over visible keys
  *   lse    OUT [B, H, Sq] fp32, contiguous: log sum_j exp(scale * q_i . k_j)
+ *   workspace, workspace_bytes
+ *          optional device scratch (see ring_attn_workspace_size). NULL: one workgroup
+ *          per 128 query rows. Given, and the call is one that one workgroup per 128 rows
+ *          would leave the device's workgroup slots more than a tenth idle: the call's
+ *          (query tile, key tile) iterations are cut into equal ranges, one per workgroup
+ *          the device holds at once, and query tiles split between ranges are combined in
+ *          the library, in key order (results do not depend on timing). The workspace must
+ *          be 256-byte aligned and all zero before its first use; every call leaves it
+ *          ready for the next. Calls that may run at the same time need separate
+ *          workspaces. Ignored by the fp32 path and by calls that do not split.
  * Supported: D in {64, 128} (fp32), D == 128 (bf16); MHA (same H for q and kv).
  * Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
- * CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ * CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_WORKSPACE (too small), CA_ERR_HIP.
  */
 ca_status ring_attn_step(const void* q, ca_strides q_strides,
                          const void* k, const void* v, ca_strides kv_strides,
                          int dtype, int B, int H, int Sq, int Sk, int D,
                          float softmax_scale, int mask,
-                         float* o, float* lse, void* stream);
+                         float* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ring_attn_workspace_size -- bytes of step workspace that ring_attn_step and
+ * ring_attn_const_max_step (mask CA_MASK_NONE) need for these sizes on the CURRENT
+ * device (the split depends on its compute-unit count). 0: the call does not split
+ * (fp32, no key tiles, or enough query tiles to fill the device). The bytes are per-call
+ * scratch: split partials (2 * workgroups * 128 rows * (D + 2) fp32) and one counter per
+ * (query tile, wave).
+ */
+ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask,
+                                   size_t* bytes);
 
 /*
  * key_sqnorm_max -- per (b, h) maximum over the chunk's keys of |k_j|^2.
@@ -144,13 +166,16 @@ ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq
  *   o         OUT (FINAL only) [B, H, Sq, D], o_dtype CA_FP32 or CA_BF16:
  *             acc_o / max(acc_sum, 1e-37)
  *   lse       OUT (FINAL only, nullable) [B, H, Sq] fp32: c + log(max(acc_sum, 1e-37))
+ *   workspace, workspace_bytes   as ring_attn_step (size for mask CA_MASK_NONE); split
+ *             query tiles add their segments' sums in key order
  * Supported: as ring_attn_step.
  */
 ca_status ring_attn_const_max_step(const void* q, ca_strides q_strides,
                                    const void* k, const void* v, ca_strides kv_strides,
                                    int dtype, int B, int H, int Sq, int Sk, int D,
                                    float softmax_scale, const float* c, float* acc, int phase,
-                                   void* o, int o_dtype, float* lse, void* stream);
+                                   void* o, int o_dtype, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * lse_merge -- LSE-corrected merge of n partial attention results.

@@ -45,20 +45,20 @@ def test_rejections_without_gpu():
     lib = _lib.load()
     st = _lib.ca_strides(0, 128, 0)
     # unknown dtype
-    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, 9, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_DTYPE
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, 9, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_DTYPE
     # bf16 head_dim other than 128
-    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 96, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 96, 0.0, 0, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_UNSUPPORTED
     assert b"128" in lib.ca_last_error()
     # unknown mask
-    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 7, _fake(), _fake(), None) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 7, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_UNSUPPORTED
     # NULL inputs
-    assert lib.ring_attn_step(None, st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_NULL
+    assert lib.ring_attn_step(None, st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_NULL
     # misaligned q
-    assert lib.ring_attn_step(_fake(0x1002), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None) == _lib.CA_ERR_SHAPE
+    assert lib.ring_attn_step(_fake(0x1002), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_SHAPE
     # empty query shard is a no-op success
-    assert lib.ring_attn_step(None, st, None, None, st, _lib.CA_BF16, 1, 1, 0, 0, 128, 0.0, 0, None, None, None) == _lib.CA_OK
+    assert lib.ring_attn_step(None, st, None, None, st, _lib.CA_BF16, 1, 1, 0, 0, 128, 0.0, 0, None, None, None, 0, None) == _lib.CA_OK
     # const-max: middle phase without an accumulator
-    assert lib.ring_attn_const_max_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, _fake(), None, 0, None, 0, None, None) == _lib.CA_ERR_NULL
+    assert lib.ring_attn_const_max_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, _fake(), None, 0, None, 0, None, None, 0, None) == _lib.CA_ERR_NULL
     # merge: n = 0, unsupported D, overlapping output
     assert lib.lse_merge(0, _fake(), _fake(), 4, 128, _fake(0x9000), 1, None, None) == _lib.CA_ERR_SHAPE
     assert lib.lse_merge(2, _fake(), _fake(), 4, 96, _fake(0x9000), 1, None, None) == _lib.CA_ERR_UNSUPPORTED
@@ -75,3 +75,14 @@ def test_rejections_without_gpu():
     assert lib.kv_chunk_copy(_fake(0x1008), _fake(), _fake(), _fake(), 4096, None) == _lib.CA_ERR_SHAPE
     assert lib.kv_chunk_copy(_fake(), _fake(0x2000), _fake(0x3000), _fake(0x4000), 4100, None) == _lib.CA_ERR_SHAPE
     assert lib.kv_chunk_copy(None, None, None, None, 0, None) == _lib.CA_OK
+    # step workspace: fp32 never splits; bf16 needs one; too small a workspace is rejected
+    n = ctypes.c_size_t(1)
+    assert lib.ring_attn_workspace_size(_lib.CA_FP32, 1, 2, 300, 300, 64, 0, ctypes.byref(n)) == _lib.CA_OK
+    assert n.value == 0
+    assert lib.ring_attn_workspace_size(_lib.CA_BF16, 1, 2, 300, 300, 128, 2, ctypes.byref(n)) == _lib.CA_OK
+    assert n.value > 0
+    assert lib.ring_attn_workspace_size(_lib.CA_BF16, 1, 2, 300, 300, 128, 9, ctypes.byref(n)) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(),
+                              _fake(0x10000), 16, None) == _lib.CA_ERR_WORKSPACE
+    assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(),
+                              _fake(0x10010), 1 << 30, None) == _lib.CA_ERR_SHAPE   # misaligned workspace

@@ -48,22 +48,46 @@ def _allowed(mask, Sq, Sk):
     return None
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64), ("fp32", 128)])
+@pytest.mark.parametrize("dtype,D,split", [("bf16", 128, False), ("bf16", 128, True), ("fp32", 64, False),
+                                           ("fp32", 128, False)])
 @pytest.mark.parametrize("mask,Sq,Sk", [("none", 300, 200), ("none", 129, 1), ("causal_incl", 300, 300),
-                                        ("causal_strict", 300, 300)])
-def test_step_partial_matches_oracle(dev, dtype, D, mask, Sq, Sk):
+                                        ("causal_strict", 300, 300), ("none", 1000, 1003),
+                                        ("causal_incl", 1000, 1000), ("causal_strict", 1000, 1000)])
+def test_step_partial_matches_oracle(dev, dtype, D, split, mask, Sq, Sk):
     ca = _ca()
     B, H = 2, 3
-    say(f"step dtype={dtype} D={D} mask={mask} Sq={Sq} Sk={Sk}")
+    say(f"step dtype={dtype} D={D} split={split} mask={mask} Sq={Sq} Sk={Sk}")
     q, _, _ = _inputs(dev, B, Sq, H, D, dtype, 100)
     _, k, v = _inputs(dev, B, Sk, H, D, dtype, 200)
-    o, l = ca.ring_attn_step(q, k, v, mask=mask)
+    ws = ca.step_workspace(q, k, mask) if split else None
+    o, l = ca.ring_attn_step(q, k, v, mask=mask, workspace=ws)
     torch.cuda.synchronize()
     scale = oracle.default_scale(D)
     ro, rl = oracle.attention_heads(q, k, v, scale, allowed=_allowed(mask, Sq, Sk))
     check("step", o, l, ro, rl)
     if mask == "causal_strict":
         assert np.all(to_np(l)[:, :, 0] == -np.inf) and np.all(to_np(o)[:, :, 0] == 0)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal_incl", "causal_strict"])
+def test_split_step_is_deterministic_and_leaves_workspace_ready(dev, mask):
+    """Split tiles are combined in key order, so repeated calls give identical bits, and
+    each call resets its counters: a workspace serves calls of other shapes afterwards."""
+    ca = _ca()
+    q, k, v = _inputs(dev, 1, 777, 4, 128, "bf16", 150)
+    ws = ca.step_workspace(q, k, mask)
+    assert ws is not None
+    o1, l1 = (x.clone() for x in ca.ring_attn_step(q, k, v, mask=mask, workspace=ws))
+    for _ in range(3):
+        o2, l2 = ca.ring_attn_step(q, k, v, mask=mask, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert int(ws[:4 * 4 * 7 * 4].count_nonzero()) == 0      # every counter back at zero
+    small_q, small_k = q[:, :200, :2], k[:, :90, :2]
+    o3, l3 = ca.ring_attn_step(small_q, small_k, v[:, :90, :2], mask="none", workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_heads(small_q, small_k, v[:, :90, :2], oracle.default_scale(128))
+    check("reused workspace", o3, l3, ro, rl)
 
 
 def test_step_explicit_scale_and_empty_chunk(dev):
@@ -107,11 +131,11 @@ def test_const_max_bound_matches_oracle(dev, dtype, D, S, H):
             assert np.allclose(to_np(c[b, h]), rc, rtol=2e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,D,split", [("bf16", 128, False), ("bf16", 128, True), ("fp32", 64, False)])
 @pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
-def test_const_max_steps_match_oracle(dev, dtype, D, out_dtype):
+def test_const_max_steps_match_oracle(dev, dtype, D, split, out_dtype):
     ca = _ca()
-    say(f"const-max steps dtype={dtype} D={D} out={out_dtype}")
+    say(f"const-max steps dtype={dtype} D={D} split={split} out={out_dtype}")
     B, H, Sq = 1, 3, 260
     q, _, _ = _inputs(dev, B, Sq, H, D, dtype, 500)
     _, k, v = _inputs(dev, B, 405, H, D, dtype, 600)
@@ -125,9 +149,10 @@ def test_const_max_steps_match_oracle(dev, dtype, D, out_dtype):
     acc = torch.empty(ca.const_max_acc_size(B, H, Sq, D), dtype=torch.float32, device=dev)
     odt = gen.torch_dtype(out_dtype)
     o = l = None
+    ws = ca.step_workspace(q, k) if split else None
     for s in range(3):
         phase = (1 if s == 0 else 0) | (2 if s == 2 else 0)
-        res = ca.ring_attn_const_max_step(q, ks[s], vs[s], c, acc, phase, out_dtype=odt)
+        res = ca.ring_attn_const_max_step(q, ks[s], vs[s], c, acc, phase, out_dtype=odt, workspace=ws)
         if res is not None:
             o, l = res
     torch.cuda.synchronize()
@@ -207,7 +232,7 @@ def test_lse_merge_matches_oracle(dev):
 
 # ---------------------------------------------------------------- ring passes
 
-def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=None):
+def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=None, split=False):
     ca = _ca()
     wl = wl.scaled(S=S, **({"H": H} if H else {}))
     layout = layout or wl.layout
@@ -216,9 +241,10 @@ def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=
     scale = oracle.default_scale(wl.D)
     S_all = np.arange(S)
     for r in ranks:
-        say(f"ring {wl.name} S={S} cp={wl.cp} rank={r} variant={variant} layout={layout} causal={causal} depth={depth}")
+        say(f"ring {wl.name} S={S} cp={wl.cp} rank={r} variant={variant} layout={layout} causal={causal} "
+            f"depth={depth} split={split}")
         o, l = ca.ring.ring_attention(t["q"], t["k"], t["v"], wl.cp, r, layout=layout, causal=causal,
-                                      variant=variant, prefetch_depth=depth)
+                                      variant=variant, prefetch_depth=depth, split=split)
         torch.cuda.synchronize()
         rows = (oracle.contiguous_tokens if layout == "contiguous" else oracle.striped_tokens)(S, wl.cp, r)
         allowed = oracle.causal_allowed(rows, S_all) if causal else None
@@ -257,6 +283,13 @@ def test_contiguous_causal_ring_scaled(dev):
 def test_ring_prefetch_depth(dev, depth):
     wl = workloads.workload("wan22_cp8_online")
     _ring_case(dev, wl, 8 * 64, ranks=(2,), variant="online", depth=depth, H=2)
+
+
+@pytest.mark.parametrize("variant,layout,causal", [("online", "contiguous", False), ("constmax", "contiguous", False),
+                                                   ("online", "striped", True)])
+def test_ring_with_split_steps(dev, variant, layout, causal):
+    wl = workloads.workload("wan22_cp8_online")
+    _ring_case(dev, wl, 8 * 300, ranks=(0, 5), variant=variant, layout=layout, causal=causal, H=3, split=True)
 
 
 def test_ring_pass_is_repeatable(dev):
