@@ -8,32 +8,37 @@
 // Design "A static bound makes the ring reduction pure addition", Implementation
 // "Accumulate, then normalize once").
 //
-// Work layout (gfx950, wave64, two workgroups of four waves per CU):
-//  * a workgroup is 4 waves and 128 query rows of one (batch, head); each wave owns
-//    32 rows and keeps Q, the output accumulator and the scores in VGPRs;
-//  * keys stream through LDS in tiles of 32, triple-buffered: tile t+2 is copied from
+// Work layout (gfx950, wave64, one workgroup of eight waves per CU, two waves per SIMD):
+//  * a workgroup owns 256 query rows of one (batch, head); each wave owns 32 rows and
+//    keeps Q, the output accumulator and the scores in VGPRs;
+//  * keys stream through LDS in tiles of 32 held in a ring of NBUF buffers, copied from
 //    HBM straight into LDS (global_load_lds_dwordx4: no staging registers, one scalar
-//    base per tile plus a fixed per-lane offset) while tile t computes; one barrier per
-//    tile; the tile loop is unrolled by three so every LDS buffer offset is an
-//    instruction immediate;
+//    base per tile plus a fixed per-lane offset), NBUF - 1 tiles ahead of use;
+//  * ping-pong: on a SIMD, one wave's matrix phase (the scores of tile j+1, K Q^T, and
+//    the output update of tile j, V^T P^T: 16 MFMAs) runs while the other wave does the
+//    softmax of tile j on the VALU and reads the next fragments from LDS. A single wave
+//    cannot overlap its own MFMAs with its VALU work, two waves on one SIMD can; the
+//    phases are held in step by one workgroup barrier per phase, waves 4..7 starting
+//    one phase behind waves 0..3;
 //  * LDS rows are dense (256 B) with XOR-swizzled 16-byte chunks so that both read
-//    patterns are bank-conflict free whether the hardware serves 8 or 16 lanes of a
-//    16-byte read (32 or 64 banks) per cycle: K chunk c of row r sits at c ^ (r & 15),
-//    V chunk c at c ^ (4(r & 3) + 2((r >> 1) & 1));
+//    patterns are bank-conflict free: K chunk c of row r sits at c ^ (r & 15), V chunk
+//    c at c ^ (4(r & 3) + 2((r >> 1) & 1));
 //  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each
 //    lane holds 16 scores of one query row: the row max needs one exchange between
-//    lanes l and l^32 per tile and nothing else;
+//    lanes l and l^32 per tile (v_permlane32_swap) and nothing else;
 //  * O^T = V^T P^T takes P straight from the score registers (B operand); V stays in
 //    natural [key][d] order in LDS and ds_read_b64_tr_b16 transposes it on the read
 //    (within 16 lanes, lane i element t <- lane i/4 + 4t's element i%4), fetching the
 //    keys in exactly the order the score registers hold them;
 //  * softmax uses exp2 with scale*log2(e) folded into one FMA per score; the running max
 //    moves only when a tile's max exceeds it by more than 8 (log2 units), so the
-//    accumulator rescale is rare and probabilities stay <= 256.
+//    accumulator rescale is rare and probabilities stay <= 256;
+//  * causal masks: a workgroup visits key tiles up to its last row's diagonal; tiles
+//    past a wave's own diagonal are masked in full (every probability is 0).
 //
 // Key-split schedule (when the caller passes a workspace and one workgroup per query tile
-// would leave over a tenth of the device's workgroup slots idle, e.g. 320 tiles on 512
-// slots): the (query tile, key tile) iterations of the whole call are laid end to end and
+// would leave over a tenth of the device's workgroup slots idle, e.g. 160 tiles on 256
+// CUs): the (query tile, key tile) iterations of the whole call are laid end to end and
 // cut into G equal ranges, G = the number of workgroups the device holds at once (or fewer
 // for small calls), so every workgroup does the same work and the grid fills the machine.
 // A query tile whose keys fall into several ranges is computed in segments; each segment
@@ -50,18 +55,18 @@ namespace ctxattn {
 namespace {
 
 constexpr int D = 128;         // head dim of the bf16 path
-constexpr int NW = 4;          // waves per workgroup
+constexpr int NW = 8;          // waves per workgroup: two per SIMD
 constexpr int NT = 64 * NW;    // threads per workgroup
 constexpr int BQ = 32 * NW;    // query rows per workgroup (32 per wave)
 constexpr int BK = 32;         // keys per LDS tile
-constexpr int NBUF = 3;        // LDS tile buffers
+constexpr int NBUF = 6;        // LDS tile buffers (copies run NBUF - 1 tiles ahead)
 constexpr int ROW = D;                    // bf16 per LDS row (dense, swizzled)
 constexpr int TILE = BK * ROW;            // bf16 per tile and tensor (8 KB)
 constexpr int TILE_BYTES = TILE * 2;
 constexpr int V_OFF = NBUF * TILE_BYTES;  // byte offset of the V buffers
 constexpr size_t LDS_BYTES = size_t(NBUF) * 2 * TILE_BYTES;
-constexpr int COPIES = BK * D / 8 / NT;   // 16-byte copies per lane per tile and tensor (2)
 constexpr float kRescaleSlack = 8.0f;
+static_assert(BK * D / 8 == NT, "one 16-byte copy per lane per tile and tensor");
 
 enum { MODE_ONLINE = 0, MODE_CONSTMAX = 1 };
 
@@ -87,12 +92,45 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, ui
                :: "s"(lds_byte), "v"(off), "s"(base) : "memory", "m0");
 }
 
-// Barrier after this wave's copies of the current tile have landed: with another tile's
-// batch (2*COPIES copies) issued later, vmcnt(2*COPIES) leaves exactly that batch in flight.
-__device__ __forceinline__ void wait_tile_and_barrier(bool newer_batch_in_flight) {
-  static_assert(2 * COPIES == 4, "vmcnt immediate below assumes 4 copies per batch");
-  if (newer_batch_in_flight) asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+// End of a phase: this wave's LDS reads have returned, at most 2*PENDING of its tile copies
+// are still in flight (two per tile: K and V), then the workgroup barrier. The scheduling
+// barriers keep the compiler from moving any instruction across the phase boundary.
+template <int PENDING>
+__device__ __forceinline__ void phase_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(2 * PENDING) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+#ifndef VECTOR_PRIO_ON
+#define VECTOR_PRIO_ON
+#define VECTOR_PRIO_OFF
+#define MATRIX_PRIO_ON
+#define MATRIX_PRIO_OFF
+#endif
+
+// Plain workgroup barrier between phases (no wait for copies).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16-byte store at device (agent) scope: written through to the coherence point that every
+// XCD's agent-scope loads read (the form the compiler gives a relaxed agent-scope atomic
+// store, as inline asm so that it does not pin the surrounding schedule).
+__device__ __forceinline__ void store_agent4(float* p, floatx4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(p), "v"(v) : "memory");
+}
+
+// Exchange with lane l ^ 32 (v_permlane32_swap): returns max / sum of the pair.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int IMM>
@@ -137,7 +175,7 @@ __device__ __forceinline__ float online_update(const floatx16& s, float sl2e, fl
   float tmax = fmaxf(s[0], s[1]);
 #pragma unroll
   for (int r = 2; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[r], s[r + 1]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = xor32_max(tmax);
   const float t2 = tmax * sl2e;
   const bool move = t2 > m_ref + kRescaleSlack;
   if (__any(move)) {
@@ -255,8 +293,8 @@ __host__ __device__ inline int64_t tiles_prefix(int mask, int qb, int nkt) {
 // Key-split schedule and its workspace (see the file comment).
 struct Split {
   int* cnt;        // [B*H*nqb][NW] arrivals per (query tile, wave); zero between calls
-  float* po;       // [2G][NW][64 values][64 lanes] unnormalised partial outputs, one record per
-                   // segment and wave, lane-interleaved so every access is one contiguous 256 B
+  float* po;       // [2G][NW][16 quads][64 lanes][4] unnormalised partial outputs, one record per
+                   // segment and wave, lane-interleaved so every 16-byte store is one contiguous 1 KB
   float* pml;      // [2G][NW][2][64 lanes] partial running max (log2 units) and full row sum
   int G;           // logical workgroups
   int64_t T;       // iterations (query tile x key tile) of the whole call
@@ -275,7 +313,7 @@ __device__ __forceinline__ int64_t segment_slot(const Split& sp, int w, int64_t 
 }
 
 template <int MODE, int MASK, bool SPLIT>
-__global__ __launch_bounds__(NT, 2)
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
@@ -285,26 +323,21 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const bool lagging = w >= NW / 2;   // waves 4..7 run one phase behind waves 0..3
   const int li = lane & 31;
   const int hl = lane >> 5;
   const int Sq = a.Sq, Sk = a.Sk;
   const int64_t kss_bytes = a.kss * 2;
   const float sl2e = a.sl2e;
 
-  // Per-lane copy offsets (bytes from the tile's first key): copy u of this wave fills LDS
-  // rows (COPIES*w+u)*4 + lane/16 at physical chunk lane%16, i.e. reads that row's logical
-  // chunk (lane%16) ^ swizzle(row).
-  uint32_t koff[COPIES], voff[COPIES];
-  int crow[COPIES];
-#pragma unroll
-  for (int u = 0; u < COPIES; ++u) {
-    const int r = (w * COPIES + u) * 4 + (lane >> 4);
-    const int p = lane & 15;
-    crow[u] = r;
-    koff[u] = uint32_t(r * kss_bytes) + uint32_t((p ^ k_swz(r)) << 4);
-    voff[u] = uint32_t(r * kss_bytes) + uint32_t((p ^ v_swz(r)) << 4);
-  }
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  // Per-lane copy offset (bytes from the tile's first key): wave w fills LDS rows
+  // 4w + lane/16 at physical chunk lane%16, i.e. reads that row's logical chunk
+  // (lane%16) ^ swizzle(row).
+  const int crow = 4 * w + (lane >> 4);
+  const int cchunk = lane & 15;
+  const uint32_t koff = uint32_t(crow * kss_bytes) + uint32_t((cchunk ^ k_swz(crow)) << 4);
+  const uint32_t voff = uint32_t(crow * kss_bytes) + uint32_t((cchunk ^ v_swz(crow)) << 4);
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(lds_addr(lds) + w * 1024);
 
   // Per-lane LDS read offsets (elements; buffer offsets are added as immediates).
   // K: row li, logical chunk 2c+hl.
@@ -330,7 +363,11 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     it = range_begin(sp, logical);
     it_end = range_begin(sp, logical + 1);
   }
-  bool first_segment = true;
+  // Tiles this wave combines once its own range is done (at most its first and last
+  // segment's tiles): tile index bh * nqb + qb and the tile's first iteration.
+  int ncomb = 0;
+  int comb_tile[2] = {0, 0};
+  int64_t comb_start[2] = {0, 0};
   while (it < it_end) {
     // ---- which query tile, and which of its key tiles, this segment covers
     int bh, qb, k0, k1;
@@ -361,8 +398,6 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       k1 = tile_iters(MASK, qb, nkt);
       it = it_end;
     }
-    if (!first_segment) __syncthreads();   // every wave is done with the LDS buffers and stores
-    first_segment = false;
 
     const int b = bh / a.H;
     const int h = bh - b * a.H;
@@ -399,64 +434,65 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       settle(c2);
     }
 
-    // A tile is skipped by a wave when causality hides all of its keys from all 32 rows.
-    auto skip_tile = [&](int t) -> bool {
-      if (MASK == CA_MASK_CAUSAL_INCL) return t * BK > row_w0 + 31;
-      if (MASK == CA_MASK_CAUSAL_STRICT) return t * BK >= row_w0 + 31;
-      return false;
-    };
-
-    // Issues the copies of key tile t into LDS buffer BUF. The last tile of a chunk clamps its
-    // rows to the last key (their scores are masked, their values meet p = 0).
-    auto issue = [&](auto bufc, int t) {
+    // Issues the copies of the segment's key tile j into LDS buffer BUF. The last tile of a
+    // chunk clamps its rows to the last key (their scores are masked, their values meet p = 0).
+    auto issue = [&](auto bufc, int j) {
       constexpr int BUF = decltype(bufc)::value;
-      const int key0 = t * BK;
+      const int key0 = (k0 + j) * BK;
       const char* kt = kbase + key0 * kss_bytes;
       const char* vt = vbase + key0 * kss_bytes;
-      const bool full = key0 + BK <= Sk;
-#pragma unroll
-      for (int u = 0; u < COPIES; ++u) {
-        uint32_t ko = koff[u], vo = voff[u];
-        if (!full) {
-          const int rr = min(crow[u], Sk - 1 - key0);
-          const int p = lane & 15;
-          ko = uint32_t(rr * kss_bytes) + uint32_t((p ^ k_swz(crow[u])) << 4);
-          vo = uint32_t(rr * kss_bytes) + uint32_t((p ^ v_swz(crow[u])) << 4);
-        }
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + BUF * TILE_BYTES + (w * COPIES + u) * 1024);
-        copy16_to_lds(kt, ko, dst);
-        copy16_to_lds(vt, vo, dst + V_OFF);
+      uint32_t ko = koff, vo = voff;
+      if (key0 + BK > Sk) {
+        const int rr = min(crow, Sk - 1 - key0);
+        ko = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ k_swz(crow)) << 4);
+        vo = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ v_swz(crow)) << 4);
       }
+      copy16_to_lds(kt, ko, lds_w + BUF * TILE_BYTES);
+      copy16_to_lds(vt, vo, lds_w + BUF * TILE_BYTES + V_OFF);
     };
 
-    // The segment's i-th key tile (key tile k0 + i): wait for its copies, launch the copies
-    // of tile i+2, compute.
-    auto step = [&](auto bufc, int i) {
+    bf16x8 ka[8];    // K fragments of the tile whose scores the next matrix phase forms
+    bf16x8 va[8];    // V fragments of the tile whose output update the next matrix phase does
+    floatx16 s;      // scores of the tile in flight
+    bf16x8 p[2];     // probabilities of the tile whose output update is next
+    auto read_k = [&](auto bufc) {
       constexpr int BUF = decltype(bufc)::value;
-      constexpr int BUF2 = (BUF + 2) % NBUF;
-      wait_tile_and_barrier(i + 1 < nk);
-      if (i + 2 < nk) issue(std::integral_constant<int, BUF2>{}, k0 + i + 2);
-      const int t = k0 + i;
-      if (skip_tile(t)) return;
-      const int key0 = t * BK;
-      // All fragment reads up front: K first (QK^T waits for those only), then V, whose
-      // latency hides behind QK^T and the softmax.
-      bf16x8 ka[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) ka[c] = lds_read16<BUF * TILE_BYTES>(lds, kr[c]);
-      bf16x8 va[8];
+    };
+    auto read_v = [&](auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         va[db * 2] = lds_read_tr<V_OFF + BUF * TILE_BYTES>(lds, vr[db]);
         va[db * 2 + 1] = lds_read_tr<V_OFF + BUF * TILE_BYTES + 16 * ROW * 2>(lds, vr[db]);
       }
-      __builtin_amdgcn_sched_barrier(0);   // every fragment read is issued before the first MFMA
-      floatx16 s;
+    };
+    // Matrix phase: the output update with the V fragments and probabilities of the last
+    // vector phase (PV), then the scores of the next tile (QK). Its K fragments are read at
+    // the start of the phase; the eight PV MFMAs cover the read latency. The group barriers
+    // pin that order: K reads, PV MFMAs, QK MFMAs.
+    auto matrix_phase = [&](auto bufc, bool do_qk, bool do_pv) {
+      constexpr int BUF = decltype(bufc)::value;
+      if (do_qk) read_k(bufc);
+      if (do_pv) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+        for (int c = 0; c < 8; ++c)
+          o[c & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(c & 3) * 2 + (c >> 2)], p[c >> 2], o[c & 3], 0, 0, 0);
+      }
+      if (do_qk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], q[0], floatx16{}, 0, 0, 0);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
-      // s[r] is the raw score q_row . k_j for key j = key0 + 8*(r/4) + 4*hl + r%4
+        for (int c = 1; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
+      }
+      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 K fragment reads
+      if (do_pv) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // PV
+      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // QK
+      (void)BUF;
+    };
+    // Softmax of the segment's tile j (scores in s): probabilities into p, row sum into l_part.
+    auto softmax = [&](int j) {
+      const int key0 = (k0 + j) * BK;
       bool need_mask = key0 + BK > Sk;
       if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
       if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
@@ -464,28 +500,73 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       float mu;
       if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
       else mu = c2;
-      bf16x8 p[2];
-      // The softmax runs at raised wave priority: the two waves sharing a SIMD then tend to
-      // alternate, one on the VALU while the other keeps the matrix core busy.
-      __builtin_amdgcn_s_setprio(2);
       exp_pack(s, sl2e, mu, p, l_part);
-      __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)   // kc outer: consecutive MFMAs hit different accumulators
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db * 2 + kc], p[kc], o[db], 0, 0, 0);
     };
+    // One tile j of the segment (buffer BUF = j % NBUF), in two phases.
+    //  vector phase: read V of tile j, start the copies of tile j + NBUF - 1 into the buffer
+    //    tile j - 1 used, softmax of tile j; ends once this wave's copies of tile j + 2 have
+    //    landed, then the workgroup barrier;
+    //  matrix phase: read K of tile j + 1, output update of tile j, scores of tile j + 1;
+    //    then the barrier.
+    // The body is the same for every tile: past the segment's last tile the copies repeat
+    // that tile into free buffers and the scores of the nonexistent tile are never used,
+    // so the copy count in flight, the waits and the MFMA sequence never change.
+    auto tile = [&](auto bufc, int j) {
+      constexpr int BUF = decltype(bufc)::value;
+      constexpr int NEXT = (BUF + 1) % NBUF;
+      constexpr int FREE = (BUF + NBUF - 1) % NBUF;
+      VECTOR_PRIO_ON;
+      read_v(bufc);
+      issue(std::integral_constant<int, FREE>{}, min(j + NBUF - 1, nk - 1));
+      softmax(j);
+      VECTOR_PRIO_OFF;
+      phase_end<NBUF - 3>();
+      MATRIX_PRIO_ON;
+      matrix_phase(std::integral_constant<int, NEXT>{}, true, true);
+      MATRIX_PRIO_OFF;
+      phase_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    static_assert(NBUF == 6, "the tile loop is unrolled for six buffers");
 
-    if (nk > 0) issue(std::integral_constant<int, 0>{}, k0);
-    if (nk > 1) issue(std::integral_constant<int, 1>{}, k0 + 1);
-    for (int i = 0; i < nk; i += NBUF) {
-      step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < nk) step(std::integral_constant<int, 1>{}, i + 1);
-      if (i + 2 < nk) step(std::integral_constant<int, 2>{}, i + 2);
+    if (nk > 0) {
+      // prologue: tiles 0 .. NBUF-2 in flight, wait for tiles 0 and 1, scores of tile 0
+      issue(I0{}, 0);
+      issue(I1{}, min(1, nk - 1));
+      issue(I2{}, min(2, nk - 1));
+      issue(I3{}, min(3, nk - 1));
+      issue(I4{}, min(4, nk - 1));
+      phase_end<NBUF - 3>();
+      if (lagging) phase_barrier();
+      matrix_phase(I0{}, true, false);   // scores of tile 0
+      phase_barrier();
+      for (int j = 0;; j += NBUF) {
+        tile(I0{}, j);
+        if (j + 1 >= nk) break;
+        tile(I1{}, j + 1);
+        if (j + 2 >= nk) break;
+        tile(I2{}, j + 2);
+        if (j + 3 >= nk) break;
+        tile(I3{}, j + 3);
+        if (j + 4 >= nk) break;
+        tile(I4{}, j + 4);
+        if (j + 5 >= nk) break;
+        tile(I5{}, j + 5);
+        if (j + 6 >= nk) break;
+      }
+      // every copy has landed and every wave is past its last LDS read before the buffers
+      // are reused (next segment) or released
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (!lagging) phase_barrier();
+      phase_barrier();
     }
 
-    const float lrow = l_part + __shfl_xor(l_part, 32);
+    const float lrow = xor32_sum(l_part);
     if (!SPLIT) {
       store_rows<MODE>(a, bh, Sq, row, hl, o, lrow, m_ref, c2);
       continue;
@@ -505,12 +586,13 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     // final count.
     {
       const int64_t rec = segment_slot(sp, logical, tile_start) * NW + w;
-      float* po = sp.po + rec * (64 * 64) + lane;
+      float* po = sp.po + rec * (64 * 64) + lane * 4;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __hip_atomic_store(po + (db * 16 + r) * 64, o[db][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < 4; ++g)
+          store_agent4(po + (db * 4 + g) * 256,
+                       floatx4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]});
       __hip_atomic_store(sp.pml + rec * 128 + lane, m_ref, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(sp.pml + rec * 128 + 64 + lane, lrow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -520,19 +602,37 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     if (lane == 0) seen = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     seen = __shfl(seen, 0);
     if (seen != w_last - w_first) continue;   // another segment is still running
-
     if (lane == 0) __hip_atomic_exchange(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+    comb_tile[ncomb] = bh * nqb + qb;
+    comb_start[ncomb] = tile_start;
+    ++ncomb;
+  }
+  if (!SPLIT) return;
+
+  // ---- combine the segments of the tiles this wave arrived at last, in key order
+  // (deterministic sums). Done after the tile loop, so none of the loop's state is live here.
+  for (int ci = 0; ci < ncomb; ++ci) {
+    const int tix = ci == 0 ? comb_tile[0] : comb_tile[1];
+    const int64_t tile_start = ci == 0 ? comb_start[0] : comb_start[1];
+    const int bh = tix / nqb;
+    const int qb = tix - bh * nqb;
+    const int row = qb * BQ + w * 32 + li;
+    const int w_first = range_owner(sp, tile_start);
+    const int w_last = range_owner(sp, tile_start + tile_iters(MASK, qb, nkt) - 1);
+    float c2 = 0.0f;
+    if (MODE == MODE_CONSTMAX) c2 = a.c[int64_t(bh) * Sq + min(row, Sq - 1)] * kLog2e;
     float M = -INFINITY;
     if (MODE == MODE_ONLINE)
       for (int wq = w_first; wq <= w_last; ++wq)
         M = fmaxf(M, __hip_atomic_load(sp.pml + (segment_slot(sp, wq, tile_start) * NW + w) * 128 + lane,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     float L = 0.0f;
+    floatx16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    for (int wq = w_first; wq <= w_last; ++wq) {   // key order: deterministic sums
+    for (int wq = w_first; wq <= w_last; ++wq) {
       const int64_t rec = segment_slot(sp, wq, tile_start) * NW + w;
       float wt = 1.0f;
       if (MODE == MODE_ONLINE) {
@@ -540,18 +640,23 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
         wt = mq == -INFINITY ? 0.0f : exp2f(mq - M);
       }
       L += wt * __hip_atomic_load(sp.pml + rec * 128 + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float* po = sp.po + rec * (64 * 64) + lane;
+      // 8-byte agent-scope loads: 32 per record and lane, all in flight at once
+      const uint64_t* po = reinterpret_cast<const uint64_t*>(sp.po + rec * (64 * 64) + lane * 4);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          o[db][r] += wt * __hip_atomic_load(po + (db * 16 + r) * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int r = 0; r < 16; r += 2) {
+          const uint64_t bits = __hip_atomic_load(po + (db * 4 + r / 4) * 128 + (r % 4) / 2, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+          o[db][r] += wt * __uint_as_float(uint32_t(bits));
+          o[db][r + 1] += wt * __uint_as_float(uint32_t(bits >> 32));
+        }
     }
     store_rows<MODE>(a, bh, Sq, row, hl, o, L, M, c2);
   }
 }
 
-// Workgroups resident at once on the current device (two per CU).
+// Workgroups resident at once on the current device (one per CU).
 int resident_workgroups() {
   static int cache[64] = {0};
   int dev = 0;
@@ -559,7 +664,7 @@ int resident_workgroups() {
   if (cache[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cache[dev] = 2 * cus;
+    cache[dev] = cus;
   }
   return cache[dev];
 }
