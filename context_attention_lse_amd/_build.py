@@ -42,6 +42,12 @@ def _run(cmd):
     return out
 
 
+# Per-source extra flags. The bf16 step kernel builds without NaN semantics: its inputs are
+# finite or -inf (masked scores), and the row maxima then compile to v_max3_f32 with no
+# canonicalising moves in front of them.
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans"]}
+
+
 def build(verbose: bool = False, jobs: int = 6) -> str:
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
@@ -49,7 +55,7 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out, file=sys.stderr)
         return obj

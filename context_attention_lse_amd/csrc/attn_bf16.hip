@@ -172,9 +172,12 @@ __device__ __forceinline__ void exp_pack(const floatx16& s, float sl2e, float mu
 // Online-max bookkeeping for one tile; returns the exp2 offset mu.
 __device__ __forceinline__ float online_update(const floatx16& s, float sl2e, float& m_ref, float& l_part,
                                                floatx16 (&o)[4]) {
-  float tmax = fmaxf(s[0], s[1]);
-#pragma unroll
-  for (int r = 2; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[r], s[r + 1]));
+  // a three-level tree of 3-input maxima (v_max3_f32; this file builds without NaN
+  // semantics, so no canonicalising moves precede them)
+  const float a0 = fmaxf(fmaxf(s[0], s[1]), s[2]), a1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float a2 = fmaxf(fmaxf(s[6], s[7]), s[8]), a3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  float tmax = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15]));
   tmax = xor32_max(tmax);
   const float t2 = tmax * sl2e;
   const bool move = t2 > m_ref + kRescaleSlack;
