@@ -4,7 +4,8 @@
 //
 // Work decomposition (bandwidth-bound: every resident K/V byte is read once):
 //  * grid (split, kv head, sequence); a split is 1024 shard-local tokens (64 blocks);
-//  * a workgroup is 4 waves; wave w streams 16 blocks of the split, two blocks per step;
+//  * a workgroup is 4 waves; wave w streams 16 blocks of the split, two blocks per step,
+//    with the loads of the next two steps in flight (a ring of three register sets);
 //  * the GQA group's query heads (<= 16) share each K/V block: scores are
 //    S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows = 16 tokens, cols = heads), so
 //    a block is read once for all heads of its group;
@@ -30,25 +31,20 @@ struct PairRegs {
   uint2 v[2][8];   // [block][d block of 16]: 4 bf16 (tokens 4g..4g+3) at d = 16*db + c16
 };
 
+// Loads one block pair; blk0 and blk1 are wave-uniform physical block ids, always inside
+// the pool (the caller substitutes a resident block for missing ones), so the loads carry
+// no branches and the compiler's wait counts stay exact.
 __device__ __forceinline__ void load_pair(PairRegs& r, const uint16_t* kp, const uint16_t* vp, int hkv, int Hkv,
-                                          const int32_t* btab, int jb0, int nblk, int num_blocks, int g, int c16) {
+                                          int blk0, int blk1, int g, int c16) {
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
-    const int j = jb0 + bi;
-    const int64_t blk = j < nblk ? btab[j] : -1;
-    if (blk >= 0 && blk < num_blocks) {
-      const uint16_t* kb = kp + ((blk * Hkv + hkv) * BS + c16) * D + 8 * g;
+    const int64_t blk = bi == 0 ? blk0 : blk1;
+    const uint16_t* kb = kp + ((blk * Hkv + hkv) * BS + c16) * D + 8 * g;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = *reinterpret_cast<const uint4*>(kb + 32 * cc);
-      const uint16_t* vb = vp + ((blk * Hkv + hkv) * D + c16) * BS + 4 * g;
+    for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = *reinterpret_cast<const uint4*>(kb + 32 * cc);
+    const uint16_t* vb = vp + ((blk * Hkv + hkv) * D + c16) * BS + 4 * g;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) r.v[bi][db] = *reinterpret_cast<const uint2*>(vb + 16 * BS * db);
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) r.v[bi][db] = make_uint2(0, 0);
-    }
+    for (int db = 0; db < 8; ++db) r.v[bi][db] = *reinterpret_cast<const uint2*>(vb + 16 * BS * db);
   }
 }
 
@@ -68,7 +64,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so block ids load as scalars
   const int g = lane >> 4;
   const int c16 = lane & 15;
 
@@ -93,22 +89,19 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   float l_part = 0.0f;
   const float sl2e = a.sl2e;
 
-  PairRegs cur, nxt;
-  load_pair(cur, kp, vp, hkv, a.Hkv, btab, wave_blk0, nblk, a.num_blocks, g, c16);
-  for (int it = 0; it < WAVE_BLOCKS / 2; ++it) {
-    const int jb0 = wave_blk0 + 2 * it;
-    if (jb0 >= nblk) break;   // wave-uniform
-    if (it + 1 < WAVE_BLOCKS / 2) load_pair(nxt, kp, vp, hkv, a.Hkv, btab, jb0 + 2, nblk, a.num_blocks, g, c16);
-
+  // Block pairs stream through a ring of three register sets: the loads of pair it + 2 are
+  // issued before pair it is computed, so two pairs (32 KB per wave) stay in flight.
+  auto compute = [&](const PairRegs& cur, int jb0, uint32_t zero2) {
     floatx4 s[2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       s[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        bf16x8 kf = *reinterpret_cast<bf16x8*>(&cur.k[bi][cc]);
+        bf16x8 kf = *reinterpret_cast<const bf16x8*>(&cur.k[bi][cc]);
         s[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], s[bi], 0, 0, 0);
       }
+      if ((zero2 >> bi) & 1) s[bi] = floatx4{0.f, 0.f, 0.f, 0.f};   // all-zero block: q.0
     }
     // s[bi][r]: score of head c16 against token (jb0 + bi)*16 + 4g + r
     float tmax = -INFINITY;
@@ -144,13 +137,42 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
     uint4 pk = make_uint4(pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                           pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3]));
     const bf16x8 pb = *reinterpret_cast<bf16x8*>(&pk);
+    const bool z0 = zero2 & 1, z1 = (zero2 >> 1) & 1;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      uint4 vv = make_uint4(cur.v[0][db].x, cur.v[0][db].y, cur.v[1][db].x, cur.v[1][db].y);
+      uint4 vv = make_uint4(z0 ? 0u : cur.v[0][db].x, z0 ? 0u : cur.v[0][db].y, z1 ? 0u : cur.v[1][db].x,
+                            z1 ? 0u : cur.v[1][db].y);
       const bf16x8 vf = *reinterpret_cast<bf16x8*>(&vv);
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc[db], 0, 0, 0);
     }
-    cur = nxt;
+  };
+
+  // This wave's physical block ids (scalar loads). Past the sequence a resident block of
+  // the split stands in (its scores are masked, so it adds nothing). An id outside the pool
+  // reads as an all-zero block: its scores become 0 and its values 0 (bit i of zero_blk).
+  const int first = btab[split * SPLIT_BLOCKS];
+  const int fallback = (first >= 0 && first < a.num_blocks) ? first : 0;
+  int bid[WAVE_BLOCKS];
+  uint32_t zero_blk = 0;
+#pragma unroll
+  for (int i = 0; i < WAVE_BLOCKS; ++i) {
+    const int j = wave_blk0 + i;
+    const int blk = j < nblk ? btab[j] : fallback;
+    const bool ok = blk >= 0 && blk < a.num_blocks;
+    bid[i] = ok ? blk : fallback;
+    zero_blk |= (ok ? 0u : 1u) << i;
+  }
+
+  constexpr int PAIRS = WAVE_BLOCKS / 2;
+  PairRegs ring[3];
+  load_pair(ring[0], kp, vp, hkv, a.Hkv, bid[0], bid[1], g, c16);
+  load_pair(ring[1], kp, vp, hkv, a.Hkv, bid[2], bid[3], g, c16);
+#pragma unroll
+  for (int it = 0; it < PAIRS; ++it) {
+    const int jb0 = wave_blk0 + 2 * it;
+    if (jb0 >= nblk) break;   // wave-uniform
+    if (it + 2 < PAIRS) load_pair(ring[(it + 2) % 3], kp, vp, hkv, a.Hkv, bid[2 * it + 4], bid[2 * it + 5], g, c16);
+    compute(ring[it % 3], jb0, (zero_blk >> (2 * it)) & 3u);
   }
 
   // Row sums per head: fold the 4 token groups (lanes c16, c16+16, c16+32, c16+48).
@@ -194,35 +216,60 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   }
 }
 
-// One row (sequence, query head) per D/4 lanes: fold that sequence's splits.
+// One wave per row (sequence, query head) folds that sequence's splits: lane i holds split
+// i's LSE (64 at a time) for the weights; for the outputs, the two half-waves take
+// alternate splits, each lane four consecutive d, eight splits' loads in flight per round.
+constexpr int COMBINE_WAVES = NT / 64;
+
 __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs a) {
-  constexpr int LPR = D / 4;
-  constexpr int RPB = NT / LPR;
-  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / LPR;
-  const int col = (threadIdx.x % LPR) * 4;
-  if (row >= int64_t(a.B) * a.Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * COMBINE_WAVES + (threadIdx.x >> 6);
+  if (row >= int64_t(a.B) * a.Hq) return;   // wave-uniform
   const int b = int(row / a.Hq);
   const int len = min(max(a.local_lens[b], 0), a.max_blocks * BS);
   const int n = (len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
   const float* lp = a.ws_lse + row * a.max_splits;
+  const int half = lane >> 5;
+  const int col = (lane & 31) * 4;
   const float* op = a.ws_o + row * a.max_splits * D + col;
+
   float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, lp[s]);
-  float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
-  float gl = -INFINITY;
+  for (int s0 = 0; s0 < n; s0 += 64) M = fmaxf(M, s0 + lane < n ? lp[s0 + lane] : -INFINITY);
+  M = wave_max(M);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float total = 0.0f;
   if (M != -INFINITY) {
-    float total = 0.0f;
-    for (int s = 0; s < n; ++s) total += __expf(lp[s] - M);
-    gl = M + __logf(total);
-    for (int s = 0; s < n; ++s) {
-      const float wt = __expf(lp[s] - gl);
-      const float4 v = *reinterpret_cast<const float4*>(op + int64_t(s) * D);
-      out.x = fmaf(wt, v.x, out.x); out.y = fmaf(wt, v.y, out.y);
-      out.z = fmaf(wt, v.z, out.z); out.w = fmaf(wt, v.w, out.w);
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const float wl = s0 + lane < n ? __expf(lp[s0 + lane] - M) : 0.0f;
+      total += wl;
+      const int cnt = min(64, n - s0);
+      for (int s = 0; s < cnt; s += 8) {
+        float4 v[4];
+        float wt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = s + 2 * u + half;   // split s0 + j of this half-wave
+          wt[u] = __shfl(wl, j & 63);
+          v[u] = j < cnt ? *reinterpret_cast<const float4*>(op + int64_t(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = s + 2 * u + half < cnt ? wt[u] : 0.0f;
+          acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
+          acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
+        }
+      }
     }
+    total = wave_sum(total);
   }
-  *reinterpret_cast<float4*>(a.o + row * D + col) = out;
-  if (col == 0) a.lse[row] = gl;
+  // the two halves hold disjoint splits of the same four d: add them
+  acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);
+  acc.z += __shfl_xor(acc.z, 32); acc.w += __shfl_xor(acc.w, 32);
+  if (half == 0) {
+    const float inv = total > 0.0f ? 1.0f / total : 0.0f;
+    *reinterpret_cast<float4*>(a.o + row * D + col) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (col == 0) a.lse[row] = total > 0.0f ? M + __logf(total) : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -241,9 +288,9 @@ hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int RPB = NT / (D / 4);
   const int64_t rows = int64_t(a.B) * a.Hq;
-  hipLaunchKernelGGL(dcp_decode_combine_kernel, dim3(unsigned((rows + RPB - 1) / RPB)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(dcp_decode_combine_kernel, dim3(unsigned((rows + COMBINE_WAVES - 1) / COMBINE_WAVES)), dim3(NT), 0,
+                     s, a);
   return hipGetLastError();
 }
 
