@@ -149,6 +149,7 @@ ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq
   CA_TRY(check_bshd("q", q, qs, dtype, B, Sq, H, D));
   if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
   if (!kmax_sq || !c) return fail(CA_ERR_NULL, "kmax_sq and c are required");
+  if (H > 256) return fail(CA_ERR_UNSUPPORTED, "at most 256 heads");
   hipError_t e = ctxattn::launch_const_max_bound(q, qs.b, qs.s, qs.h, dtype == CA_BF16, B, Sq, H, D,
                                                  resolve_scale(softmax_scale, D), kmax_sq, c,
                                                  static_cast<hipStream_t>(stream));

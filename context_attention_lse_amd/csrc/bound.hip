@@ -111,34 +111,48 @@ __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64
     if (smax[h] > 0) atomicMax(reinterpret_cast<int*>(kmax_sq) + b * H + h, smax[h]);
 }
 
-// grid: (ceil(Sq*H / ROWS_PER_BLOCK), B): c_i = sqrt(scale^2 * kmax_sq[b,h] * |q_i|^2).
+// grid: (ceil(Sq / TOK), B): c_i = sqrt(scale^2 * kmax_sq[b,h] * |q_i|^2). A workgroup
+// takes TOK consecutive tokens of every head: it reads their rows in memory order (token
+// major), keeps |q|^2 in LDS as [head][token], and writes c one head at a time, so the
+// [B, H, Sq] output goes out in runs of TOK consecutive floats.
+constexpr int TOK = 64;
+
 template <bool BF16>
 __global__ __launch_bounds__(NT) void const_max_bound_kernel(const void* q, int64_t sb, int64_t ss, int64_t sh,
                                                              int Sq, int H, int D, float scale,
                                                              const float* kmax_sq, float* c) {
+  extern __shared__ float qn[];   // [H][TOK]
   const int b = blockIdx.y;
+  const int t0 = blockIdx.x * TOK;
+  const int ntok = min(TOK, Sq - t0);
   const int grp = threadIdx.x >> 4;
   const int lane16 = threadIdx.x & 15;
-  const int64_t pairs = int64_t(Sq) * H;
-  const int64_t p0 = int64_t(blockIdx.x) * ROWS_PER_BLOCK;
-  for (int it = 0; it < ITERS; ++it) {
+  const int rows = ntok * H;
+  for (int r0 = 0; r0 < rows; r0 += GROUPS * RIF) {
     RowPiece<BF16> r[RIF];
 #pragma unroll
     for (int u = 0; u < RIF; ++u) {
-      const int64_t p = p0 + (int64_t(it) * RIF + u) * GROUPS + grp;
-      const int64_t pc = p < pairs ? p : 0;
-      const int i = int(pc / H), h = int(pc % H);
-      r[u] = load_piece<BF16>(q, b * sb + int64_t(i) * ss + int64_t(h) * sh, lane16, D);
+      const int p = r0 + u * GROUPS + grp;
+      const int pc = p < rows ? p : 0;
+      const int i = pc / H, h = pc - (pc / H) * H;
+      r[u] = load_piece<BF16>(q, b * sb + int64_t(t0 + i) * ss + int64_t(h) * sh, lane16, D);
     }
 #pragma unroll
     for (int u = 0; u < RIF; ++u) {
-      const int64_t p = p0 + (int64_t(it) * RIF + u) * GROUPS + grp;
-      const float qn2 = group16_sum(piece_sqnorm<BF16>(r[u]));
-      if (p < pairs && lane16 == 0) {
-        const int i = int(p / H), h = int(p % H);
-        c[(int64_t(b) * H + h) * Sq + i] = sqrtf(scale * scale * kmax_sq[b * H + h] * qn2);
+      const int p = r0 + u * GROUPS + grp;
+      // p is uniform over the 16 lanes of a group, so the reduction runs with all 16 active
+      const float v = group16_sum(piece_sqnorm<BF16>(r[u]));
+      if (p < rows && lane16 == 0) {
+        const int i = p / H, h = p - (p / H) * H;
+        qn[h * TOK + i] = v;
       }
     }
+  }
+  __syncthreads();
+  const float s2 = scale * scale;
+  for (int e = threadIdx.x; e < H * TOK; e += NT) {
+    const int h = e / TOK, i = e - (e / TOK) * TOK;
+    if (i < ntok) c[(int64_t(b) * H + h) * Sq + t0 + i] = sqrtf(s2 * kmax_sq[b * H + h] * qn[e]);
   }
 }
 
@@ -166,12 +180,12 @@ hipError_t launch_key_sqnorm_max(const void* k, int64_t sb, int64_t ss, int64_t 
 hipError_t launch_const_max_bound(const void* q, int64_t sb, int64_t ss, int64_t sh, bool bf16, int B, int Sq,
                                   int H, int D, float scale, const float* kmax_sq, float* c, hipStream_t s) {
   if (Sq == 0 || B == 0) return hipSuccess;
-  const int64_t pairs = int64_t(Sq) * H;
-  dim3 grid(unsigned((pairs + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), B);
+  dim3 grid(unsigned((Sq + TOK - 1) / TOK), B);
+  const size_t lds = size_t(H) * TOK * sizeof(float);
   if (bf16)
-    hipLaunchKernelGGL((const_max_bound_kernel<true>), grid, dim3(NT), 0, s, q, sb, ss, sh, Sq, H, D, scale, kmax_sq, c);
+    hipLaunchKernelGGL((const_max_bound_kernel<true>), grid, dim3(NT), lds, s, q, sb, ss, sh, Sq, H, D, scale, kmax_sq, c);
   else
-    hipLaunchKernelGGL((const_max_bound_kernel<false>), grid, dim3(NT), 0, s, q, sb, ss, sh, Sq, H, D, scale, kmax_sq, c);
+    hipLaunchKernelGGL((const_max_bound_kernel<false>), grid, dim3(NT), lds, s, q, sb, ss, sh, Sq, H, D, scale, kmax_sq, c);
   return hipGetLastError();
 }
 

@@ -155,9 +155,16 @@ class RingPass:
             self.copied[step].record(self.copy_stream)
 
     def prologue(self):
-        """const-max bound: per-head max key norm over the whole ring, then c per row."""
-        for r in range(self.cp):
-            api.key_sqnorm_max(self.k_pool[r], self.kmax, accumulate=r > 0)
+        """const-max bound: per-head max key norm over the whole ring, then c per row.
+        With one sequence and a contiguous pool, the chunks are one [1, cp*S, H, D] run of
+        keys and the max-fold over the ring is a single call."""
+        kp = self.k_pool
+        if kp.shape[1] == 1 and kp.is_contiguous():
+            cp, _, S, H, D = kp.shape
+            api.key_sqnorm_max(kp.view(1, cp * S, H, D), self.kmax)
+        else:
+            for r in range(self.cp):
+                api.key_sqnorm_max(kp[r], self.kmax, accumulate=r > 0)
         api.const_max_bound(self.q, self.kmax, scale=self.scale, out=self.c)
 
     def run(self, timing_events=None):

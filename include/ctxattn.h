@@ -115,7 +115,7 @@ ca_status ring_attn_step(const void* q, ca_strides q_strides,
  * ring_attn_const_max_step (mask CA_MASK_NONE) need for these sizes on the CURRENT
  * device (the split depends on its compute-unit count). 0: the call does not split
  * (fp32, no key tiles, or enough query tiles to fill the device). The bytes are per-call
- * scratch: split partials (2 * workgroups * 128 rows * (D + 2) fp32) and one counter per
+ * scratch: split partials (2 * workgroups * 256 rows * (D + 2) fp32) and one counter per
  * (query tile, wave).
  */
 ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask,
@@ -128,8 +128,9 @@ ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int 
  * "Global key max" (all_reduce(max) across the ring). On one device the
  * all-reduce is the max-fold over chunks: accumulate = 0 overwrites kmax_sq with
  * this chunk's maxima, accumulate = 1 folds them into kmax_sq by max.
- *   k        [B, S, H, D], strides ks; D a multiple of 8 in [8, 128]
+ *   k        [B, S, H, D], strides ks; D a multiple of 8 in [8, 128]; H <= 4096
  *   kmax_sq  IN/OUT [B, H] fp32
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED (D, H), CA_ERR_HIP.
  */
 ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, int H, int D,
                          float* kmax_sq, int accumulate, void* stream);
@@ -139,9 +140,10 @@ ca_status key_sqnorm_max(const void* k, ca_strides ks, int dtype, int B, int S, 
  * Source: kernel reference page, Design "Picking a max that is safe without
  * measuring it" (Cauchy-Schwarz: c_i >= every score of row i) and Implementation
  * "Assembling the bound" (one square root of scale^2 * kmax_sq * |q_i|^2).
- *   q        [B, Sq, H, D], strides qs; D a multiple of 8 in [8, 128]
+ *   q        [B, Sq, H, D], strides qs; D a multiple of 8 in [8, 128]; H <= 256
  *   kmax_sq  [B, H] fp32 (from key_sqnorm_max over every chunk of the ring)
  *   c        OUT [B, H, Sq] fp32
+ * Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED (D, H), CA_ERR_HIP.
  */
 ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq, int H, int D,
                           float softmax_scale, const float* kmax_sq, float* c, void* stream);

@@ -112,7 +112,7 @@ def test_step_rejects_bad_arguments(dev):
 
 
 @pytest.mark.parametrize("dtype,D,S,H", [("bf16", 128, 150, 3), ("fp32", 64, 150, 3), ("bf16", 128, 2001, 5),
-                                         ("fp32", 128, 1203, 3)])
+                                         ("fp32", 128, 1203, 3), ("bf16", 128, 333, 40)])
 def test_const_max_bound_matches_oracle(dev, dtype, D, S, H):
     ca = _ca()
     say(f"bound dtype={dtype} D={D} S={S} H={H}")
