@@ -17,8 +17,6 @@ constexpr int NT = 256;
 // Each group keeps RIF rows' loads in flight before reducing any of them.
 constexpr int RIF = 8;                  // rows in flight per 16-lane group
 constexpr int GROUPS = NT / 16;         // 16-lane groups per block
-constexpr int ITERS = 4;                // row batches per group
-constexpr int ROWS_PER_BLOCK = GROUPS * RIF * ITERS;
 
 template <bool BF16>
 struct RowPiece {
@@ -75,9 +73,12 @@ __global__ void fill_kernel(float* p, int n, float v) {
   if (i < n) p[i] = v;
 }
 
-// grid: (ceil(S*H / ROWS_PER_BLOCK), B). Per-head maxima gather in LDS, then one global
-// atomicMax per head per block. Squared norms are non-negative floats, whose bit patterns
-// order like ints, so the max is exact and independent of arrival order.
+// grid: (ceil(S / KTOK), B); a workgroup takes KTOK tokens of every head. Per-head maxima
+// gather in LDS, then one global atomicMax per head per block. Squared norms are
+// non-negative floats, whose bit patterns order like ints, so the max is exact and
+// independent of arrival order.
+constexpr int KTOK = 32;   // tokens (of every head) per key-norm workgroup
+
 template <bool BF16>
 __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64_t sb, int64_t ss, int64_t sh,
                                                             int S, int H, int D, float* kmax_sq) {
@@ -87,23 +88,23 @@ __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64
   __syncthreads();
   const int grp = threadIdx.x >> 4;
   const int lane16 = threadIdx.x & 15;
-  const int64_t pairs = int64_t(S) * H;
-  const int64_t p0 = int64_t(blockIdx.x) * ROWS_PER_BLOCK;
-  for (int it = 0; it < ITERS; ++it) {
+  const int t0 = blockIdx.x * KTOK;
+  const int rows = min(KTOK, S - t0) * H;   // this workgroup's (token, head) rows, token major
+  for (int r0 = 0; r0 < rows; r0 += GROUPS * RIF) {
     RowPiece<BF16> r[RIF];
 #pragma unroll
     for (int u = 0; u < RIF; ++u) {
-      const int64_t p = p0 + (int64_t(it) * RIF + u) * GROUPS + grp;
-      const int64_t pc = p < pairs ? p : 0;
-      const int t = int(pc / H), h = int(pc % H);
-      r[u] = load_piece<BF16>(k, b * sb + int64_t(t) * ss + int64_t(h) * sh, lane16, D);
+      const int p = r0 + u * GROUPS + grp;
+      const int pc = p < rows ? p : 0;
+      const int i = pc / H, h = pc - i * H;
+      r[u] = load_piece<BF16>(k, b * sb + int64_t(t0 + i) * ss + int64_t(h) * sh, lane16, D);
     }
 #pragma unroll
     for (int u = 0; u < RIF; ++u) {
-      const int64_t p = p0 + (int64_t(it) * RIF + u) * GROUPS + grp;
+      const int p = r0 + u * GROUPS + grp;
       // p is uniform over the 16 lanes of a group, so the reduction runs with all 16 active
       const float v = group16_sum(piece_sqnorm<BF16>(r[u]));
-      if (p < pairs && lane16 == 0) atomicMax(&smax[int(p % H)], __float_as_int(v));
+      if (p < rows && lane16 == 0) atomicMax(&smax[p - (p / H) * H], __float_as_int(v));
     }
   }
   __syncthreads();
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64
 // takes TOK consecutive tokens of every head: it reads their rows in memory order (token
 // major), keeps |q|^2 in LDS as [head][token], and writes c one head at a time, so the
 // [B, H, Sq] output goes out in runs of TOK consecutive floats.
-constexpr int TOK = 64;
+constexpr int TOK = 16;
 
 template <bool BF16>
 __global__ __launch_bounds__(NT) void const_max_bound_kernel(const void* q, int64_t sb, int64_t ss, int64_t sh,
@@ -167,8 +168,7 @@ hipError_t launch_key_sqnorm_max(const void* k, int64_t sb, int64_t ss, int64_t 
     if (e != hipSuccess) return e;
   }
   if (S == 0 || B == 0) return hipSuccess;
-  const int64_t pairs = int64_t(S) * H;
-  dim3 grid(unsigned((pairs + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK), B);
+  dim3 grid(unsigned((S + KTOK - 1) / KTOK), B);
   const size_t lds = size_t(H) * sizeof(int);
   if (bf16)
     hipLaunchKernelGGL((key_sqnorm_max_kernel<true>), grid, dim3(NT), lds, s, k, sb, ss, sh, S, H, D, kmax_sq);
