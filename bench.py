@@ -9,11 +9,14 @@ Also reported (``workloads``): the const-max ring on the 720p share (40 heads,
 local 9450), the striped causal ring at S = 128k (all 8 ranks' passes), DCP decode
 over two interleaved paged shards (KV GB/s), and the tiny fp32 ring.
 
-``roofline`` is measured live for the dominant kernel with HIP events on the stream it
-is launched on; ``cpu_baseline`` times the fp64 oracle on a bounded row sample.
+``roofline`` is measured live for the dominant kernel, the step kernel: 30 back-to-back
+launches with the pass's inputs and workspace on one stream, bracketed by HIP events on that
+stream (inside the pass the steps overlap on two streams, so their own durations include the
+sharing). ``--roofline-only`` runs just that loop, for a profiler run of the kernel alone.
+``cpu_baseline`` times the fp64 oracle on a bounded row sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
-                       [--only constmax,striped,decode,tiny,copy]
+                       [--only constmax,striped,decode,tiny,copy] [--roofline-only]
 
 ``--only`` runs the headline plus the named extra workloads; ``copy`` times a plain device
 copy of 1 GiB through the library (kv_chunk_copy), the reference used to scale the
@@ -42,10 +45,10 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "7ca660989a7f787f",
-                                        "fetch_kib": 21570.0, "write_kib": 20640.1},
-    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "a4babf5203842dce",
-                                  "fetch_kib": 2773545.7 + 22174.5, "write_kib": 46925.6 + 1032.0},
+    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "43b69744e748b3ec",
+                                        "fetch_kib": 76744.6, "write_kib": 73000.4},
+    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "febecae0207bf690",
+                                  "fetch_kib": 2774639.8 + 22131.5, "write_kib": 47158.8 + 1040.0},
 }
 
 
@@ -68,28 +71,50 @@ def ring_flops(H, Sq, Sk, D):
 
 
 def time_ring(rp, steps, warmup, torch, union=None):
-    """Runs warmup + timed ring passes; returns (ms per pass, per-step mean kernel ms). If ``union``
-    is a list, the mean time from the first step's start to the last step's end is appended."""
+    """Runs warmup + timed ring passes; returns (ms per pass, per-step mean kernel ms). The
+    pass time comes from one event pair around ``steps`` passes with nothing else recorded;
+    per-step durations (and, if ``union`` is a list, the mean span from the first step's
+    start to the last step's end) come from a second, separately timed set of passes."""
     cp = rp.cp
     for _ in range(warmup):
         rp.run()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cp)]
-          for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for k in range(steps):
-        rp.run(timing_events=ev[k])
+        rp.run()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    per_step = [sum(ev[k][s][0].elapsed_time(ev[k][s][1]) for k in range(steps)) / steps for s in range(cp)]
+    n = max(2, min(steps, 5))
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cp)]
+          for _ in range(n)]
+    for k in range(n):
+        rp.run(timing_events=ev[k])
+    torch.cuda.synchronize()
+    per_step = [sum(ev[k][s][0].elapsed_time(ev[k][s][1]) for k in range(n)) / n for s in range(cp)]
     if union is not None:
-        union.append(sum(max(ev[k][s][0].elapsed_time(ev[k][j][1]) for j in range(cp)) for k in range(steps)
-                         for s in [0]) / steps)
+        union.append(sum(max(ev[k][0][0].elapsed_time(ev[k][j][1]) for j in range(cp)) for k in range(n)) / n)
     return ms, per_step
+
+
+def step_roofline(q, k, v, ws, torch, ca, reps=30):
+    """Mean duration of the step kernel alone: ``reps`` back-to-back launches of
+    ring_attn_step on the current stream with the headline's inputs and launch
+    configuration (key-split workspace), bracketed by one HIP event pair."""
+    B, Sq, H, D = q.shape
+    o = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    ca.ring_attn_step(q, k, v, out=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ca.ring_attn_step(q, k, v, out=o, lse=lse, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def headline(args, torch, ca, workloads, gen, dev):
@@ -100,32 +125,33 @@ def headline(args, torch, ca, workloads, gen, dev):
     kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
     del t
-    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online")
-    log("[bench] timing ring pass")
-    union = []
-    ms, per_step = time_ring(rp, args.steps, args.warmup, torch, union)
-    union_ms = union[0]
+    # key-split steps (each fills the device) on two compute streams, so one step's drain
+    # overlaps the next step's start
+    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=True, compute_streams=2)
     Sq = wl.local_S
     flops_pass = ring_flops(wl.H, Sq, wl.S, wl.D)
     flops_step = ring_flops(wl.H, Sq, wl.local_S, wl.D)
-    step_ms = sum(per_step) / len(per_step)
-    achieved = flops_step / (step_ms * 1e-3) / 1e12
-    return {
-        "wl": wl, "ms": ms, "tflops": flops_pass / (ms * 1e-3) / 1e12, "step_ms": step_ms,
-        "per_step_ms": per_step,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic("attn_step_bf16/wan22_cp8_online"),
-                     "kernel": "attn_step_bf16 (ring_attn_step)",
-                     "per_launch": f"{flops_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
-                     "note": ("steps run one after another on one compute stream, each on a key-split "
-                              "grid that fills the device" if rp.aux_stream is None else
-                              "consecutive ring steps run on two compute streams and overlap, so each "
-                              "launch's duration includes sharing the GPU with its neighbour step; "
-                              "steps_union_tflops is the step kernels' throughput over their union")},
-        "steps_union_tflops": round(8 * flops_step / (union_ms * 1e-3) / 1e12, 2),
-        "inputs": (q, kp, vp),
-    }
+    out = {"wl": wl, "inputs": (q, kp, vp)}
+    if not args.roofline_only:
+        log("[bench] timing ring pass")
+        union = []
+        ms, per_step = time_ring(rp, args.steps, args.warmup, torch, union)
+        out.update({"ms": ms, "tflops": flops_pass / (ms * 1e-3) / 1e12,
+                    "per_step_ms": per_step, "step_ms": sum(per_step) / len(per_step),
+                    "steps_union_tflops": round(8 * flops_step / (union[0] * 1e-3) / 1e12, 2)})
+    log("[bench] timing the step kernel alone (roofline)")
+    kernel_ms = step_roofline(q, kp[0], vp[0], rp.ws[0], torch, ca)
+    achieved = flops_step / (kernel_ms * 1e-3) / 1e12
+    out["kernel_ms"] = kernel_ms
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                       "traffic": traffic("attn_step_bf16/wan22_cp8_online"),
+                       "kernel": "attn_step_bf16 (ring_attn_step, key-split schedule)",
+                       "per_launch": f"{flops_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
+                       "kernel_ms": round(kernel_ms, 4),
+                       "note": ("mean of 30 back-to-back launches on one stream with the pass's inputs and "
+                                "workspace; inside the pass, steps alternate two streams and overlap")}
+    return out
 
 
 def cpu_baseline(q, kp, vp, D, budget_s=12.0):
@@ -325,6 +351,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="time only the step kernel's back-to-back launches (for profiling it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="constmax,striped,decode,tiny",
                     help="comma-separated extra workloads to run after the headline")
@@ -345,6 +373,9 @@ def main():
 
     h = headline(args, torch, ca, workloads, gen, dev)
     wl = h["wl"]
+    if args.roofline_only:
+        print(json.dumps({"workload": wl.name, "roofline": h["roofline"]}), flush=True)
+        return
     line = {
         "metric": "ring-step attention TFLOP/s (% bf16 MFMA peak); DCP decode KV GB/s (% HBM)",
         "value": round(h["tflops"], 2),
@@ -362,7 +393,7 @@ def main():
                    "cp": wl.cp, "local_seq": wl.local_S, "rank": 0, "steps_per_pass": wl.cp,
                    "flops_per_pass": ring_flops(wl.H, wl.local_S, wl.S, wl.D)},
         "roofline": h["roofline"],
-        "step_kernel_ms": round(h["step_ms"], 4),
+        "step_ms_in_pass": round(h["step_ms"], 4),
         "steps_union_tflops": h["steps_union_tflops"],
     }
     extra = {}
