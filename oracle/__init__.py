@@ -49,4 +49,9 @@ from .sharding import (  # noqa: F401
     dcp_active_owner,
     dcp_prefill_prior_global_position,
 )
-from .dcp import decode_shard_partial, decode_full  # noqa: F401
+from .dcp import (  # noqa: F401
+    decode_shard_partial,
+    decode_shard_partial_active,
+    decode_full,
+    segmented_attention_partial,
+)

@@ -237,3 +237,66 @@ def pins_const_max(attn, const_max, bound):
     if abs(float(o90[0, 0]) - 4.5) < 1.0:
         bad.append("collapse_at_90")
     return bad
+
+
+def pins_dcp_active(partial_active, world, interleave):
+    """DCP decode with the current token (DCP page, dcp_active_mask): the W partials merge
+    to full attention over the N prior tokens plus the current one, and each partial equals
+    brute force over the keys listed from the slot mapping (the owner taken from the
+    position, not from the vblock rule). Returns the failures."""
+    import oracle
+    bad = []
+    rng = np.random.default_rng(100 * world + interleave)
+    Hq, Hkv, D, bs = 4, 2, 3, 16
+    for N in (0, 1, 15, 16, 17, 40, 63, 64, 65, 100):
+        q = rng.normal(size=(Hq, D)) * 2
+        k = rng.normal(size=(N, Hkv, D)); v = rng.normal(size=(N, Hkv, 2))
+        ka = rng.normal(size=(Hkv, D)) * 2; va = rng.normal(size=(Hkv, 2))
+        parts = [partial_active(q, k, v, ka, va, r, interleave, world, bs, 0.5) for r in range(world)]
+        o, l = oracle.merge_lse([p[0] for p in parts], [p[1] for p in parts])
+        fo, fl = oracle.decode_full(q, np.concatenate([k, ka[None]]), np.concatenate([v, va[None]]), 0.5)
+        if not (np.allclose(o, fo, atol=TOL) and np.allclose(l, fl, atol=TOL)):
+            bad.append(f"merge != full at N={N}")
+        for r in range(world):
+            keys = [p for p in range(N) if (p // interleave) % world == r]
+            kk, vv = k[keys], v[keys]
+            if (N // interleave) % world == r:
+                kk = np.concatenate([kk, ka[None]]); vv = np.concatenate([vv, va[None]])
+            for h in range(Hq):
+                bo, bl = brute_attention(q[h:h + 1], kk[:, h // 2], vv[:, h // 2], 0.5)
+                if not (np.allclose(parts[r][0][h], bo[0], atol=TOL) and _close(parts[r][1][h], bl[0])):
+                    bad.append(f"partial of rank {r} at N={N}, head {h}")
+    return bad
+
+
+def pins_segmented(seg_partial, world, interleave, prior_rounds):
+    """DCP prefill (DCP page, segmented attention): every rank's partial over its prior
+    slots and its slice of the chunk, causal on global positions, merges to causal
+    attention of the chunk's queries over the whole context; one query of one rank by brute
+    force. Rank slices are enumerated from the slot mapping. Returns the failures."""
+    import oracle
+    bad = []
+    rng = np.random.default_rng(7 * world + interleave + 100 * prior_rounds)
+    Hq, Hkv, D = 4, 2, 3
+    rnd = world * interleave
+    P = prior_rounds * rnd            # prior tokens: whole interleave rounds, as earlier chunks leave
+    S = 2 * rnd                        # chunk length: a multiple of W * I
+    q = rng.normal(size=(S, Hq, D)) * 1.5
+    k = rng.normal(size=(P + S, Hkv, D)); v = rng.normal(size=(P + S, Hkv, 2))
+    parts = []
+    for r in range(world):
+        prior = [p for p in range(P) if (p // interleave) % world == r]
+        cur = [P + j for j in range(S) if (j // interleave) % world == r]
+        parts.append(seg_partial(q, k[cur], v[cur], k[prior], v[prior], P, r, interleave, world, 0.7))
+    o, l = oracle.merge_lse([p[0] for p in parts], [p[1] for p in parts])
+    allowed = oracle.causal_allowed(P + np.arange(S), np.arange(P + S))
+    for h in range(Hq):
+        fo, fl = brute_attention(q[:, h], k[:, h // 2], v[:, h // 2], 0.7, allowed)
+        if not (np.allclose(o[h], fo, atol=TOL) and np.allclose(l[h], fl, atol=TOL)):
+            bad.append(f"merge != causal attention, head {h}")
+    r = world - 1
+    keys = [p for p in range(P + S) if (p // interleave) % world == r and p <= P + S - 2]
+    bo, bl = brute_attention(q[S - 2:S - 1, 1], k[keys, 0], v[keys, 0], 0.7)
+    if not (np.allclose(parts[r][0][1, S - 2], bo[0], atol=TOL) and _close(parts[r][1][1, S - 2], bl[0])):
+        bad.append("one query of the last rank")
+    return bad

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from pins import pins_attention, pins_const_max, pins_merge
+from pins import pins_attention, pins_const_max, pins_dcp_active, pins_merge, pins_segmented
 
 
 def _attn_factory(scale_pow=1, use_max=True, lse_log=np.log, normalise=True, honour_mask=True,
@@ -136,3 +136,71 @@ def test_unmutated_factories_pass():
     assert pins_merge(oracle.attention, _merge_factory("ok")) == []
     b = _bound_factory("ok")
     assert pins_const_max(oracle.attention, _const_max_factory(b), b) == []
+
+
+# ---------------------------------------------------------------- DCP decode with the current token
+
+def _active_factory(gate):
+    """gate(N, rank, interleave, world) -> whether this rank adds the current token."""
+    def partial(q, k, v, ka, va, rank, interleave, world, block_size, scale):
+        N = k.shape[0]
+        mine = oracle.dcp_shard_of_position(np.arange(N), interleave, world) == rank
+        kk, vv = k[mine], v[mine]
+        if gate(N, rank, interleave, world):
+            kk = np.concatenate([kk, ka[None]]); vv = np.concatenate([vv, va[None]])
+        return oracle.decode_full(q, kk, vv, scale)
+    return partial
+
+
+ACTIVE_MUTANTS = {
+    "every_rank_adds_it": _active_factory(lambda N, r, I, W: True),
+    "no_rank_adds_it": _active_factory(lambda N, r, I, W: False),
+    "rank0_adds_it": _active_factory(lambda N, r, I, W: r == 0),
+    "owner_of_previous_position": _active_factory(lambda N, r, I, W: ((N - 1) // I) % W == r if N else r == 0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ACTIVE_MUTANTS))
+def test_dcp_active_mutant_caught(name):
+    assert any(pins_dcp_active(ACTIVE_MUTANTS[name], W, I) for W, I in ((2, 16), (4, 4), (3, 1))), name
+
+
+# ---------------------------------------------------------------- DCP prefill (segmented attention)
+
+def _segmented_factory(cur_offset=True, rank_term=True, causal=True, query_offset=True):
+    def pos(slots, rank, I, W):
+        s = np.asarray(slots)
+        return (s // I) * (W * I) + (rank * I if rank_term else 0) + (s % I)
+
+    def partial(q, k_cur, v_cur, k_prior, v_prior, prior_global, rank, I, W, scale):
+        k = np.concatenate([k_prior, k_cur]); v = np.concatenate([v_prior, v_cur])
+        kpos = np.concatenate([pos(np.arange(k_prior.shape[0]), rank, I, W),
+                               (prior_global if cur_offset else 0) + pos(np.arange(k_cur.shape[0]), rank, I, W)])
+        qpos = (prior_global if query_offset else 0) + np.arange(q.shape[0])
+        allowed = oracle.causal_allowed(qpos, kpos) if causal else None
+        Hq, Hkv = q.shape[1], k.shape[1]
+        o = np.zeros((Hq, q.shape[0], v.shape[2])); lse = np.zeros((Hq, q.shape[0]))
+        for h in range(Hq):
+            o[h], lse[h] = oracle.attention(q[:, h], k[:, h * Hkv // Hq], v[:, h * Hkv // Hq], scale, allowed)
+        return o, lse
+    return partial
+
+
+SEGMENTED_MUTANTS = {
+    "current_slice_without_prior_offset": _segmented_factory(cur_offset=False),
+    "positions_without_rank_term": _segmented_factory(rank_term=False),
+    "mask_ignored": _segmented_factory(causal=False),
+    "queries_without_prior_offset": _segmented_factory(query_offset=False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SEGMENTED_MUTANTS))
+def test_segmented_mutant_caught(name):
+    assert any(pins_segmented(SEGMENTED_MUTANTS[name], W, I, pr) for W, I, pr in ((2, 4, 1), (4, 4, 3), (2, 16, 0))), name
+
+
+def test_segmented_reference_copy_passes():
+    """The unmutated copy passes the same pins, so the catches above are the plants'."""
+    assert not any(pins_segmented(_segmented_factory(), W, I, pr) for W, I, pr in ((2, 4, 1), (4, 4, 3), (2, 16, 0)))
+    assert not any(pins_dcp_active(_active_factory(lambda N, r, I, W: (N // I) % W == r), W, I)
+                   for W, I in ((2, 16), (4, 4), (3, 1)))

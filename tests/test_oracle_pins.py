@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 
-from pins import brute_attention, pins_attention, pins_const_max, pins_merge
+from pins import brute_attention, pins_attention, pins_const_max, pins_dcp_active, pins_merge, pins_segmented
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -174,6 +174,32 @@ def test_dcp_decode_shards_merge_to_full(N):
             bo, bl = brute_attention(q[h:h + 1], k[mine, h // 2], v[mine, h // 2], 0.5)
             assert np.allclose(parts[r][0][h], bo[0], atol=1e-12)
             assert (parts[r][1][h] == bl[0]) or abs(parts[r][1][h] - bl[0]) < 1e-12
+
+
+@pytest.mark.parametrize("world", [1, 2, 3, 4])
+@pytest.mark.parametrize("interleave", [1, 4, 16])
+def test_dcp_decode_active_token_counts_once(world, interleave):
+    assert pins_dcp_active(oracle.decode_shard_partial_active, world, interleave) == []
+
+
+def test_dcp_decode_ungated_active_token_is_not_full_attention():
+    """Without the gate every rank adds the current token and the merge weighs it W times."""
+    Hq, Hkv, D = 2, 1, 3
+    q = np.ones((Hq, D)); k = np.zeros((5, Hkv, D)); v = np.zeros((5, Hkv, 2))
+    ka = np.ones((Hkv, D)); va = np.ones((Hkv, 2))
+    parts = []
+    for r in range(2):
+        mine = [p for p in range(5) if (p // 1) % 2 == r]
+        parts.append(oracle.decode_full(q, np.concatenate([k[mine], ka[None]]), np.concatenate([v[mine], va[None]]), 0.5))
+    o, _ = oracle.merge_lse([p[0] for p in parts], [p[1] for p in parts])
+    fo, _ = oracle.decode_full(q, np.concatenate([k, ka[None]]), np.concatenate([v, va[None]]), 0.5)
+    assert not np.allclose(o, fo, atol=1e-6)
+
+
+@pytest.mark.parametrize("world,interleave", [(1, 16), (2, 1), (2, 4), (2, 16), (4, 4), (3, 2)])
+@pytest.mark.parametrize("prior_rounds", [0, 1, 3])
+def test_dcp_prefill_segments_merge_to_causal_attention(world, interleave, prior_rounds):
+    assert pins_segmented(oracle.segmented_attention_partial, world, interleave, prior_rounds) == []
 
 
 def test_sum_clamp_value():
