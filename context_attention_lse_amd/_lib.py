@@ -23,7 +23,8 @@ STATUS_NAMES = {
 # Every symbol include/ctxattn.h declares.
 EXPORTS = (
     "ring_attn_step", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "lse_merge",
-    "dcp_decode_partial", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error", "ca_version",
+    "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error",
+    "ca_version",
 )
 
 
@@ -47,6 +48,8 @@ SIGNATURES = {
                                  _vp, _i, _vp, _vp, _sz, _vp],
     "lse_merge": [_i, _vp, _vp, _i64, _i, _vp, _i, _vp, _vp],
     "dcp_decode_partial": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp],
+    "dcp_decode_partial_active": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
+                                  _vp, _vp, _sz, _vp],
     "dcp_decode_workspace_size": [_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
     "kv_chunk_copy": [_vp, _vp, _vp, _vp, _sz, _vp],
     "ca_last_error": [],

@@ -219,6 +219,42 @@ def dcp_decode_partial(q, k_pool, v_pool, block_table, local_lens, scale=None, o
     return out, lse
 
 
+def dcp_decode_partial_active(q, k_pool, v_pool, block_table, prior_lens, k_cur, v_cur, rank, world,
+                              interleave=16, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """One DCP shard's decode step with the current token gated to its owner. q [B, Hq, D]
+    bf16; pools and block_table as dcp_decode_partial (this shard's prior tokens);
+    prior_lens [B] int32 (global prior count N); k_cur, v_cur [B, Hkv, D] bf16.
+    Returns (o [B, Hq, D] fp32, lse [B, Hq] fp32)."""
+    _check_cuda(q, k_pool, v_pool, block_table, prior_lens, k_cur, v_cur, out, lse, workspace)
+    B, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_pool.shape
+    if tuple(v_pool.shape) != (NB, Hkv, D, bs):
+        raise ValueError(f"v_pool must be [NB, Hkv, D, block_size], got {tuple(v_pool.shape)}")
+    if tuple(k_cur.shape) != (B, Hkv, D) or tuple(v_cur.shape) != (B, Hkv, D):
+        raise ValueError(f"k_cur and v_cur must be [B, Hkv, D] = {(B, Hkv, D)}")
+    for t in (q, k_pool, v_pool, block_table, prior_lens, k_cur, v_cur):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or prior_lens.dtype != torch.int32:
+        raise TypeError("block_table and prior_lens must be int32")
+    for t in (q, k_pool, v_pool, k_cur, v_cur):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("decode q, pools and current K/V must be bfloat16")
+    max_blocks = block_table.shape[1]
+    need = dcp_decode_workspace_size(B, Hq, D, bs, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _lib.call("dcp_decode_partial_active", _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(prior_lens),
+              _ptr(k_cur), _ptr(v_cur), int(rank), int(world), int(interleave), B, Hq, Hkv, D, bs, max_blocks, NB,
+              _scale(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream(stream))
+    return out, lse
+
+
 def kv_chunk_copy(dst_k, dst_v, src_k, src_v, stream=None):
     """Asynchronous device copy of one K and one V chunk (the ring hop on one GPU)."""
     _check_cuda(dst_k, dst_v, src_k, src_v)

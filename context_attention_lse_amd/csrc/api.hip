@@ -214,22 +214,40 @@ ca_status dcp_decode_workspace_size(int B, int Hq, int D, int block_size, int ma
   return CA_OK;
 }
 
-ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
-                             const int32_t* local_lens, int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
-                             int num_blocks, float softmax_scale, float* o, float* lse, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of both decode entry points. local_lens != NULL: resident
+// counts given; otherwise prior_lens, k_cur, v_cur, rank, world, interleave describe the
+// current-token form.
+ca_status decode_launch(const char* name, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* local_lens, const int32_t* prior_lens,
+                        const void* k_cur, const void* v_cur, int rank, int world, int interleave, int B, int Hq,
+                        int Hkv, int D, int block_size, int max_blocks, int num_blocks, float softmax_scale, float* o,
+                        float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_blocks < 0 || num_blocks < 0) return fail(CA_ERR_SHAPE, "bad sizes");
   if (D != 128) return fail(CA_ERR_UNSUPPORTED, "decode supports head_dim 128 only (got %d)", D);
   if (block_size != 16) return fail(CA_ERR_UNSUPPORTED, "decode supports block_size 16 only (got %d)", block_size);
   if (Hq % Hkv) return fail(CA_ERR_UNSUPPORTED, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (Hq / Hkv > 16) return fail(CA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
   if (B > 65535 || Hkv > 65535) return fail(CA_ERR_UNSUPPORTED, "at most 65535 sequences and KV heads");
+  if (!local_lens) {
+    if (world < 1 || rank < 0 || rank >= world)
+      return fail(CA_ERR_SHAPE, "rank %d outside a DCP group of %d", rank, world);
+    if (interleave < 1 || block_size % interleave)
+      return fail(CA_ERR_UNSUPPORTED, "interleave (%d) must divide block_size (%d)", interleave, block_size);
+    if (int64_t(block_size) * world > (int64_t(1) << 30)) return fail(CA_ERR_UNSUPPORTED, "DCP group too large");
+  }
   if (B == 0) return hip_status(hipSuccess, "");
-  if (!q || !o || !lse || !local_lens) return fail(CA_ERR_NULL, "q, o, lse and local_lens are required");
+  if (!q || !o || !lse || (!local_lens && !prior_lens))
+    return fail(CA_ERR_NULL, "q, o, lse and the sequence lengths are required");
+  if (!local_lens && (!k_cur || !v_cur)) return fail(CA_ERR_NULL, "k_cur and v_cur are required");
   if (max_blocks > 0 && num_blocks > 0 && (!k_pool || !v_pool || !block_table))
     return fail(CA_ERR_NULL, "k_pool, v_pool and block_table are required");
-  if (!aligned16(q) || !aligned16(o) || (k_pool && !aligned16(k_pool)) || (v_pool && !aligned16(v_pool)))
-    return fail(CA_ERR_SHAPE, "q, o, k_pool and v_pool must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(o) || (k_pool && !aligned16(k_pool)) || (v_pool && !aligned16(v_pool)) ||
+      (k_cur && !aligned16(k_cur)) || (v_cur && !aligned16(v_cur)))
+    return fail(CA_ERR_SHAPE, "q, o, the pools and the current K/V must be 16-byte aligned");
   const size_t need = ctxattn::decode_workspace_bytes(B, Hq, D, block_size, max_blocks);
   if (!workspace || workspace_bytes < need)
     return fail(CA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
@@ -241,13 +259,43 @@ ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_po
   a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.block_table = block_table; a.local_lens = local_lens;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
-  a.sl2e = resolve_scale(softmax_scale, D) * ctxattn::kLog2e;
+  a.scale = resolve_scale(softmax_scale, D);
+  a.sl2e = a.scale * ctxattn::kLog2e;
   a.o = o; a.lse = lse;
   a.max_splits = max_splits;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = a.ws_o + int64_t(B) * Hq * (max_splits > 0 ? max_splits : 1) * D;
+  if (!local_lens) {
+    a.prior_lens = prior_lens; a.k_cur = k_cur; a.v_cur = v_cur;
+    a.rank = rank; a.world = world; a.interleave = interleave;
+  }
   hipError_t e = ctxattn::launch_dcp_decode(a, static_cast<hipStream_t>(stream));
-  return hip_status(e, "dcp_decode_partial launch");
+  return hip_status(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                             const int32_t* local_lens, int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                             int num_blocks, float softmax_scale, float* o, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (B > 0 && !local_lens) return fail(CA_ERR_NULL, "local_lens is required");
+  return decode_launch("dcp_decode_partial launch", q, k_pool, v_pool, block_table, local_lens, nullptr, nullptr,
+                       nullptr, 0, 1, 1, B, Hq, Hkv, D, block_size, max_blocks, num_blocks, softmax_scale, o, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+ca_status dcp_decode_partial_active(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                                    const int32_t* prior_lens, const void* k_cur, const void* v_cur, int rank,
+                                    int world, int interleave, int B, int Hq, int Hkv, int D, int block_size,
+                                    int max_blocks, int num_blocks, float softmax_scale, float* o, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && !prior_lens) return fail(CA_ERR_NULL, "prior_lens is required");
+  return decode_launch("dcp_decode_partial_active launch", q, k_pool, v_pool, block_table, nullptr, prior_lens,
+                       k_cur, v_cur, rank, world, interleave, B, Hq, Hkv, D, block_size, max_blocks, num_blocks,
+                       softmax_scale, o, lse, workspace, workspace_bytes, stream);
 }
 
 ca_status kv_chunk_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v, size_t bytes, void* stream) {

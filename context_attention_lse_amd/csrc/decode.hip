@@ -48,6 +48,14 @@ __device__ __forceinline__ void load_pair(PairRegs& r, const uint16_t* kp, const
   }
 }
 
+// Tokens of sequence b resident in this shard: given (local_lens) or derived from the
+// sequence's prior length (current-token form); clamped to the block table.
+__device__ __forceinline__ int resident_len(const DecodeArgs& a, int b) {
+  const int n = a.prior_lens ? dcp_local_filled(max(a.prior_lens[b], 0), a.rank, BS, a.interleave, a.world)
+                             : a.local_lens[b];
+  return min(max(n, 0), a.max_blocks * BS);
+}
+
 __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[WAVES][16][D];
   __shared__ float s_m[WAVES][16];
@@ -56,7 +64,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   const int split = blockIdx.x;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
-  const int len = min(max(a.local_lens[b], 0), a.max_blocks * BS);
+  const int len = resident_len(a, b);
   const int split_tok0 = split * kDecodeSplitTokens;
   if (split_tok0 >= len) return;   // workgroup-uniform: nothing resident in this split
   const int nblk = (len + BS - 1) / BS;
@@ -226,14 +234,38 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
   const int64_t row = int64_t(blockIdx.x) * COMBINE_WAVES + (threadIdx.x >> 6);
   if (row >= int64_t(a.B) * a.Hq) return;   // wave-uniform
   const int b = int(row / a.Hq);
-  const int len = min(max(a.local_lens[b], 0), a.max_blocks * BS);
+  const int len = resident_len(a, b);
   const int n = (len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
   const float* lp = a.ws_lse + row * a.max_splits;
   const int half = lane >> 5;
   const int col = (lane & 31) * 4;
   const float* op = a.ws_o + row * a.max_splits * D + col;
 
-  float M = -INFINITY;
+  // Current-token form: on the owner of position N the current token is one more part,
+  // with lse = its score and output = its value row (dcp_active_mask).
+  bool cur = false;
+  float s_cur = -INFINITY;
+  float4 v_cur = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a.prior_lens) {
+    const int N = max(a.prior_lens[b], 0);
+    cur = dcp_active_owner(N, BS, a.interleave, a.world) == a.rank;
+    if (cur) {
+      const int hq = int(row - int64_t(b) * a.Hq);
+      const int64_t kv_row = int64_t(b) * a.Hkv + hq / (a.Hq / a.Hkv);
+      const uint2 qb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q) + row * D + col);
+      const uint2 kb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.k_cur) + kv_row * D + col);
+      const uint2 vb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v_cur) + kv_row * D + col);
+      float dot = bf16_bits_to_float(qb.x & 0xffffu) * bf16_bits_to_float(kb.x & 0xffffu);
+      dot = fmaf(bf16_bits_to_float(qb.x >> 16), bf16_bits_to_float(kb.x >> 16), dot);
+      dot = fmaf(bf16_bits_to_float(qb.y & 0xffffu), bf16_bits_to_float(kb.y & 0xffffu), dot);
+      dot = fmaf(bf16_bits_to_float(qb.y >> 16), bf16_bits_to_float(kb.y >> 16), dot);
+      s_cur = a.scale * wave_sum(half == 0 ? dot : 0.0f);
+      v_cur = make_float4(bf16_bits_to_float(vb.x & 0xffffu), bf16_bits_to_float(vb.x >> 16),
+                          bf16_bits_to_float(vb.y & 0xffffu), bf16_bits_to_float(vb.y >> 16));
+    }
+  }
+
+  float M = s_cur;
   for (int s0 = 0; s0 < n; s0 += 64) M = fmaxf(M, s0 + lane < n ? lp[s0 + lane] : -INFINITY);
   M = wave_max(M);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -261,6 +293,14 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
       }
     }
     total = wave_sum(total);
+    if (cur) {
+      const float wc = __expf(s_cur - M);
+      total += wc;
+      if (half == 0) {
+        acc.x = fmaf(wc, v_cur.x, acc.x); acc.y = fmaf(wc, v_cur.y, acc.y);
+        acc.z = fmaf(wc, v_cur.z, acc.z); acc.w = fmaf(wc, v_cur.w, acc.w);
+      }
+    }
   }
   // the two halves hold disjoint splits of the same four d: add them
   acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);

@@ -107,7 +107,34 @@ struct DecodeArgs {
   float* ws_o;      // [B, Hq, max_splits, D]
   float* ws_lse;    // [B, Hq, max_splits]
   int max_splits;
+  // current-token form (prior_lens != NULL): each sequence's resident count is local_filled
+  // of its prior length, and the current token's K/V joins on the rank that owns position N
+  const int32_t* prior_lens;   // [B] prior tokens N of each sequence (global count)
+  const void* k_cur;           // [B, Hkv, D] bf16
+  const void* v_cur;           // [B, Hkv, D] bf16
+  int rank, world, interleave;
+  float scale;
 };
+
+// Tokens among positions [0, N) that shard `rank` holds when blocks of `interleave`
+// positions are dealt round-robin over `world` shards and each shard fills blocks of
+// `block_size` (a multiple of interleave): DCP page, local_filled computation.
+__host__ __device__ inline int dcp_local_filled(int N, int rank, int block_size, int interleave, int world) {
+  const int vblock = block_size * world;
+  const int stride = interleave * world;
+  int filled = (N / vblock) * block_size;
+  const int remaining = N - (N / vblock) * vblock;
+  filled += (remaining / stride) * interleave;
+  const int leftover = remaining - (remaining / stride) * stride;
+  filled += min(max(leftover - rank * interleave, 0), interleave);
+  return filled;
+}
+
+// The shard whose slot mapping holds position N (DCP page, dcp_active_mask).
+__host__ __device__ inline int dcp_active_owner(int N, int block_size, int interleave, int world) {
+  const int vblock = block_size * world;
+  return ((N % vblock) / interleave) % world;
+}
 
 constexpr int kDecodeSplitTokens = 1024;   // tokens per decode split (64 blocks of 16)
 size_t decode_workspace_bytes(int B, int Hq, int D, int block_size, int max_blocks);

@@ -126,3 +126,15 @@ class DcpDecode:
                                    out=self.o_parts[r], lse=self.lse_parts[r], workspace=self.ws[r])
         api.lse_merge(self.o_parts, self.lse_parts, out=self.out, lse_out=self.lse)
         return self.out, self.lse
+
+    def run_active(self, prior_lens, k_cur, v_cur, interleave=16):
+        """A decode step with the current token: the shards hold the prior tokens
+        (positions [0, N) of each sequence, N = prior_lens), every shard gets the current
+        token's K/V, and only the owner of position N attends it (dcp_active_mask)."""
+        W = len(self.shards)
+        for r, sc in enumerate(self.shards):
+            api.dcp_decode_partial_active(self.q, sc.k_pool, sc.v_pool, sc.block_table, prior_lens, k_cur, v_cur,
+                                          r, W, interleave, scale=self.scale, out=self.o_parts[r],
+                                          lse=self.lse_parts[r], workspace=self.ws[r])
+        api.lse_merge(self.o_parts, self.lse_parts, out=self.out, lse_out=self.lse)
+        return self.out, self.lse

@@ -226,6 +226,35 @@ ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_po
                              int num_blocks, float softmax_scale, float* o, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dcp_decode_partial_active -- one DCP shard's decode step with the page's two-part
+ * mask: the prior tokens this shard holds plus the current decode token, which only
+ * the shard owning its position attends, so that the merged result counts it once.
+ * Source: DCP page, "Active Token Handling and dcp_active_mask" (prior_mask over slots
+ * [0, local_filled), the current token's slot gated by owner == dcp_rank, owner from
+ * pos_in_vblock) and "local_filled Computation" (the resident count, computed here on
+ * the device from each sequence's prior length N).
+ *
+ *   q, k_pool, v_pool, block_table, num_blocks, softmax_scale, o, lse, workspace:
+ *                as dcp_decode_partial (the cache holds this shard's prior tokens)
+ *   prior_lens   [B] int32: prior tokens N of each sequence, a global count; the
+ *                current token sits at position N
+ *   k_cur, v_cur [B, Hkv, D] bf16 contiguous: the current token's K and V (every shard
+ *                of the group holds the same values)
+ *   rank, world  this shard's DCP rank and the group size (0 <= rank < world)
+ *   interleave   positions per interleave block; must divide block_size
+ * The shard's resident count is local_filled(N, rank, block_size, interleave, world),
+ * clamped to max_blocks * block_size. A shard with no resident token that does not own
+ * position N yields o = 0, lse = -inf. Errors as dcp_decode_partial, and CA_ERR_SHAPE
+ * for a rank outside the group.
+ */
+ca_status dcp_decode_partial_active(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* prior_lens,
+                                    const void* k_cur, const void* v_cur, int rank, int world,
+                                    int interleave, int B, int Hq, int Hkv, int D, int block_size,
+                                    int max_blocks, int num_blocks, float softmax_scale, float* o,
+                                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace dcp_decode_partial needs for these sizes. */
 ca_status dcp_decode_workspace_size(int B, int Hq, int D, int block_size, int max_blocks,
                                     size_t* bytes);

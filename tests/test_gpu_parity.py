@@ -372,3 +372,60 @@ def test_decode_four_shards_and_empty_shard(dev):
     for r in (1, 2, 3):
         assert np.all(to_np(run.lse_parts[r, 0]) == -np.inf) and np.all(to_np(run.o_parts[r, 0]) == 0)
 
+
+
+# ---------------------------------------------------------------- DCP decode with the current token
+
+def _decode_active_case(dev, B, Hq, Hkv, prior, world, interleave, seed=5):
+    """Sequences of prior + 1 tokens: the shards hold the first N (positions [0, N)), the
+    last one is the current token, attended only by the shard that owns position N."""
+    ca = _ca()
+    ctx = tuple(n + 1 for n in prior)
+    wl = workloads.workload("dcp_decode_gqa").scaled(B=B, Hq=Hq, Hkv=Hkv, ctx_override=ctx, seed=seed,
+                                                     shards=world, interleave=interleave)
+    say(f"decode active B={B} Hq={Hq} Hkv={Hkv} prior={prior} world={world} interleave={interleave}")
+    d = gen.decode_inputs(wl, dev)
+    shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], np.asarray(prior), r, world, interleave,
+                                       16, d["block_rand"]) for r in range(world)]
+    last = torch.from_numpy(d["offsets"][:-1] + np.asarray(prior)).to(dev)
+    k_cur = d["k_seq"][last].contiguous()
+    v_cur = d["v_seq"][last].contiguous()
+    prior_lens = torch.tensor(prior, dtype=torch.int32, device=dev)
+    run = ca.dcp.DcpDecode(d["q"], shards)
+    o, l = run.run_active(prior_lens, k_cur, v_cur, interleave)
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(wl.D)
+    for b in range(B):
+        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
+        kb, vb = d["k_seq"][s0:s1], d["v_seq"][s0:s1]
+        N = prior[b]
+        for r in range(world):
+            po, pl = oracle.decode_shard_partial_active(d["q"][b], kb[:N], vb[:N], kb[N], vb[N], r, interleave, world,
+                                                        16, scale)
+            check(f"seq {b} (N={N}) shard {r} partial", run.o_parts[r, b], run.lse_parts[r, b], po, pl)
+        fo, fl = oracle.decode_full(d["q"][b], kb, vb, scale)
+        check(f"seq {b} (N={N}) merged", o[b], l[b], fo, fl)
+    return run
+
+
+@pytest.mark.parametrize("world,interleave", [(2, 16), (4, 16), (2, 4), (3, 8)])
+def test_decode_active_token_matches_oracle(dev, world, interleave):
+    _decode_active_case(dev, 8, 16, 2, (0, 15, 16, 17, 47, 48, 2000, 3071), world, interleave)
+
+
+def test_decode_active_token_gqa_full_group(dev):
+    _decode_active_case(dev, 3, 64, 8, (1023, 1024, 5000), 2, 16)
+
+
+def test_decode_active_rejects_bad_rank(dev):
+    ca = _ca()
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device=dev)
+    kp = torch.zeros((1, 8, 16, 128), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros((1, 8, 128, 16), dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    n = torch.zeros((1,), dtype=torch.int32, device=dev)
+    kc = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ca.CtxAttnError, match="rank"):
+        ca.dcp_decode_partial_active(q, kp, vp, bt, n, kc, kc, 2, 2)
+    with pytest.raises(ca.CtxAttnError, match="interleave"):
+        ca.dcp_decode_partial_active(q, kp, vp, bt, n, kc, kc, 0, 2, interleave=5)
