@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libctxattn.so")
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "bound.hip", "decode.hip", "copy.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "bound.hip", "decode.hip", "copy.hip",
+           "segmented.hip"]
 ARCH = os.environ.get("CTXATTN_ARCH", "gfx950")
 
 FLAGS = [

@@ -255,6 +255,45 @@ def dcp_decode_partial_active(q, k_pool, v_pool, block_table, prior_lens, k_cur,
     return out, lse
 
 
+def segmented_attention_workspace_size(Hq, Hkv, S, D, prior_tokens) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.call("segmented_attention_workspace_size", Hq, Hkv, S, D, int(prior_tokens), ctypes.byref(n))
+    return int(n.value)
+
+
+def segmented_attention_partial(q, k_cur, v_cur, k_cache, v_cache, block_table, prior_tokens, rank, world,
+                                interleave=16, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """One rank's DCP prefill partial. q [1, S, Hq, D] bf16 (the chunk's queries in global
+    order); k_cur, v_cur [1, S/world, Hkv, D] bf16 (the rank's slice); k_cache [NB, Hkv, 16, D]
+    and v_cache [NB, Hkv, D, 16] bf16 (the prior cache); block_table [max_blocks] int32;
+    prior_tokens: the rank's prior slots. Returns (o [Hq, S, D] fp32, lse [Hq, S] fp32)."""
+    _check_cuda(q, k_cur, v_cur, k_cache, v_cache, block_table, out, lse, workspace)
+    _, S, Hq, D = q.shape
+    _, S_local, Hkv, _ = k_cur.shape
+    if k_cur.shape != v_cur.shape or k_cur.stride() != v_cur.stride():
+        raise ValueError("k_cur and v_cur must share shape and strides")
+    NB = k_cache.shape[0]
+    if tuple(k_cache.shape) != (NB, Hkv, 16, D) or tuple(v_cache.shape) != (NB, Hkv, D, 16):
+        raise ValueError("caches must be [NB, Hkv, 16, D] (K) and [NB, Hkv, D, 16] (V)")
+    for t in (k_cache, v_cache, block_table):
+        if not t.is_contiguous():
+            raise ValueError("caches and block_table must be contiguous")
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    need = segmented_attention_workspace_size(Hq, Hkv, S, D, prior_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((Hq, S, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device)
+    _lib.call("segmented_attention_partial", _ptr(q), _strides(q), _ptr(k_cur), _ptr(v_cur), _strides(k_cur),
+              _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.numel(), NB, int(prior_tokens), int(rank),
+              int(world), int(interleave), Hq, Hkv, S, S_local, D, _scale(scale), _ptr(out), _ptr(lse),
+              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return out, lse
+
+
 def kv_chunk_copy(dst_k, dst_v, src_k, src_v, stream=None):
     """Asynchronous device copy of one K and one V chunk (the ring hop on one GPU)."""
     _check_cuda(dst_k, dst_v, src_k, src_v)

@@ -111,6 +111,7 @@ ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void
   a.scale = resolve_scale(softmax_scale, D);
   a.sl2e = a.scale * ctxattn::kLog2e;
   a.mask = mask;
+  a.G = 1;
   a.o = o; a.lse = lse;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -179,6 +180,7 @@ ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, 
   a.scale = resolve_scale(softmax_scale, D);
   a.sl2e = a.scale * ctxattn::kLog2e;
   a.mask = CA_MASK_NONE;
+  a.G = 1;
   a.c = c; a.acc = acc; a.phase = phase;
   a.o_cm = o; a.o_cm_bf16 = (o_dtype == CA_BF16); a.lse_cm = lse;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
@@ -296,6 +298,59 @@ ca_status dcp_decode_partial_active(const void* q, const void* k_pool, const voi
   return decode_launch("dcp_decode_partial_active launch", q, k_pool, v_pool, block_table, nullptr, prior_lens,
                        k_cur, v_cur, rank, world, interleave, B, Hq, Hkv, D, block_size, max_blocks, num_blocks,
                        softmax_scale, o, lse, workspace, workspace_bytes, stream);
+}
+
+ca_status segmented_attention_workspace_size(int Hq, int Hkv, int S, int D, int prior_tokens, size_t* bytes) {
+  if (!bytes) return fail(CA_ERR_NULL, "bytes is NULL");
+  if (Hq <= 0 || Hkv <= 0 || S < 0 || D <= 0 || prior_tokens < 0) return fail(CA_ERR_SHAPE, "bad sizes");
+  *bytes = ctxattn::segmented_workspace_bytes(Hq, Hkv, S, D, prior_tokens);
+  g_err[0] = 0;
+  return CA_OK;
+}
+
+ca_status segmented_attention_partial(const void* q, ca_strides qs, const void* k_cur, const void* v_cur,
+                                      ca_strides kvs, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, int max_blocks, int num_blocks, int prior_tokens,
+                                      int rank, int world, int interleave, int Hq, int Hkv, int S, int S_local, int D,
+                                      float softmax_scale, float* o, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (D != 128) return fail(CA_ERR_UNSUPPORTED, "segmented attention supports head_dim 128 only (got %d)", D);
+  if (Hq <= 0 || Hkv <= 0 || S < 0 || S_local < 0 || prior_tokens < 0 || max_blocks < 0 || num_blocks < 0)
+    return fail(CA_ERR_SHAPE, "bad sizes");
+  if (Hq % Hkv) return fail(CA_ERR_UNSUPPORTED, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Hkv > 16) return fail(CA_ERR_UNSUPPORTED, "at most 16 KV heads (got %d)", Hkv);
+  if (world < 1 || rank < 0 || rank >= world) return fail(CA_ERR_SHAPE, "rank %d outside a DCP group of %d", rank, world);
+  if (interleave < 1) return fail(CA_ERR_SHAPE, "interleave must be positive");
+  if (int64_t(world) * interleave > (int64_t(1) << 30)) return fail(CA_ERR_UNSUPPORTED, "DCP group too large");
+  if (S % (world * interleave))
+    return fail(CA_ERR_SHAPE, "chunk length %d is not a multiple of world * interleave = %d", S, world * interleave);
+  if (S_local != S / world) return fail(CA_ERR_SHAPE, "S_local (%d) must be S / world (%d)", S_local, S / world);
+  if (prior_tokens > int64_t(max_blocks) * 16)
+    return fail(CA_ERR_SHAPE, "prior_tokens %d exceeds the block table (%d blocks of 16)", prior_tokens, max_blocks);
+  CA_TRY(check_bshd("q", q, qs, CA_BF16, 1, S, Hq, D));
+  CA_TRY(check_bshd("k_cur", k_cur, kvs, CA_BF16, 1, S_local, Hkv, D));
+  CA_TRY(check_bshd("v_cur", v_cur, kvs, CA_BF16, 1, S_local, Hkv, D));
+  if (S == 0) return hip_status(hipSuccess, "");
+  if (!o || !lse) return fail(CA_ERR_NULL, "o and lse are required");
+  if (!aligned16(o)) return fail(CA_ERR_SHAPE, "o must be 16-byte aligned");
+  if (prior_tokens > 0) {
+    if (!k_cache || !v_cache || !block_table) return fail(CA_ERR_NULL, "k_cache, v_cache and block_table are required");
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return fail(CA_ERR_SHAPE, "the caches must be 16-byte aligned");
+  }
+  const size_t need = ctxattn::segmented_workspace_bytes(Hq, Hkv, S, D, prior_tokens);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(CA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if (need && !aligned16(workspace)) return fail(CA_ERR_SHAPE, "workspace must be 16-byte aligned");
+  ctxattn::SegmentedArgs g{};
+  g.q = q; g.qss = qs.s; g.qsh = qs.h;
+  g.k_cur = k_cur; g.v_cur = v_cur; g.kss = kvs.s; g.ksh = kvs.h;
+  g.k_cache = k_cache; g.v_cache = v_cache; g.block_table = block_table;
+  g.num_blocks = num_blocks; g.prior = prior_tokens;
+  g.rank = rank; g.world = world; g.interleave = interleave;
+  g.Hq = Hq; g.Hkv = Hkv; g.S = S; g.S_local = S_local;
+  g.scale = resolve_scale(softmax_scale, D);
+  g.o = o; g.lse = lse; g.ws = workspace;
+  return hip_status(ctxattn::launch_segmented(g, static_cast<hipStream_t>(stream)), "segmented_attention_partial launch");
 }
 
 ca_status kv_chunk_copy(void* dst_k, void* dst_v, const void* src_k, const void* src_v, size_t bytes, void* stream) {

@@ -194,15 +194,23 @@ __device__ __forceinline__ float online_update(const floatx16& s, float sl2e, fl
   return (m_ref == -INFINITY) ? 0.0f : m_ref;
 }
 
+// Keys a query row may see: every key j < row_key_limit(row) of the chunk (and j < Sk).
 template <int MASK>
-__device__ __forceinline__ void apply_mask(floatx16& s, int key0, int hl, int row, int Sk) {
+__host__ __device__ inline int row_key_limit(const AttnArgs& a, int row) {
+  if (MASK == CA_MASK_CAUSAL_INCL) return row + 1;
+  if (MASK == CA_MASK_CAUSAL_STRICT) return row;
+  if (MASK == kMaskDcp) {
+    const int n = row + 1, round = a.dcp_I * a.dcp_W;
+    return (n / round) * a.dcp_I + min(max(n - (n / round) * round - a.dcp_R * a.dcp_I, 0), a.dcp_I);
+  }
+  return a.Sk;
+}
+
+__device__ __forceinline__ void apply_mask(floatx16& s, int key0, int hl, int lim) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int j = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-    bool ok = j < Sk;
-    if (MASK == CA_MASK_CAUSAL_INCL) ok &= j <= row;
-    if (MASK == CA_MASK_CAUSAL_STRICT) ok &= j < row;
-    s[r] = ok ? s[r] : -INFINITY;
+    s[r] = j < lim ? s[r] : -INFINITY;
   }
 }
 
@@ -282,6 +290,14 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int64_t bh, int Sq
 __host__ __device__ inline int tile_iters(int mask, int qb, int nkt) {
   if (mask == CA_MASK_NONE) return nkt;
   return min(nkt, (BQ / BK) * (qb + 1));
+}
+
+// As tile_iters, for any mask: the tiles holding the keys the tile's last row may see.
+template <int MASK>
+__host__ __device__ inline int tile_iters_of(const AttnArgs& a, int qb, int nkt) {
+  if (MASK != kMaskDcp) return tile_iters(MASK, qb, nkt);
+  const int lim = row_key_limit<MASK>(a, min(qb * BQ + BQ, a.Sq) - 1);
+  return min(nkt, (lim + BK - 1) / BK);
 }
 
 // Iterations of query tiles [0, qb) of one (batch, head). Causal: the first nkt / (BQ/BK)
@@ -398,7 +414,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       qb = logical - bh * nqb;
       if (MASK != CA_MASK_NONE) qb = nqb - 1 - qb;   // heavy (late) query blocks first
       k0 = 0;
-      k1 = tile_iters(MASK, qb, nkt);
+      k1 = tile_iters_of<MASK>(a, qb, nkt);
       it = it_end;
     }
 
@@ -419,8 +435,12 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       for (int c = 0; c < 8; ++c) settle(q[c]);
     }
 
-    const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + h * a.ksh);
-    const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + h * a.ksh);
+    const int hk = h / a.G;                // K/V head of this query head
+    const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + hk * a.ksh);
+    const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + hk * a.ksh);
+    // keys this lane's row may see, and the fewest any row of this wave may see
+    const int lane_lim = min(Sk, row_key_limit<MASK>(a, row));
+    const int wave_lim = min(Sk, row_key_limit<MASK>(a, row_w0));
     const int nk = k1 - k0;   // key tiles of this segment
 
     floatx16 o[4];
@@ -496,10 +516,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     // Softmax of the segment's tile j (scores in s): probabilities into p, row sum into l_part.
     auto softmax = [&](int j) {
       const int key0 = (k0 + j) * BK;
-      bool need_mask = key0 + BK > Sk;
-      if (MASK == CA_MASK_CAUSAL_INCL) need_mask |= key0 + BK - 1 > row_w0;
-      if (MASK == CA_MASK_CAUSAL_STRICT) need_mask |= key0 + BK - 1 >= row_w0;
-      if (need_mask) apply_mask<MASK>(s, key0, hl, row, Sk);
+      if (key0 + BK > wave_lim) apply_mask(s, key0, hl, lane_lim);
       float mu;
       if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
       else mu = c2;
@@ -736,7 +753,7 @@ hipError_t launch_one(const AttnArgs& a, const Plan& p, hipStream_t s) {
 template <int MODE, int MASK>
 hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
   const Plan p = make_plan(a.B, a.H, a.Sq, a.Sk, MASK);
-  if (a.ws != nullptr && p.split) return launch_one<MODE, MASK, true>(a, p, s);
+  if (MASK != kMaskDcp && a.ws != nullptr && p.split) return launch_one<MODE, MASK, true>(a, p, s);
   return launch_one<MODE, MASK, false>(a, p, s);
 }
 
@@ -751,6 +768,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s) {
   switch (a.mask) {
     case CA_MASK_CAUSAL_INCL: return launch_mode<MODE_ONLINE, CA_MASK_CAUSAL_INCL>(a, s);
     case CA_MASK_CAUSAL_STRICT: return launch_mode<MODE_ONLINE, CA_MASK_CAUSAL_STRICT>(a, s);
+    case kMaskDcp: return launch_mode<MODE_ONLINE, kMaskDcp>(a, s);
     default: return launch_mode<MODE_ONLINE, CA_MASK_NONE>(a, s);
   }
 }

@@ -77,7 +77,17 @@ struct AttnArgs {
   // key-split workspace (bf16 path); NULL: one workgroup per query tile
   void* ws;
   size_t ws_bytes;
+  // query heads per K/V head (1: MHA); query head h reads K/V head h / G (bf16 path)
+  int G;
+  // kMaskDcp: DCP prefill slice of rank dcp_R in a group of dcp_W, interleave dcp_I
+  int dcp_I, dcp_W, dcp_R;
 };
+
+// Internal mask (bf16 path, online-max only): the keys are rank R's slice of a chunk
+// whose positions are dealt to W ranks in blocks of I (slice token j at chunk position
+// (j / I) * W * I + R * I + j % I) and query i sits at chunk position i; key j is
+// visible iff its position is <= i, i.e. iff j < local_filled(i + 1).
+constexpr int kMaskDcp = 3;
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s);
@@ -139,6 +149,26 @@ __host__ __device__ inline int dcp_active_owner(int N, int block_size, int inter
 constexpr int kDecodeSplitTokens = 1024;   // tokens per decode split (64 blocks of 16)
 size_t decode_workspace_bytes(int B, int Hq, int D, int block_size, int max_blocks);
 hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s);
+// DCP prefill (segmented attention) of one rank; B == 1, D == 128, block size 16.
+struct SegmentedArgs {
+  const void* q;            // [S, Hq, D] bf16, strides qss, qsh
+  int64_t qss, qsh;
+  const void* k_cur;        // [S_local, Hkv, D] bf16, strides kss, ksh (v_cur the same)
+  const void* v_cur;
+  int64_t kss, ksh;
+  const void* k_cache;      // [num_blocks, Hkv, 16, D] bf16
+  const void* v_cache;      // [num_blocks, Hkv, D, 16] bf16
+  const int32_t* block_table;
+  int num_blocks, prior;    // prior: this rank's prior slots
+  int rank, world, interleave;
+  int Hq, Hkv, S, S_local;
+  float scale;
+  float* o;                 // [Hq, S, D] fp32
+  float* lse;               // [Hq, S] fp32
+  void* ws;                 // segmented_workspace_bytes()
+};
+size_t segmented_workspace_bytes(int Hq, int Hkv, int S, int D, int prior);
+hipError_t launch_segmented(const SegmentedArgs& g, hipStream_t s);
 hipError_t launch_kv_copy(void* dk, void* dv, const void* sk, const void* sv, size_t bytes, hipStream_t s);
 
 }  // namespace ctxattn

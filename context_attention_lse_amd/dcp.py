@@ -138,3 +138,48 @@ class DcpDecode:
                                           lse=self.lse_parts[r], workspace=self.ws[r])
         api.lse_merge(self.o_parts, self.lse_parts, out=self.out, lse_out=self.lse)
         return self.out, self.lse
+
+
+def rank_slice(x, world: int, rank: int, interleave: int):
+    """Rank ``rank``'s tokens of a chunk x [1, S, H, D] in local order: the blocks of
+    ``interleave`` positions that the slot mapping deals to it (S a multiple of W * I)."""
+    _, S, H, D = x.shape
+    if S % (world * interleave):
+        raise ValueError(f"chunk length {S} is not a multiple of world * interleave = {world * interleave}")
+    return x.view(S // (world * interleave), world, interleave, H, D)[:, rank].reshape(1, S // world, H, D)
+
+
+class DcpPrefill:
+    """DCP prefill of one chunk on one GPU: every rank's segmented attention (its prior
+    cache plus its slice of the chunk), then the LSE merge over the ranks, standing in
+    for the page's LSE all-gather and output reduce-scatter.
+
+    q [1, S, Hq, D]: the chunk's queries; k_chunk, v_chunk [1, S, Hkv, D]: the chunk's
+    keys/values in global order (each rank keeps only its slice); caches: one ShardCache
+    per rank holding the prior tokens (batch of one sequence); prior_global: the prior
+    length."""
+
+    def __init__(self, q, k_chunk, v_chunk, caches, prior_global, interleave=16, scale=None):
+        self.W = len(caches)
+        self.q, self.caches, self.interleave, self.scale = q, list(caches), interleave, scale
+        self.k_local = [rank_slice(k_chunk, self.W, r, interleave).contiguous() for r in range(self.W)]
+        self.v_local = [rank_slice(v_chunk, self.W, r, interleave).contiguous() for r in range(self.W)]
+        self.prior = [local_filled(prior_global, r, interleave, self.W) for r in range(self.W)]
+        _, S, Hq, D = q.shape
+        Hkv = k_chunk.shape[2]
+        dev = q.device
+        self.o_parts = torch.empty((self.W, Hq, S, D), dtype=torch.float32, device=dev)
+        self.lse_parts = torch.empty((self.W, Hq, S), dtype=torch.float32, device=dev)
+        self.ws = [torch.empty(max(16, api.segmented_attention_workspace_size(Hq, Hkv, S, D, n)), dtype=torch.uint8,
+                               device=dev) for n in self.prior]
+        self.out = torch.empty((Hq, S, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((Hq, S), dtype=torch.float32, device=dev)
+
+    def run(self):
+        for r, sc in enumerate(self.caches):
+            api.segmented_attention_partial(self.q, self.k_local[r], self.v_local[r], sc.k_pool, sc.v_pool,
+                                            sc.block_table[0], self.prior[r], r, self.W, self.interleave,
+                                            scale=self.scale, out=self.o_parts[r], lse=self.lse_parts[r],
+                                            workspace=self.ws[r])
+        api.lse_merge(self.o_parts, self.lse_parts, out=self.out, lse_out=self.lse)
+        return self.out, self.lse

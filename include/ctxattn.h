@@ -255,6 +255,45 @@ ca_status dcp_decode_partial_active(const void* q, const void* k_pool, const voi
                                     int max_blocks, int num_blocks, float softmax_scale, float* o,
                                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * segmented_attention_partial -- one rank's DCP prefill attention for a chunk: every query
+ * of the chunk against this rank's prior tokens (in the paged cache) and its slice of the
+ * chunk, causal on global positions; the rank's partial output and LSE, to be merged
+ * across the group with lse_merge (the page's LSE all-gather and reduce-scatter).
+ * Source: DCP page, "Segmented Attention CP": Purpose, API and Algorithm steps 1-4
+ * (prior read from the cache and masked by slot count, prior + current keys, causal mask
+ * from global positions: prior slot s at (s / I)(W I) + R I + s % I, chunk token j at
+ * prior_global + (j / I)(W I) + R I + j % I, query i at prior_global + i).
+ *
+ *   q             [1, S, Hq, D] bf16, strides qs: every query of the chunk, in global order
+ *   k_cur, v_cur  [1, S_local, Hkv, D] bf16, strides kvs: this rank's slice of the chunk
+ *                 (S_local = S / world; S a multiple of world * interleave)
+ *   k_cache       [num_blocks, Hkv, 16, D] bf16 and v_cache [num_blocks, Hkv, D, 16] bf16:
+ *                 the paged prior cache in dcp_decode_partial's layout
+ *   block_table   [max_blocks] int32: physical block of prior slot s / 16; an id outside
+ *                 [0, num_blocks) reads as an all-zero block
+ *   prior_tokens  this rank's prior slots (local_filled of the global prior length; 0 on
+ *                 the first chunk). Every prior position precedes every query of the
+ *                 chunk, so the prior keys carry no mask.
+ *   rank, world, interleave   the rank's place in the DCP group and the interleave size
+ *   o             OUT [Hq, S, D] fp32; lse OUT [Hq, S] fp32 (natural log; -inf for a query
+ *                 that sees no key of this rank)
+ *   workspace     segmented_attention_workspace_size() bytes (0 when prior_tokens == 0)
+ * Query head h reads K/V head h / (Hq / Hkv). Supported: D == 128, Hkv <= 16, one
+ * sequence per call. Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_UNSUPPORTED,
+ * CA_ERR_WORKSPACE, CA_ERR_HIP.
+ */
+ca_status segmented_attention_partial(const void* q, ca_strides qs, const void* k_cur, const void* v_cur,
+                                      ca_strides kvs, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, int max_blocks, int num_blocks,
+                                      int prior_tokens, int rank, int world, int interleave, int Hq,
+                                      int Hkv, int S, int S_local, int D, float softmax_scale, float* o,
+                                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace segmented_attention_partial needs for these sizes. */
+ca_status segmented_attention_workspace_size(int Hq, int Hkv, int S, int D, int prior_tokens,
+                                             size_t* bytes);
+
 /* Bytes of device workspace dcp_decode_partial needs for these sizes. */
 ca_status dcp_decode_workspace_size(int B, int Hq, int D, int block_size, int max_blocks,
                                     size_t* bytes);

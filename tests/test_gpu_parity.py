@@ -429,3 +429,61 @@ def test_decode_active_rejects_bad_rank(dev):
         ca.dcp_decode_partial_active(q, kp, vp, bt, n, kc, kc, 2, 2)
     with pytest.raises(ca.CtxAttnError, match="interleave"):
         ca.dcp_decode_partial_active(q, kp, vp, bt, n, kc, kc, 0, 2, interleave=5)
+
+
+# ---------------------------------------------------------------- DCP prefill (segmented attention)
+
+def _prefill_case(dev, world, interleave, prior_global, S, Hq, Hkv, seed=11):
+    ca = _ca()
+    say(f"prefill world={world} I={interleave} prior={prior_global} S={S} Hq={Hq} Hkv={Hkv}")
+    D = 128
+    dt = torch.bfloat16
+    q = gen.normal((1, S, Hq, D), seed, dev, dt)
+    k_all = gen.normal((prior_global + S, Hkv, D), seed + 1, dev, dt)
+    v_all = gen.normal((prior_global + S, Hkv, D), seed + 2, dev, dt)
+    k_chunk = k_all[prior_global:].unsqueeze(0)
+    v_chunk = v_all[prior_global:].unsqueeze(0)
+    offsets = np.array([0, prior_global])
+    rand = torch.rand((prior_global // 16 + 2 * world + 2,), generator=torch.Generator().manual_seed(seed),
+                      dtype=torch.float64).numpy()
+    caches = [ca.dcp.build_shard_cache(k_all, v_all, offsets, np.array([prior_global]), r, world, interleave, 16, rand)
+              for r in range(world)]
+    run = ca.dcp.DcpPrefill(q, k_chunk, v_chunk, caches, prior_global, interleave)
+    o, l = run.run()
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(D)
+    for r in range(world):
+        prior = [p for p in range(prior_global) if (p // interleave) % world == r]
+        cur = [j for j in range(S) if (j // interleave) % world == r]
+        po, pl = oracle.segmented_attention_partial(q[0], k_chunk[0, cur], v_chunk[0, cur], k_all[prior], v_all[prior],
+                                                    prior_global, r, interleave, world, scale)
+        check(f"rank {r} partial", run.o_parts[r], run.lse_parts[r], po, pl)
+    allowed = oracle.causal_allowed(prior_global + np.arange(S), np.arange(prior_global + S))
+    fo, fl = oracle.attention_heads(q, k_all.unsqueeze(0), v_all.unsqueeze(0), scale, allowed,
+                                    kv_head_of=lambda h: h // (Hq // Hkv))
+    check("merged", o, l, fo[0], fl[0])
+
+
+@pytest.mark.parametrize("world,interleave,prior_rounds", [(1, 16, 0), (2, 16, 0), (2, 16, 13), (4, 16, 5),
+                                                           (2, 4, 40), (3, 8, 7)])
+def test_prefill_segmented_matches_oracle(dev, world, interleave, prior_rounds):
+    rnd = world * interleave
+    S = rnd * ((640 + rnd - 1) // rnd)        # several 256-row query tiles and a ragged one
+    _prefill_case(dev, world, interleave, prior_rounds * rnd, S, 8, 2)
+
+
+def test_prefill_segmented_mha(dev):
+    _prefill_case(dev, 2, 16, 32 * 40, 1024, 4, 4)
+
+
+def test_prefill_rejects_bad_chunk(dev):
+    ca = _ca()
+    q = torch.zeros((1, 48, 2, 128), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((1, 24, 2, 128), dtype=torch.bfloat16, device=dev)
+    kcache = torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16, device=dev)
+    vcache = torch.zeros((1, 2, 128, 16), dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros((1,), dtype=torch.int32, device=dev)
+    with pytest.raises(ca.CtxAttnError, match="multiple"):
+        ca.segmented_attention_partial(q, kc, kc, kcache, vcache, bt, 0, 0, 2, 16)   # 48 % 32 != 0
+    with pytest.raises(ca.CtxAttnError, match="exceeds"):
+        ca.segmented_attention_partial(q, kc, kc, kcache, vcache, bt, 17, 0, 2, 8)
