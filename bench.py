@@ -297,13 +297,44 @@ def run_decode(args, torch, ca, workloads, gen, dev):
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     per_launch = [sc.nbytes_kv / (m * 1e-3) / 1e9 for sc, m in zip(shards, shard_ms)]
     ach = sum(per_launch) / len(per_launch)
+    # the same step with a current token: the caches hold positions [0, N) of each sequence
+    # and the new token at position N joins on its owner shard only (dcp_active_mask)
+    prior = torch.tensor([int(n) for n in d["ctx"]], dtype=torch.int32, device=dev)
+    k_cur = gen.normal((wl.B, wl.Hkv, wl.D), 1000 * wl.seed + 21, dev, torch.bfloat16)
+    v_cur = gen.normal((wl.B, wl.Hkv, wl.D), 1000 * wl.seed + 22, dev, torch.bfloat16)
+    ms_active = time_calls(lambda: run.run_active(prior, k_cur, v_cur, wl.interleave), steps, torch)
     return {"workload": wl.name, "config": "B=32 Hq=64 Hkv=8 D=128 bf16, ctx U[32k,128k], block 16, 2 interleaved shards",
             "kv_bytes": kv_bytes, "ms_per_step": round(ms, 4), "kv_GBps": round(gbs, 1),
+            "with_current_token": {"ms_per_step": round(ms_active, 4),
+                                   "kv_GBps": round(kv_bytes / (ms_active * 1e-3) / 1e9, 1),
+                                   "note": "N resident tokens on their shards plus a new token at position N, attended on its owner shard only"},
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic("dcp_decode/dcp_decode_gqa"),
                          "kernel": "dcp_decode_split_kernel + combine (dcp_decode_partial)",
                          "per_launch": "one shard's resident K+V bytes = local tokens * Hkv * D * 2 * 2"}}
+
+
+def run_prefill(args, torch, ca, workloads, gen, dev):
+    """DCP prefill of one chunk (segmented attention on every rank + the LSE merge):
+    S = 8192 new tokens after 65536 prior ones, 32 query heads over 8 KV heads, D = 128,
+    DCP = 2 ranks interleaving blocks of 16, bf16; synthetic N(0, 1) inputs."""
+    import numpy as np
+    S, P, Hq, Hkv, D, W, I = 8192, 65536, 32, 8, 128, 2, 16
+    log("[bench] dcp prefill")
+    q = gen.normal((1, S, Hq, D), 901, dev, torch.bfloat16)
+    k_all = gen.normal((P + S, Hkv, D), 902, dev, torch.bfloat16)
+    v_all = gen.normal((P + S, Hkv, D), 903, dev, torch.bfloat16)
+    offsets = np.array([0, P])
+    caches = [ca.dcp.build_shard_cache(k_all, v_all, offsets, np.array([P]), r, W, I, 16) for r in range(W)]
+    run = ca.dcp.DcpPrefill(q, k_all[P:].unsqueeze(0), v_all[P:].unsqueeze(0), caches, P, I)
+    del k_all, v_all
+    ms = time_calls(run.run, max(3, args.steps // 4), torch)
+    flops = 4.0 * Hq * D * (S * P + S * (S + 1) / 2)
+    return {"workload": "dcp_prefill_chunk", "config": f"S={S} after {P} prior, Hq={Hq} Hkv={Hkv} D={D}, DCP={W} "
+            f"interleave {I}, bf16, both ranks + merge", "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def run_tiny(args, torch, ca, workloads, gen, dev):
@@ -342,7 +373,8 @@ def run_copy(args, torch, ca, workloads, gen, dev):
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
-EXTRAS = {"constmax": run_constmax, "striped": run_striped, "decode": run_decode, "tiny": run_tiny, "copy": run_copy}
+EXTRAS = {"constmax": run_constmax, "striped": run_striped, "decode": run_decode, "prefill": run_prefill,
+          "tiny": run_tiny, "copy": run_copy}
 
 
 def main():
@@ -354,7 +386,7 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="time only the step kernel's back-to-back launches (for profiling it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="constmax,striped,decode,tiny",
+    ap.add_argument("--only", default="constmax,striped,decode,prefill,tiny",
                     help="comma-separated extra workloads to run after the headline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
