@@ -18,7 +18,8 @@ What it computes, and where the pages define it:
   without measuring it"), the pure-addition fold over ring steps ("A static bound
   makes the ring reduction pure addition"), one normalisation with the row sum
   clamped at 1e-37 ("Accumulate, then normalize once"), and lse = c + log(sum)
-  (Interface, ``training``).
+  (Interface, ``training``). ``const_max_sink_robust``: the same with a handful of
+  huge-norm keys taken out of the bound and attended exactly ("Adapting this kernel").
 - ``sharding``: contiguous and striped ring sharding (Striped Attention on the
   sequence-sharding survey page; ring schedule from the kernel reference page's
   Overview figure) and the DCP interleave rules (DCP page: local_filled
@@ -38,6 +39,8 @@ from .attention import (  # noqa: F401
     merge_lse,
     const_max,
     const_max_bound,
+    const_max_sink_robust,
+    key_sinks,
 )
 from .sharding import (  # noqa: F401
     contiguous_tokens,

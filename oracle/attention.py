@@ -157,3 +157,45 @@ def const_max(q, k_chunks, v_chunks, scale, clamp=SUM_CLAMP):
             A[r0:r1] += p @ vc
     Zc = np.maximum(Z, clamp)
     return A / Zc[:, None], c + np.log(Zc), c
+
+
+def key_sinks(k_chunks, theta, max_sinks):
+    """Sink keys of the ring: |k_j| above theta times the mean key norm over every chunk
+    (kernel reference page, "Adapting this kernel": a handful of keys whose norms dwarf the
+    rest inflate max_j |k_j| for every row; excluding them from the max recovers the bound).
+    The mean of the norms, not of their squares, so that a few sinks 100-1000x louder than
+    the rest barely move the reference. More than ``max_sinks`` such keys, or theta <= 0,
+    means no exclusion. Returns one bool mask per chunk."""
+    k_chunks = [to_f64(x) for x in k_chunks]
+    norms = [np.sqrt((kc * kc).sum(axis=1)) for kc in k_chunks]
+    total = sum(int(n.shape[0]) for n in norms)
+    if theta <= 0 or total == 0:
+        return [np.zeros(n.shape[0], dtype=bool) for n in norms]
+    mean = sum(float(n.sum()) for n in norms) / total
+    masks = [n > theta * mean for n in norms]
+    if sum(int(m.sum()) for m in masks) > max_sinks:
+        return [np.zeros(n.shape[0], dtype=bool) for n in norms]
+    return masks
+
+
+def const_max_sink_robust(q, k_chunks, v_chunks, scale, theta, max_sinks, clamp=SUM_CLAMP):
+    """Const-max with the sinks taken out of the bound: the bound c_i uses the largest
+    non-sink key norm, the const-max fold runs over the non-sink keys, the sink keys are
+    attended exactly on their own, and the two partials are merged by the LSE rule.
+    Returns (O [Sq, Dv], lse [Sq], c [Sq]). In exact arithmetic this is ``attention``."""
+    q = to_f64(q)
+    k_chunks = [to_f64(x) for x in k_chunks]
+    v_chunks = [to_f64(x) for x in v_chunks]
+    masks = key_sinks(k_chunks, theta, max_sinks)
+    kn = [kc[~m] for kc, m in zip(k_chunks, masks)]
+    vn = [vc[~m] for vc, m in zip(v_chunks, masks)]
+    ks = np.concatenate([kc[m] for kc, m in zip(k_chunks, masks)], axis=0)
+    vs = np.concatenate([vc[m] for vc, m in zip(v_chunks, masks)], axis=0)
+    Dv = v_chunks[0].shape[1]
+    if sum(x.shape[0] for x in kn):
+        o_n, lse_n, c = const_max(q, kn, vn, scale, clamp)
+    else:
+        o_n, lse_n, c = np.zeros((q.shape[0], Dv)), np.full(q.shape[0], -np.inf), np.zeros(q.shape[0])
+    o_s, lse_s = attention(q, ks, vs, scale)
+    o, lse = merge_lse([o_n, o_s], [lse_n, lse_s])
+    return o, lse, c

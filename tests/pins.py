@@ -300,3 +300,68 @@ def pins_segmented(seg_partial, world, interleave, prior_rounds):
     if not (np.allclose(parts[r][0][1, S - 2], bo[0], atol=TOL) and _close(parts[r][1][1, S - 2], bl[0])):
         bad.append("one query of the last rank")
     return bad
+
+
+def pins_sink_robust(robust, key_sinks):
+    """robust(q, k_chunks, v_chunks, scale, theta, max_sinks) -> (O, lse, c);
+    key_sinks(k_chunks, theta, max_sinks) -> masks. Sinks: keys whose |k| exceeds theta
+    times the mean key norm of the ring; the bound then spans the other keys. Returns the
+    failures."""
+    bad = []
+    rng = np.random.default_rng(29)
+    D = 8
+    q = rng.normal(size=(7, D)) * 3.0
+    ks = [rng.normal(size=(6, D)) for _ in range(3)]
+    vs = [rng.normal(size=(6, 3)) for _ in range(3)]
+    # two keys with norms far above the rest (massive-activation sinks)
+    ks[0][4] *= 60.0
+    ks[2][1] = -ks[2][1] * 45.0
+    k_all = np.concatenate(ks); v_all = np.concatenate(vs)
+    masks = key_sinks(ks, 4.0, 32)
+    n2 = (k_all * k_all).sum(axis=1)
+    want = np.sqrt(n2) > 4.0 * np.sqrt(n2).mean()
+    if not np.array_equal(np.concatenate(masks), want) or int(want.sum()) != 2:
+        bad.append("sink_selection")
+    # equals exact attention (by brute force), where the plain bound collapses every row
+    o, l, c = robust(q, ks, vs, 0.5, 4.0, 32)
+    bo, bl = brute_attention(q, k_all, v_all, 0.5)
+    if not (_close(o, bo, 1e-10) and _close(l, bl, 1e-10)):
+        bad.append("equals_exact_with_sinks")
+    # the bound spans the non-sink keys only, and still bounds each of their scores
+    kmax_n = max(n2[~want])
+    if not _close(c, 0.5 * np.linalg.norm(q, axis=1) * math.sqrt(kmax_n)):
+        bad.append("bound_without_sinks")
+    if not np.all(0.5 * (q @ k_all[~want].T) <= c[:, None] + 1e-12):
+        bad.append("bound_is_upper_for_the_rest")
+    # too many candidates: no exclusion (the plain bound), still exact here (no collapse)
+    masks1 = key_sinks(ks, 4.0, 1)
+    if any(m.any() for m in masks1):
+        bad.append("cap_disables_exclusion")
+    # without sinks nothing is excluded and the result is exact attention
+    ks3 = [rng.normal(size=(6, D)) for _ in range(3)]
+    o3, l3, _ = robust(q, ks3, vs, 0.5, 4.0, 32)
+    bo3, bl3 = brute_attention(q, np.concatenate(ks3), v_all, 0.5)
+    if any(m.any() for m in key_sinks(ks3, 4.0, 32)) or not (_close(o3, bo3, 1e-10) and _close(l3, bl3, 1e-10)):
+        bad.append("no_sinks_plain")
+    # the reference is the mean of the norms: a key 4x louder than thirty unit keys stays
+    # below 4 x mean norm (4.39), though its square is far above 4 x the mean square
+    unit = np.eye(D)[np.arange(30) % D]
+    loud = np.zeros((1, D)); loud[0, 0] = 4.0
+    if any(m.any() for m in key_sinks([unit, loud], 4.0, 32)):
+        bad.append("reference_is_mean_norm")
+    loud[0, 0] = 5.0   # now above 4 x mean norm (4.52)
+    if not key_sinks([unit, loud], 4.0, 32)[1].all():
+        bad.append("reference_is_mean_norm_above")
+    # theta <= 0 disables exclusion
+    if any(m.any() for m in key_sinks(ks, 0.0, 32)):
+        bad.append("theta_off")
+    # an empty chunk and a chunk made only of sinks
+    ks4 = [ks[0], np.zeros((0, D)), ks[1], 80.0 * rng.normal(size=(1, D))]
+    vs4 = [vs[0], np.zeros((0, 3)), vs[1], rng.normal(size=(1, 3))]
+    if sum(int(m.sum()) for m in key_sinks(ks4, 4.0, 32)) != 2:
+        bad.append("sink_only_chunk_selection")
+    o4, l4, _ = robust(q, ks4, vs4, 0.5, 4.0, 32)
+    bo4, bl4 = brute_attention(q, np.concatenate(ks4), np.concatenate(vs4), 0.5)
+    if not (_close(o4, bo4, 1e-10) and _close(l4, bl4, 1e-10)):
+        bad.append("empty_and_sink_only_chunks")
+    return bad

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from pins import pins_attention, pins_const_max, pins_dcp_active, pins_merge, pins_segmented
+from pins import pins_attention, pins_const_max, pins_dcp_active, pins_merge, pins_segmented, pins_sink_robust
 
 
 def _attn_factory(scale_pow=1, use_max=True, lse_log=np.log, normalise=True, honour_mask=True,
@@ -204,3 +204,58 @@ def test_segmented_reference_copy_passes():
     assert not any(pins_segmented(_segmented_factory(), W, I, pr) for W, I, pr in ((2, 4, 1), (4, 4, 3), (2, 16, 0)))
     assert not any(pins_dcp_active(_active_factory(lambda N, r, I, W: (N // I) % W == r), W, I)
                    for W, I in ((2, 16), (4, 4), (3, 1)))
+
+
+
+# ---------------------------------------------------------------- sink-robust const-max
+
+def _robust_factory(bound_over_all=False, drop_sinks=False, double_count=False, theta_on_squares=False):
+    def key_sinks(k_chunks, theta, max_sinks):
+        k_chunks = [np.asarray(x, float) for x in k_chunks]
+        norms = [(kc * kc).sum(axis=1) for kc in k_chunks]
+        allv = np.concatenate(norms)
+        if theta <= 0 or allv.size == 0:
+            return [np.zeros(n.shape[0], bool) for n in norms]
+        if theta_on_squares:
+            masks = [n > theta * allv.mean() for n in norms]
+        else:
+            masks = [np.sqrt(n) > theta * np.sqrt(allv).mean() for n in norms]
+        if sum(int(m.sum()) for m in masks) > max_sinks:
+            return [np.zeros(n.shape[0], bool) for n in norms]
+        return masks
+
+    def robust(q, k_chunks, v_chunks, scale, theta, max_sinks):
+        masks = key_sinks(k_chunks, theta, max_sinks)
+        kn = [kc if double_count else kc[~m] for kc, m in zip(k_chunks, masks)]
+        vn = [vc if double_count else vc[~m] for vc, m in zip(v_chunks, masks)]
+        ks = np.concatenate([kc[m] for kc, m in zip(k_chunks, masks)])
+        vs = np.concatenate([vc[m] for vc, m in zip(v_chunks, masks)])
+        if bound_over_all:
+            # the fold over the kept keys, but with the bound taken over every key
+            c, _ = oracle.const_max_bound(q, k_chunks, scale)
+            Z = sum(np.exp(scale * (q @ np.asarray(x, float).T) - c[:, None]).sum(axis=1) for x in kn if len(x))
+            A = sum(np.exp(scale * (q @ np.asarray(x, float).T) - c[:, None]) @ np.asarray(y, float)
+                    for x, y in zip(kn, vn) if len(x))
+            Zc = np.maximum(Z, oracle.SUM_CLAMP)
+            o_n, l_n = A / Zc[:, None], c + np.log(Zc)
+        else:
+            o_n, l_n, c = oracle.const_max(q, kn, vn, scale)
+        if drop_sinks:
+            return o_n, l_n, c
+        o_s, l_s = oracle.attention(q, ks, vs, scale)
+        o, l = oracle.merge_lse([o_n, o_s], [l_n, l_s])
+        return o, l, c
+    return robust, key_sinks
+
+
+ROBUST_MUTANTS = {
+    "bound_over_every_key": _robust_factory(bound_over_all=True),
+    "sinks_not_attended": _robust_factory(drop_sinks=True),
+    "sinks_counted_twice": _robust_factory(double_count=True),
+    "threshold_on_squared_norms": _robust_factory(theta_on_squares=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROBUST_MUTANTS))
+def test_sink_robust_mutant_caught(name):
+    assert pins_sink_robust(*ROBUST_MUTANTS[name]), name

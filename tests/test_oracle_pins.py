@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 
-from pins import brute_attention, pins_attention, pins_const_max, pins_dcp_active, pins_merge, pins_segmented
+from pins import (brute_attention, pins_attention, pins_const_max, pins_dcp_active, pins_merge, pins_segmented,
+                  pins_sink_robust)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -200,6 +201,24 @@ def test_dcp_decode_ungated_active_token_is_not_full_attention():
 @pytest.mark.parametrize("prior_rounds", [0, 1, 3])
 def test_dcp_prefill_segments_merge_to_causal_attention(world, interleave, prior_rounds):
     assert pins_segmented(oracle.segmented_attention_partial, world, interleave, prior_rounds) == []
+
+
+def test_sink_robust_const_max_pinned():
+    assert pins_sink_robust(oracle.const_max_sink_robust, oracle.key_sinks) == []
+
+
+def test_plain_const_max_collapses_on_the_sink_pin_input():
+    """The input of the sink pins defeats the plain bound: rows collapse (the page's named
+    failure), so the robust result above is not the plain one by accident."""
+    rng = np.random.default_rng(29)
+    q = rng.normal(size=(7, 8)) * 3.0
+    ks = [rng.normal(size=(6, 8)) for _ in range(3)]
+    vs = [rng.normal(size=(6, 3)) for _ in range(3)]
+    ks[0][4] *= 60.0
+    ks[2][1] = -ks[2][1] * 45.0
+    o, l, _ = oracle.const_max(q, ks, vs, 0.5)
+    eo, el = oracle.attention(q, np.concatenate(ks), np.concatenate(vs), 0.5)
+    assert np.abs(l - el).max() > 1.0
 
 
 def test_sum_clamp_value():
