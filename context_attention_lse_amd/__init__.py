@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     CtxAttnError,
     const_max_acc_size,
     const_max_bound,
+    const_max_sink_prologue,
     dcp_decode_partial,
     dcp_decode_partial_active,
     dcp_decode_workspace_size,
@@ -22,6 +23,8 @@ from .api import (  # noqa: F401
     ring_attn_workspace_size,
     segmented_attention_partial,
     segmented_attention_workspace_size,
+    sink_attention_partial,
+    sink_attention_workspace_size,
     step_workspace,
     version,
 )
@@ -31,6 +34,7 @@ __all__ = [
     "CtxAttnError", "const_max_acc_size", "const_max_bound", "dcp_decode_partial", "dcp_decode_partial_active",
     "dcp_decode_workspace_size",
     "key_sqnorm_max", "kv_chunk_copy", "lse_merge", "ring_attn_const_max_step", "ring_attn_step", "ring_attn_workspace_size",
-    "segmented_attention_partial", "segmented_attention_workspace_size", "step_workspace", "version",
+    "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
+    "sink_attention_partial", "sink_attention_workspace_size", "step_workspace", "version",
     "dcp", "ring",
 ]

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libctxattn.so")
 SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "merge.hip", "bound.hip", "decode.hip", "copy.hip",
-           "segmented.hip"]
+           "segmented.hip", "sinks.hip"]
 ARCH = os.environ.get("CTXATTN_ARCH", "gfx950")
 
 FLAGS = [

@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTS = (
     "ring_attn_step", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "lse_merge",
     "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error",
-    "ca_version", "segmented_attention_partial", "segmented_attention_workspace_size",
+    "ca_version", "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
+    "ring_attn_const_max_step_sinks", "sink_attention_partial", "sink_attention_workspace_size",
 )
 
 
@@ -55,6 +56,12 @@ SIGNATURES = {
     "segmented_attention_partial": [_vp, ca_strides, _vp, _vp, ca_strides, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                     _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp],
     "segmented_attention_workspace_size": [_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
+    "const_max_sink_prologue": [_vp, _i64, ca_strides, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _vp],
+    "ring_attn_const_max_step_sinks": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                       _i, _vp, _i, _vp, _vp, _vp, _i, _i64, _vp, _sz, _vp],
+    "sink_attention_partial": [_vp, ca_strides, _vp, _vp, _i64, ca_strides, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
+                               _vp, _vp, _vp, _sz, _vp],
+    "sink_attention_workspace_size": [_i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
     "ca_last_error": [],
     "ca_version": [],
 }

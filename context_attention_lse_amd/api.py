@@ -126,16 +126,68 @@ def const_max_bound(q, kmax_sq, scale=None, out=None, stream=None):
     return out
 
 
+def const_max_sink_prologue(k_pool, theta, sink_cap=32, out=None, stream=None):
+    """Sink-robust bound prologue over a chunk pool [cp, B, S_local, H, D] (any strides with D
+    contiguous). Returns dict(kmax_sq, kmax_sq_robust, knorm_sum [B, H] fp32,
+    sink_idx [B, H, sink_cap] int32, sink_cnt [B, H] int32); ``out`` reuses such a dict."""
+    _check_cuda(k_pool)
+    cp, B, S, H, D = k_pool.shape
+    dev = k_pool.device
+    if out is None:
+        out = {"kmax_sq": torch.empty((B, H), dtype=torch.float32, device=dev),
+               "kmax_sq_robust": torch.empty((B, H), dtype=torch.float32, device=dev),
+               "knorm_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
+               "sink_idx": torch.zeros((B, H, sink_cap), dtype=torch.int32, device=dev),
+               "sink_cnt": torch.empty((B, H), dtype=torch.int32, device=dev)}
+    st = k_pool.stride()
+    _lib.call("const_max_sink_prologue", _ptr(k_pool), st[0], _lib.ca_strides(st[1], st[2], st[3]),
+              _dtype_code(k_pool), cp, B, S, H, D, float(theta), int(sink_cap), _ptr(out["kmax_sq"]),
+              _ptr(out["kmax_sq_robust"]), _ptr(out["knorm_sum"]), _ptr(out["sink_idx"]), _ptr(out["sink_cnt"]),
+              _stream(stream))
+    return out
+
+
+def sink_attention_workspace_size(B, H, D, sink_cap) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.call("sink_attention_workspace_size", B, H, D, int(sink_cap), ctypes.byref(n))
+    return int(n.value)
+
+
+def sink_attention_partial(q, k_pool, v_pool, sinks, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Exact attention of q [B, Sq, H, D] against the listed sink keys of the pool alone.
+    ``sinks``: the dict from const_max_sink_prologue. Returns (o [B, H, Sq, D], lse [B, H, Sq])."""
+    _check_cuda(q, k_pool, v_pool, out, lse, workspace)
+    cp, B, S, H, D = k_pool.shape
+    Sq = q.shape[1]
+    if k_pool.stride() != v_pool.stride() or k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must share shape and strides")
+    cap = sinks["sink_idx"].shape[2]
+    if workspace is None:
+        workspace = torch.empty(max(16, sink_attention_workspace_size(B, H, D, cap)), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    st = k_pool.stride()
+    _lib.call("sink_attention_partial", _ptr(q), _strides(q), _ptr(k_pool), _ptr(v_pool), st[0],
+              _lib.ca_strides(st[1], st[2], st[3]), cp, B, H, Sq, S, D, _scale(scale), _ptr(sinks["sink_idx"]),
+              _ptr(sinks["sink_cnt"]), cap, _ptr(out), _ptr(lse), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream))
+    return out, lse
+
+
 def const_max_acc_size(B, H, Sq, D) -> int:
     """Floats of the const-max accumulator: [B, H, Sq, D] output then [B, H, Sq] row sums."""
     return B * H * Sq * (D + 1)
 
 
 def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dtype=torch.float32,
-                             scale=None, workspace=None, stream=None):
+                             scale=None, workspace=None, stream=None, sinks=None, key_offset=0):
     """One const-max ring step. acc: fp32 tensor of const_max_acc_size floats (None allowed
     when phase == INIT|FINAL). On the FINAL phase returns (o [B, H, Sq, D], lse [B, H, Sq]).
-    ``workspace`` as for ring_attn_step."""
+    ``workspace`` as for ring_attn_step. ``sinks`` (the dict from const_max_sink_prologue)
+    leaves the listed keys out; ``key_offset`` is this chunk's first key index."""
     _check_cuda(q, k, v, c, acc, out, lse, workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
@@ -151,10 +203,17 @@ def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dty
             out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device)
         if lse is None:
             lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    _lib.call("ring_attn_const_max_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
-              B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase),
-              _ptr(out) if final else None, _DT.get(out.dtype, CA_FP32) if final else CA_FP32,
-              _ptr(lse) if final else None, *_ws(workspace), _stream(stream))
+    o_args = (_ptr(out) if final else None, _DT.get(out.dtype, CA_FP32) if final else CA_FP32,
+              _ptr(lse) if final else None)
+    if sinks is None:
+        _lib.call("ring_attn_const_max_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
+                  B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase), *o_args, *_ws(workspace),
+                  _stream(stream))
+    else:
+        _lib.call("ring_attn_const_max_step_sinks", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k),
+                  _dtype_code(q), B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase), *o_args,
+                  _ptr(sinks["sink_idx"]), _ptr(sinks["sink_cnt"]), sinks["sink_idx"].shape[2], int(key_offset),
+                  *_ws(workspace), _stream(stream))
     return (out, lse) if final else None
 
 

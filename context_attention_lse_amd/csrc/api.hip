@@ -157,10 +157,15 @@ ca_status const_max_bound(const void* q, ca_strides qs, int dtype, int B, int Sq
   return hip_status(e, "const_max_bound launch");
 }
 
-ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs,
-                                   int dtype, int B, int H, int Sq, int Sk, int D, float softmax_scale,
-                                   const float* c, float* acc, int phase, void* o, int o_dtype, float* lse,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ca_status const_max_step_impl(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype,
+                              int B, int H, int Sq, int Sk, int D, float softmax_scale, const float* c, float* acc,
+                              int phase, void* o, int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                              const int32_t* sink_idx, const int32_t* sink_cnt, int sink_cap, int64_t key_offset,
+                              void* stream) {
   CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
   if (phase < 0 || phase > (CA_PHASE_INIT | CA_PHASE_FINAL)) return fail(CA_ERR_SHAPE, "unknown phase %d", phase);
   if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
@@ -183,10 +188,103 @@ ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, 
   a.G = 1;
   a.c = c; a.acc = acc; a.phase = phase;
   a.o_cm = o; a.o_cm_bf16 = (o_dtype == CA_BF16); a.lse_cm = lse;
+  a.sink_idx = sink_idx; a.sink_cnt = sink_cnt; a.sink_cap = sink_cap; a.key_offset = key_offset;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, s);
   return hip_status(e, "ring_attn_const_max_step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs,
+                                   int dtype, int B, int H, int Sq, int Sk, int D, float softmax_scale,
+                                   const float* c, float* acc, int phase, void* o, int o_dtype, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return const_max_step_impl(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale, c, acc, phase, o, o_dtype, lse,
+                             workspace, workspace_bytes, nullptr, nullptr, 0, 0, stream);
+}
+
+ca_status ring_attn_const_max_step_sinks(const void* q, ca_strides qs, const void* k, const void* v,
+                                         ca_strides kvs, int dtype, int B, int H, int Sq, int Sk, int D,
+                                         float softmax_scale, const float* c, float* acc, int phase, void* o,
+                                         int o_dtype, float* lse, const int32_t* sink_idx, const int32_t* sink_cnt,
+                                         int sink_cap, int64_t key_offset, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  if (dtype != CA_BF16) return fail(CA_ERR_UNSUPPORTED, "sink lists need the bf16 path");
+  if (sink_cap < 1 || sink_cap > 64) return fail(CA_ERR_UNSUPPORTED, "sink_cap must be in [1, 64] (got %d)", sink_cap);
+  if (int64_t(B) * H * Sq > 0 && (!sink_idx || !sink_cnt)) return fail(CA_ERR_NULL, "sink_idx and sink_cnt are required");
+  if (key_offset < 0) return fail(CA_ERR_SHAPE, "negative key_offset");
+  return const_max_step_impl(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale, c, acc, phase, o, o_dtype, lse,
+                             workspace, workspace_bytes, sink_idx, sink_cnt, sink_cap, key_offset, stream);
+}
+
+ca_status const_max_sink_prologue(const void* k, int64_t chunk_stride, ca_strides ks, int dtype, int cp, int B,
+                                  int S_local, int H, int D, float theta, int sink_cap, float* kmax_sq,
+                                  float* kmax_sq_robust, float* knorm_sum, int32_t* sink_idx, int32_t* sink_cnt,
+                                  void* stream) {
+  CA_TRY(check_dtype(dtype));
+  if (D <= 0 || D % 8 || D > 128) return fail(CA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 in [8, 128]");
+  if (cp < 0 || chunk_stride < 0) return fail(CA_ERR_SHAPE, "bad chunk count or stride");
+  CA_TRY(check_bshd("k", k, ks, dtype, B, S_local, H, D));
+  if (sink_cap < 1 || sink_cap > 64) return fail(CA_ERR_UNSUPPORTED, "sink_cap must be in [1, 64] (got %d)", sink_cap);
+  if (H > 4096) return fail(CA_ERR_UNSUPPORTED, "at most 4096 heads");
+  if (int64_t(cp) * S_local >= (int64_t(1) << 31)) return fail(CA_ERR_UNSUPPORTED, "ring too long for int32 key indices");
+  if (int64_t(B) * H == 0) return hip_status(hipSuccess, "");
+  if (!kmax_sq || !kmax_sq_robust || !knorm_sum || !sink_idx || !sink_cnt)
+    return fail(CA_ERR_NULL, "kmax_sq, kmax_sq_robust, knorm_sum, sink_idx and sink_cnt are required");
+  if (((chunk_stride * (dtype == CA_BF16 ? 2 : 4)) & 15)) return fail(CA_ERR_SHAPE, "chunk stride must keep rows 16-byte aligned");
+  hipError_t e = ctxattn::launch_sink_prologue(k, chunk_stride, ks.b, ks.s, ks.h, dtype == CA_BF16, cp, B, S_local, H, D,
+                                               theta, sink_cap, kmax_sq, knorm_sum, kmax_sq_robust, sink_idx, sink_cnt,
+                                               static_cast<hipStream_t>(stream));
+  return hip_status(e, "const_max_sink_prologue launch");
+}
+
+ca_status sink_attention_workspace_size(int B, int H, int D, int sink_cap, size_t* bytes) {
+  if (!bytes) return fail(CA_ERR_NULL, "bytes is NULL");
+  if (B < 0 || H < 0 || D <= 0 || sink_cap < 0) return fail(CA_ERR_SHAPE, "bad sizes");
+  *bytes = size_t(2) * ((size_t(B) * sink_cap * H * D * 2 + 255) & ~size_t(255));
+  g_err[0] = 0;
+  return CA_OK;
+}
+
+ca_status sink_attention_partial(const void* q, ca_strides qs, const void* k, const void* v, int64_t chunk_stride,
+                                 ca_strides kvs, int cp, int B, int H, int Sq, int S_local, int D, float softmax_scale,
+                                 const int32_t* sink_idx, const int32_t* sink_cnt, int sink_cap, float* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (D != 128) return fail(CA_ERR_UNSUPPORTED, "bf16 attention supports head_dim 128 only (got %d)", D);
+  if (sink_cap < 1 || sink_cap > 64) return fail(CA_ERR_UNSUPPORTED, "sink_cap must be in [1, 64] (got %d)", sink_cap);
+  if (cp < 0 || chunk_stride < 0 || Sq < 0) return fail(CA_ERR_SHAPE, "bad sizes");
+  CA_TRY(check_bshd("q", q, qs, CA_BF16, B, Sq, H, D));
+  CA_TRY(check_bshd("k", k, kvs, CA_BF16, B, S_local, H, D));
+  CA_TRY(check_bshd("v", v, kvs, CA_BF16, B, S_local, H, D));
+  if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
+  if (!o || !lse || !sink_idx || !sink_cnt) return fail(CA_ERR_NULL, "o, lse, sink_idx and sink_cnt are required");
+  if (!aligned16(o)) return fail(CA_ERR_SHAPE, "o must be 16-byte aligned");
+  size_t need = 0;
+  sink_attention_workspace_size(B, H, D, sink_cap, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(CA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(CA_ERR_SHAPE, "workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* kg = static_cast<char*>(workspace);
+  char* vg = kg + need / 2;
+  hipError_t e = ctxattn::launch_sink_gather(k, v, chunk_stride, kvs.b, kvs.s, kvs.h, B, S_local, H, sink_cap, sink_idx,
+                                             sink_cnt, kg, vg, s);
+  if (e != hipSuccess) return hip_status(e, "sink gather launch");
+  ctxattn::AttnArgs a{};
+  a.q = q; a.qsb = qs.b; a.qss = qs.s; a.qsh = qs.h;
+  a.k = kg; a.v = vg; a.ksb = int64_t(sink_cap) * H * D; a.kss = int64_t(H) * D; a.ksh = D;
+  a.B = B; a.H = H; a.Sq = Sq; a.Sk = sink_cap; a.D = D;
+  a.scale = resolve_scale(softmax_scale, D);
+  a.sl2e = a.scale * ctxattn::kLog2e;
+  a.mask = CA_MASK_NONE;
+  a.G = 1;
+  a.o = o; a.lse = lse;
+  a.sk_of_bh = sink_cnt;
+  return hip_status(ctxattn::launch_attn_bf16(a, false, s), "sink_attention_partial launch");
 }
 
 ca_status lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t rows, int D, void* o_out,

@@ -47,6 +47,7 @@
 // count combines the segments in key order and writes the result. No workgroup ever waits
 // for another. The combiner resets the counter, so a workspace is ready for the next call.
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -204,6 +205,21 @@ __host__ __device__ inline int row_key_limit(const AttnArgs& a, int row) {
     return (n / round) * a.dcp_I + min(max(n - (n / round) * round - a.dcp_R * a.dcp_I, 0), a.dcp_I);
   }
   return a.Sk;
+}
+
+// Leaves out the sink keys of this tile: bit l of m marks lane l's sink (a chunk-local key
+// index held in `sink`) as falling in [key0, key0 + BK).
+__device__ __forceinline__ void mask_sinks(floatx16& s, int key0, int hl, uint64_t m, int sink) {
+  while (m) {
+    const int l = __builtin_ctzll(m);
+    m &= m - 1;
+    const int j_sink = __builtin_amdgcn_readlane(sink, l);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      s[r] = j == j_sink ? -INFINITY : s[r];
+    }
+  }
 }
 
 __device__ __forceinline__ void apply_mask(floatx16& s, int key0, int hl, int lim) {
@@ -438,10 +454,22 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     const int hk = h / a.G;                // K/V head of this query head
     const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + hk * a.ksh);
     const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + hk * a.ksh);
+    // keys of this (batch, head): the whole chunk, or its own count
+    const int Skb = a.sk_of_bh ? min(Sk, max(a.sk_of_bh[bh], 0)) : Sk;
+    if (!SPLIT) k1 = min(k1, (Skb + BK - 1) / BK);
     // keys this lane's row may see, and the fewest any row of this wave may see
-    const int lane_lim = min(Sk, row_key_limit<MASK>(a, row));
-    const int wave_lim = min(Sk, row_key_limit<MASK>(a, row_w0));
-    const int nk = k1 - k0;   // key tiles of this segment
+    const int lane_lim = min(Skb, row_key_limit<MASK>(a, row));
+    const int wave_lim = min(Skb, row_key_limit<MASK>(a, row_w0));
+    const int nk = max(k1 - k0, 0);   // key tiles of this segment
+    // sink keys to leave out: lane l holds this head's l-th sink as a chunk-local index
+    int my_sink = INT_MIN;
+    bool has_sinks = false;
+    if (a.sink_idx != nullptr) {
+      const int cnt = min(a.sink_cnt[bh], a.sink_cap);
+      has_sinks = cnt > 0;
+      if (lane < cnt) my_sink = int(a.sink_idx[int64_t(bh) * a.sink_cap + lane] - a.key_offset);
+      settle(my_sink);
+    }
 
     floatx16 o[4];
 #pragma unroll
@@ -465,8 +493,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       const char* kt = kbase + key0 * kss_bytes;
       const char* vt = vbase + key0 * kss_bytes;
       uint32_t ko = koff, vo = voff;
-      if (key0 + BK > Sk) {
-        const int rr = min(crow, Sk - 1 - key0);
+      if (key0 + BK > Skb) {
+        const int rr = max(0, min(crow, Skb - 1 - key0));
         ko = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ k_swz(crow)) << 4);
         vo = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ v_swz(crow)) << 4);
       }
@@ -517,6 +545,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     auto softmax = [&](int j) {
       const int key0 = (k0 + j) * BK;
       if (key0 + BK > wave_lim) apply_mask(s, key0, hl, lane_lim);
+      if (has_sinks) {
+        const uint64_t m = __ballot(my_sink >= key0 && my_sink < key0 + BK);
+        if (m) mask_sinks(s, key0, hl, m, my_sink);
+      }
       float mu;
       if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
       else mu = c2;

@@ -81,6 +81,14 @@ struct AttnArgs {
   int G;
   // kMaskDcp: DCP prefill slice of rank dcp_R in a group of dcp_W, interleave dcp_I
   int dcp_I, dcp_W, dcp_R;
+  // keys to leave out (bf16 path): per (batch, head) up to sink_cap global key indices
+  // sink_idx[bh * sink_cap + i] for i < sink_cnt[bh]; this chunk's first key is key_offset
+  const int32_t* sink_idx;
+  const int32_t* sink_cnt;
+  int sink_cap;
+  int64_t key_offset;
+  // per (batch, head) key count (bf16 path, no key split): keys [0, min(Sk, sk_of_bh[bh]))
+  const int32_t* sk_of_bh;
 };
 
 // Internal mask (bf16 path, online-max only): the keys are rank R's slice of a chunk
@@ -149,6 +157,15 @@ __host__ __device__ inline int dcp_active_owner(int N, int block_size, int inter
 constexpr int kDecodeSplitTokens = 1024;   // tokens per decode split (64 blocks of 16)
 size_t decode_workspace_bytes(int B, int Hq, int D, int block_size, int max_blocks);
 hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s);
+// Sink-robust const-max prologue over a pool of cp chunks (key (c, b, t, h) at element
+// c*cs + b*sb + t*ss + h*sh) and the gather of the listed sink rows ([B, cap, H, 128] bf16).
+hipError_t launch_sink_prologue(const void* k, int64_t cs, int64_t sb, int64_t ss, int64_t sh, bool bf16, int cp,
+                                int B, int S, int H, int D, float theta, int cap, float* kmax_sq, float* knorm_sum,
+                                float* kmax_robust, int32_t* sink_idx, int32_t* sink_cnt, hipStream_t s);
+hipError_t launch_sink_gather(const void* k, const void* v, int64_t cs, int64_t sb, int64_t ss, int64_t sh, int B,
+                              int S, int H, int cap, const int32_t* sink_idx, const int32_t* sink_cnt, void* kg,
+                              void* vg, hipStream_t s);
+
 // DCP prefill (segmented attention) of one rank; B == 1, D == 128, block size 16.
 struct SegmentedArgs {
   const void* q;            // [S, Hq, D] bf16, strides qss, qsh

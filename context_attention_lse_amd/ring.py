@@ -72,6 +72,9 @@ class RingPass:
 
     variant "online": every step emits a partial (o_s, lse_s) with ring_attn_step and
                       the partials are merged once with lse_merge;
+    variant "constmax" with sink_theta: keys whose norm exceeds sink_theta x the mean key
+                      norm (at most sink_cap per head) leave the bound and the fold, and are
+                      attended exactly in a second partial merged by LSE;
     variant "constmax": the bound is built from every chunk's key norms (the ring's
                       all_reduce(max) becomes a max-fold), then every step adds into one
                       fp32 accumulator and the last step normalises.
@@ -86,7 +89,7 @@ class RingPass:
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
                  scale=None, prefetch_depth=2, out_dtype=torch.float32, copy_stream=None,
-                 compute_streams=None, split=False):
+                 compute_streams=None, split=False, sink_theta=None, sink_cap=32):
         if variant not in ("online", "constmax"):
             raise ValueError(f"unknown variant {variant!r}")
         if variant == "constmax" and causal:
@@ -137,6 +140,19 @@ class RingPass:
             self.kmax = torch.empty((B, H), dtype=torch.float32, device=dev)
             self.c = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
             self.acc = torch.empty(api.const_max_acc_size(B, H, Sq, D), dtype=torch.float32, device=dev)
+        # sink-robust const-max: keys above sink_theta x the mean key norm leave the bound and
+        # the fold, and are attended exactly in a second partial merged by LSE
+        self.sink_theta = sink_theta if variant == "constmax" else None
+        if self.sink_theta is not None:
+            self.sinks = {"kmax_sq": torch.empty((B, H), dtype=torch.float32, device=dev),
+                          "kmax_sq_robust": torch.empty((B, H), dtype=torch.float32, device=dev),
+                          "knorm_sum": torch.empty((B, H), dtype=torch.float32, device=dev),
+                          "sink_idx": torch.zeros((B, H, sink_cap), dtype=torch.int32, device=dev),
+                          "sink_cnt": torch.empty((B, H), dtype=torch.int32, device=dev)}
+            self.o_parts = torch.empty((2, B, H, Sq, D), dtype=torch.float32, device=dev)
+            self.lse_parts = torch.empty((2, B, H, Sq), dtype=torch.float32, device=dev)
+            self.sink_ws = torch.empty(max(16, api.sink_attention_workspace_size(B, H, D, sink_cap)),
+                                       dtype=torch.uint8, device=dev)
         self.out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=dev)
         self.lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
         self.step_events = None
@@ -155,10 +171,15 @@ class RingPass:
             self.copied[step].record(self.copy_stream)
 
     def prologue(self):
-        """const-max bound: per-head max key norm over the whole ring, then c per row.
+        """const-max bound: per-head max key norm over the whole ring, then c per row (with
+        sinks: the max over the non-sink keys, and the sink lists).
         With one sequence and a contiguous pool, the chunks are one [1, cp*S, H, D] run of
         keys and the max-fold over the ring is a single call."""
         kp = self.k_pool
+        if self.sink_theta is not None:
+            api.const_max_sink_prologue(kp, self.sink_theta, out=self.sinks)
+            api.const_max_bound(self.q, self.sinks["kmax_sq_robust"], scale=self.scale, out=self.c)
+            return
         if kp.shape[1] == 1 and kp.is_contiguous():
             cp, _, S, H, D = kp.shape
             api.key_sqnorm_max(kp.view(1, cp * S, H, D), self.kmax)
@@ -203,8 +224,14 @@ class RingPass:
                         slot += 1
                 else:
                     phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
-                    api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out,
-                                                 lse=self.lse, scale=self.scale, workspace=ws)
+                    if self.sink_theta is None:
+                        api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out,
+                                                     lse=self.lse, scale=self.scale, workspace=ws)
+                    else:
+                        src = ring_source_rank(self.rank, s, cp)
+                        api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.o_parts[0],
+                                                     lse=self.lse_parts[0], scale=self.scale, workspace=ws,
+                                                     sinks=self.sinks, key_offset=src * k.shape[1])
                 if timing_events is not None:
                     timing_events[s][1].record(st)
             self.consumed[s].record(st)
@@ -212,6 +239,10 @@ class RingPass:
             cs.wait_stream(self.aux_stream)
         if self.variant == "online":
             api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
+        elif self.sink_theta is not None:
+            api.sink_attention_partial(self.q, self.k_pool, self.v_pool, self.sinks, scale=self.scale,
+                                       out=self.o_parts[1], lse=self.lse_parts[1], workspace=self.sink_ws)
+            api.lse_merge(self.o_parts, self.lse_parts, out=self.out, lse_out=self.lse)
         # the copy stream must not run ahead into the next call's buffers
         cs.wait_stream(self.copy_stream)
         return self.out, self.lse

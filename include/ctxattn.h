@@ -180,6 +180,68 @@ ca_status ring_attn_const_max_step(const void* q, ca_strides q_strides,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * const_max_sink_prologue -- the bound prologue with sink keys taken out of the max.
+ * Source: kernel reference page, "Adapting this kernel" (attention sinks: a handful of
+ * keys whose norms dwarf the rest inflate max_j |k_j| for every row; excluding those keys
+ * from the max reduction recovers the bound) and the prologue passages cited at
+ * key_sqnorm_max. A key is a sink when |k_j| > theta * (mean key norm of its (b, h) over
+ * every chunk); its exact contribution comes from sink_attention_partial.
+ *   k            chunk c, batch b, token t, head h at k + c*chunk_stride + b*ks.b + t*ks.s
+ *                + h*ks.h (elements); cp chunks of S_local tokens (the ring's pool); D a
+ *                multiple of 8 in [8, 128]; key index of (c, t) = c * S_local + t
+ *   theta        threshold factor (<= 0: no sinks)
+ *   sink_cap     1..64 sinks per (b, h); a head with more candidates keeps the plain max
+ *                and an empty list
+ *   kmax_sq      OUT [B, H] max |k|^2 over every key
+ *   kmax_sq_robust OUT [B, H] max |k|^2 over the non-sink keys (feed it to const_max_bound)
+ *   knorm_sum    OUT [B, H] sum of |k| (scratch of the threshold)
+ *   sink_idx     OUT [B, H, sink_cap] int32 sink key indices, ascending; sink_cnt OUT [B, H]
+ * The threshold's sum is accumulated with float atomics, so a key within rounding of the
+ * threshold may land on either side between runs; both are exact (a sink is attended
+ * exactly). Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_HIP.
+ */
+ca_status const_max_sink_prologue(const void* k, int64_t chunk_stride, ca_strides ks, int dtype, int cp,
+                                  int B, int S_local, int H, int D, float theta, int sink_cap,
+                                  float* kmax_sq, float* kmax_sq_robust, float* knorm_sum,
+                                  int32_t* sink_idx, int32_t* sink_cnt, void* stream);
+
+/*
+ * ring_attn_const_max_step_sinks -- ring_attn_const_max_step with the listed sink keys
+ * left out of the fold (their scores may exceed the robust bound). Same arguments, plus
+ *   sink_idx, sink_cnt, sink_cap  the lists from const_max_sink_prologue
+ *   key_offset   key index of this chunk's first key (source rank * S_local)
+ * bf16 only. Errors as ring_attn_const_max_step.
+ */
+ca_status ring_attn_const_max_step_sinks(const void* q, ca_strides qs, const void* k, const void* v,
+                                         ca_strides kvs, int dtype, int B, int H, int Sq, int Sk, int D,
+                                         float softmax_scale, const float* c, float* acc, int phase,
+                                         void* o, int o_dtype, float* lse, const int32_t* sink_idx,
+                                         const int32_t* sink_cnt, int sink_cap, int64_t key_offset,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sink_attention_partial -- exact (online-max) attention of every query row against the
+ * sink keys alone, as a partial output and LSE to merge (lse_merge) with the sink-robust
+ * const-max result. Gathers the listed K and V rows from the pool, then runs the bf16 step
+ * kernel with a per-head key count.
+ *   q            [B, Sq, H, D] bf16, strides qs
+ *   k, v         the pool as in const_max_sink_prologue (bf16; shared strides)
+ *   o            OUT [B, H, Sq, D] fp32; lse OUT [B, H, Sq] (-inf for a head with no sink)
+ *   workspace    sink_attention_workspace_size() bytes
+ * Supported: D == 128. Errors: CA_ERR_NULL, CA_ERR_SHAPE, CA_ERR_UNSUPPORTED,
+ * CA_ERR_WORKSPACE, CA_ERR_HIP.
+ */
+ca_status sink_attention_partial(const void* q, ca_strides qs, const void* k, const void* v,
+                                 int64_t chunk_stride, ca_strides kvs, int cp, int B, int H, int Sq,
+                                 int S_local, int D, float softmax_scale, const int32_t* sink_idx,
+                                 const int32_t* sink_cnt, int sink_cap, float* o, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace sink_attention_partial needs for these sizes. */
+ca_status sink_attention_workspace_size(int B, int H, int D, int sink_cap, size_t* bytes);
+
+
+/*
  * lse_merge -- LSE-corrected merge of n partial attention results.
  * Source: DCP page, DCP Decode compute pattern steps 4-7: gather the partial LSEs,
  * global_lse = log sum_s exp(lse_s), weight_s = exp(lse_s - global_lse), output =

@@ -487,3 +487,72 @@ def test_prefill_rejects_bad_chunk(dev):
         ca.segmented_attention_partial(q, kc, kc, kcache, vcache, bt, 0, 0, 2, 16)   # 48 % 32 != 0
     with pytest.raises(ca.CtxAttnError, match="exceeds"):
         ca.segmented_attention_partial(q, kc, kc, kcache, vcache, bt, 17, 0, 2, 8)
+
+
+# ---------------------------------------------------------------- sink-robust const-max
+
+def _sink_ring_inputs(dev, sinks, seed=21):
+    """Wan2.2-style QK-normed heads at a small length (cp = 4, 200 tokens per rank) with
+    ``sinks`` = [(global token, head, factor)] keys scaled up by factor."""
+    wl = workloads.workload("wan22_cp8_online").scaled(S=4 * 200, cp=4, H=2, seed=seed)
+    t = gen.ring_inputs(wl, dev)
+    k = t["k"].clone()
+    for tok, h, f in sinks:
+        k[0, tok, h] = (k[0, tok, h].float() * f).to(k.dtype)
+    return t["q"], k, t["v"]
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+def test_const_max_sinks_match_exact_attention(dev, rank):
+    """Three planted sinks (60-90x the typical key norm, two heads, three chunks): the plain
+    bound collapses rows, the sink-robust pass matches exact attention, and its sink lists are
+    the oracle's."""
+    ca = _ca()
+    sinks = [(5, 0, 60.0), (333, 0, 90.0), (610, 1, 75.0)]
+    q, k, v = _sink_ring_inputs(dev, sinks)
+    say(f"sink-robust const-max rank={rank} sinks={sinks}")
+    scale = oracle.default_scale(128)
+    qs = ca.ring.shard(q, 4, rank, "contiguous")
+    ref_o, ref_l = oracle.attention_heads(qs, k, v, scale)
+    kp = ca.ring.chunk_pool(k, 4, "contiguous")
+    vp = ca.ring.chunk_pool(v, 4, "contiguous")
+    rp = ca.ring.RingPass(qs, kp, vp, rank, variant="constmax", sink_theta=4.0)
+    o, l = rp.run()
+    torch.cuda.synchronize()
+    check("sink-robust vs exact", o[0], l[0], ref_o[0], ref_l[0])
+    for h in range(2):
+        masks = oracle.key_sinks([kp[c, 0, :, h] for c in range(4)], 4.0, 32)
+        want = sorted(c * 200 + int(j) for c in range(4) for j in np.nonzero(masks[c])[0])
+        n = int(rp.sinks["sink_cnt"][0, h])
+        assert sorted(rp.sinks["sink_idx"][0, h, :n].tolist()) == want, (h, want)
+    plain = ca.ring.RingPass(qs, kp, vp, rank, variant="constmax")
+    po, pl = plain.run()
+    torch.cuda.synchronize()
+    assert max_err(pl[0], ref_l[0]) > 1.0      # the plain bound collapses some rows here
+
+
+def test_const_max_sinks_without_sinks_is_plain(dev):
+    ca = _ca()
+    q, k, v = _sink_ring_inputs(dev, [])
+    qs = ca.ring.shard(q, 4, 1, "contiguous")
+    kp = ca.ring.chunk_pool(k, 4, "contiguous")
+    vp = ca.ring.chunk_pool(v, 4, "contiguous")
+    rp = ca.ring.RingPass(qs, kp, vp, 1, variant="constmax", sink_theta=4.0)
+    o, l = rp.run()
+    po, pl = ca.ring.RingPass(qs, kp, vp, 1, variant="constmax").run()
+    torch.cuda.synchronize()
+    assert int(rp.sinks["sink_cnt"].sum()) == 0
+    assert torch.equal(rp.sinks["kmax_sq_robust"], rp.sinks["kmax_sq"])
+    assert max_err(o, to_np(po)) <= 1e-5 and max_err(l, to_np(pl)) <= 1e-5
+
+
+def test_const_max_sinks_over_cap_keeps_the_plain_bound(dev):
+    ca = _ca()
+    q, k, v = _sink_ring_inputs(dev, [(5, 0, 60.0), (333, 0, 90.0), (610, 0, 75.0)])
+    kp = ca.ring.chunk_pool(k, 4, "contiguous")
+    s = ca.const_max_sink_prologue(kp, 4.0, sink_cap=2)
+    torch.cuda.synchronize()
+    assert int(s["sink_cnt"][0, 0]) == 0 and torch.equal(s["kmax_sq_robust"][0, 0], s["kmax_sq"][0, 0])
+    s = ca.const_max_sink_prologue(kp, 4.0, sink_cap=3)
+    torch.cuda.synchronize()
+    assert sorted(s["sink_idx"][0, 0, :int(s["sink_cnt"][0, 0])].tolist()) == [5, 333, 610]
