@@ -193,7 +193,17 @@ def run_constmax(args, torch, ca, workloads, gen, dev):
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
     del t
     out = {}
-    for variant in ("constmax", "online"):
+    for variant in ("constmax", "constmax_sinks", "online"):
+        if variant == "constmax_sinks":
+            # sink-robust pass (theta 4): on these QK-normed keys no key qualifies, so this
+            # measures what the sink prologue, the per-tile sink test and the sink merge cost
+            rp = ca.ring.RingPass(q, kp, vp, 0, variant="constmax", sink_theta=4.0)
+            ms, _ = time_ring(rp, max(2, args.steps // 4), 1, torch)
+            fl = ring_flops(wl.H, wl.local_S, wl.S, wl.D)
+            out[variant] = {"ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                            "sinks_found": int(rp.sinks["sink_cnt"].sum().item())}
+            del rp
+            continue
         rp = ca.ring.RingPass(q, kp, vp, 0, variant=variant)
         union = []
         ms, per_step = time_ring(rp, max(2, args.steps // 4), 1, torch, union)
