@@ -110,6 +110,14 @@ __device__ __forceinline__ void phase_end() {
 #define MATRIX_PRIO_OFF
 #endif
 
+// End of a matrix phase: this wave's LDS reads have returned (the buffers they read may be
+// refilled two phases later), then the workgroup barrier.
+__device__ __forceinline__ void reads_end_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Plain workgroup barrier between phases (no wait for copies).
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -524,22 +532,22 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     // the start of the phase; the eight PV MFMAs cover the read latency. The group barriers
     // pin that order: K reads, PV MFMAs, QK MFMAs.
     auto matrix_phase = [&](auto bufc, bool do_qk, bool do_pv) {
-      constexpr int BUF = decltype(bufc)::value;
       if (do_qk) read_k(bufc);
       if (do_pv) {
 #pragma unroll
         for (int c = 0; c < 8; ++c)
           o[c & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[(c & 3) * 2 + (c >> 2)], p[c >> 2], o[c & 3], 0, 0, 0);
       }
+      if (do_qk) read_v(bufc);   // the next tile's V: its registers are free once P.V has issued
       if (do_qk) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], q[0], floatx16{}, 0, 0, 0);
 #pragma unroll
         for (int c = 1; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
       }
-      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 K fragment reads
-      if (do_pv) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // PV
-      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // QK
-      (void)BUF;
+      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // the 8 K fragment reads
+      if (do_pv) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // P.V
+      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // the 16 V fragment reads
+      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // Q.K
     };
     // Softmax of the segment's tile j (scores in s): probabilities into p, row sum into l_part.
     auto softmax = [&](int j) {
@@ -555,11 +563,13 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       exp_pack(s, sl2e, mu, p, l_part);
     };
     // One tile j of the segment (buffer BUF = j % NBUF), in two phases.
-    //  vector phase: read V of tile j, start the copies of tile j + NBUF - 1 into the buffer
-    //    tile j - 1 used, softmax of tile j; ends once this wave's copies of tile j + 2 have
-    //    landed, then the workgroup barrier;
-    //  matrix phase: read K of tile j + 1, output update of tile j, scores of tile j + 1;
-    //    then the barrier.
+    //  vector phase: start the copies of tile j + NBUF - 1 into the buffer tile j - 1 used,
+    //    softmax of tile j; ends once this wave's copies of tile j + 2 have landed, then the
+    //    workgroup barrier;
+    //  matrix phase: read K of tile j + 1, output update of tile j, read V of tile j + 1,
+    //    scores of tile j + 1; ends once its LDS reads have returned, then the barrier.
+    //  All LDS reads of a SIMD pair thus come from the wave in its matrix phase, under its
+    //  MFMAs, and none from the wave running the softmax.
     // The body is the same for every tile: past the segment's last tile the copies repeat
     // that tile into free buffers and the scores of the nonexistent tile are never used,
     // so the copy count in flight, the waits and the MFMA sequence never change.
@@ -568,7 +578,6 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       constexpr int NEXT = (BUF + 1) % NBUF;
       constexpr int FREE = (BUF + NBUF - 1) % NBUF;
       VECTOR_PRIO_ON;
-      read_v(bufc);
       issue(std::integral_constant<int, FREE>{}, min(j + NBUF - 1, nk - 1));
       softmax(j);
       VECTOR_PRIO_OFF;
@@ -576,7 +585,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       MATRIX_PRIO_ON;
       matrix_phase(std::integral_constant<int, NEXT>{}, true, true);
       MATRIX_PRIO_OFF;
-      phase_barrier();
+      reads_end_barrier();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -595,8 +604,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       issue(I4{}, min(4, nk - 1));
       phase_end<NBUF - 3>();
       if (lagging) phase_barrier();
-      matrix_phase(I0{}, true, false);   // scores of tile 0
-      phase_barrier();
+      matrix_phase(I0{}, true, false);   // scores and V fragments of tile 0
+      reads_end_barrier();
       for (int j = 0;; j += NBUF) {
         tile(I0{}, j);
         if (j + 1 >= nk) break;
