@@ -528,9 +528,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       }
     };
     // Matrix phase: the output update with the V fragments and probabilities of the last
-    // vector phase (PV), then the scores of the next tile (QK). Its K fragments are read at
-    // the start of the phase; the eight PV MFMAs cover the read latency. The group barriers
-    // pin that order: K reads, PV MFMAs, QK MFMAs.
+    // vector phase (PV), then the scores of the next tile (QK). The LDS reads are spread
+    // between the MFMAs, one K fragment read after each PV MFMA and two V fragment reads
+    // after each QK MFMA: issued in bursts they fill the CU's LDS command queue, and a wave
+    // waiting to issue a read cannot issue its next MFMA either.
     auto matrix_phase = [&](auto bufc, bool do_qk, bool do_pv) {
       if (do_qk) read_k(bufc);
       if (do_pv) {
@@ -544,10 +545,22 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
 #pragma unroll
         for (int c = 1; c < 8; ++c) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], q[c], s, 0, 0, 0);
       }
-      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // the 8 K fragment reads
-      if (do_pv) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // P.V
-      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // the 16 V fragment reads
-      if (do_qk) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);    // Q.K
+      if (do_pv) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {   // P.V MFMA, K fragment read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {   // Q.K MFMA, two V fragment reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      } else {                          // prologue: K reads, Q.K, V reads
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      }
     };
     // Softmax of the segment's tile j (scores in s): probabilities into p, row sum into l_part.
     auto softmax = [&](int j) {
