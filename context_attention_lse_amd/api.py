@@ -79,10 +79,13 @@ def _ws(workspace):
     return _ptr(workspace), workspace.numel()
 
 
-def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspace=None, stream=None):
+def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspace=None, stream=None,
+                   fold=False):
     """Online-max attention of q [B, Sq, H, D] against one K/V chunk [B, Sk, H, D].
     Returns (o [B, H, Sq, D] fp32, lse [B, H, Sq] fp32). With ``workspace`` (from
-    step_workspace) the key range is split over a grid that fills the device."""
+    step_workspace) the key range is split over a grid that fills the device. With
+    ``fold``, ``out`` and ``lse`` (required) hold a prior partial of the same rows and
+    receive its LSE merge with this chunk's partial (ring_attn_step_fold)."""
     _check_cuda(q, k, v, out, lse, workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
@@ -92,11 +95,18 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspa
         raise ValueError("k and v must share strides")
     if q.dtype != k.dtype or k.dtype != v.dtype:
         raise TypeError("q, k and v must share a dtype")
+    if fold:
+        if out is None or lse is None:
+            raise ValueError("fold needs the prior partial in out and lse")
+        if out.shape != (B, H, Sq, D) or lse.shape != (B, H, Sq) or out.dtype != torch.float32 \
+                or lse.dtype != torch.float32 or not (out.is_contiguous() and lse.is_contiguous()):
+            raise ValueError("fold: out [B, H, Sq, D] and lse [B, H, Sq] must be contiguous fp32")
     if out is None:
         out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    _lib.call("ring_attn_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
+    _lib.call("ring_attn_step_fold" if fold else "ring_attn_step", _ptr(q), _strides(q), _ptr(k), _ptr(v),
+              _strides(k), _dtype_code(q),
               B, H, Sq, Sk, D, _scale(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
               _ptr(out), _ptr(lse), *_ws(workspace), _stream(stream))
     return out, lse

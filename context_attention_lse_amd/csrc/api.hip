@@ -96,9 +96,10 @@ const char* ca_last_error(void) { return g_err; }
 
 const char* ca_version(void) { return "0.1.0"; }
 
-ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype, int B,
-                         int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides qs, const void* k, const void* v,
+                                     ca_strides kvs, int dtype, int B, int H, int Sq, int Sk, int D,
+                                     float softmax_scale, int mask, float* o, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream, int fold) {
   CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
   if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
   if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
@@ -113,10 +114,25 @@ ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void
   a.mask = mask;
   a.G = 1;
   a.o = o; a.lse = lse;
+  a.fold = fold;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
-  return hip_status(e, "ring_attn_step launch");
+  return hip_status(e, name);
+}
+
+ca_status ring_attn_step(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype, int B,
+                         int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return ring_attn_step_impl("ring_attn_step launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale, mask,
+                             o, lse, workspace, workspace_bytes, stream, 0);
+}
+
+ca_status ring_attn_step_fold(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype,
+                              int B, int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return ring_attn_step_impl("ring_attn_step_fold launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale,
+                             mask, o, lse, workspace, workspace_bytes, stream, 1);
 }
 
 ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask, size_t* bytes) {

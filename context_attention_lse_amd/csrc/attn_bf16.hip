@@ -248,14 +248,33 @@ __device__ __forceinline__ void store_rows(const AttnArgs& a, int64_t bh, int Sq
   // o[db][r] is O[row][d] for d = 32*db + 8*(r/4) + 4*hl + r%4: four consecutive d per float4.
   if (MODE == MODE_ONLINE) {
     const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
+    const float lse_t = lrow > 0.0f ? (m_ref + __log2f(lrow)) * kLn2 : -INFINITY;
     float* orow = a.o + rowidx * D;
+    if (a.fold) {
+      // merge with the prior partial in o / lse (both lanes of the row read it before either
+      // writes: they are lanes l and l + 32 of one wave)
+      float w_p, w_t;
+      const float L = lse_fold_weights(a.lse[rowidx], lse_t, w_p, w_t);
+      const float wt = w_t * inv;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float4* dst = reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * hl);
+          const float4 pr = *dst;
+          *dst = make_float4(w_p * pr.x + wt * o[db][4 * g], w_p * pr.y + wt * o[db][4 * g + 1],
+                             w_p * pr.z + wt * o[db][4 * g + 2], w_p * pr.w + wt * o[db][4 * g + 3]);
+        }
+      if (hl == 0) a.lse[rowidx] = L;
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4*>(orow + db * 32 + 8 * g + 4 * hl) =
             make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-    if (hl == 0) a.lse[rowidx] = lrow > 0.0f ? (m_ref + __log2f(lrow)) * kLn2 : -INFINITY;
+    if (hl == 0) a.lse[rowidx] = lse_t;
   } else {
     const int64_t rows = int64_t(a.B) * a.H * Sq;
     float sum = lrow;

@@ -103,10 +103,22 @@ __global__ __launch_bounds__(NT) void attn_step_f32(const AttnArgs a, int nqb) {
   const int64_t rowidx = int64_t(bh) * Sq + i;
   if (MODE == MODE_ONLINE) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lse_t = l > 0.0f ? m + logf(l) : -INFINITY;
     float* orow = a.o + rowidx * D + half * DH;
+    if (a.fold) {
+      // merge with the prior partial in o / lse (the row's two threads are adjacent lanes of
+      // one wave: both read the prior LSE before either writes)
+      float w_p, w_t;
+      const float L = lse_fold_weights(a.lse[rowidx], lse_t, w_p, w_t);
+      const float wt = w_t * inv;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) orow[d] = acc[d] * inv;
-    if (half == 0) a.lse[rowidx] = l > 0.0f ? m + logf(l) : -INFINITY;
+      for (int d = 0; d < DH; ++d) orow[d] = w_p * orow[d] + wt * acc[d];
+      if (half == 0) a.lse[rowidx] = L;
+    } else {
+#pragma unroll
+      for (int d = 0; d < DH; ++d) orow[d] = acc[d] * inv;
+      if (half == 0) a.lse[rowidx] = lse_t;
+    }
   } else {
     const int64_t rows = int64_t(a.B) * a.H * Sq;
     float* arow = a.acc ? a.acc + rowidx * D + half * DH : nullptr;

@@ -54,6 +54,23 @@ __device__ __forceinline__ int xcd_logical_id(int wg, int grid, int nwork) {
 __host__ __device__ inline int round_up8(int n) { return (n + 7) & ~7; }
 
 // ---------------------------------------------------------------- launch descriptors
+// Two-way LSE merge of a prior partial (lse_p) with a new one (lse_t), natural-log LSEs:
+// M = max, L = M + log(e^(lse_p - M) + e^(lse_t - M)), weights e^(lse - L) ("Sharding the
+// Input": ring attention's per-block rescale; the DCP merge of partial outputs by their LSE).
+// Both empty (-inf): weights 0 and L = -inf, so the merged row is O = 0, LSE = -inf.
+__device__ __forceinline__ float lse_fold_weights(float lse_p, float lse_t, float& w_p, float& w_t) {
+  const float M = fmaxf(lse_p, lse_t);
+  if (M == -INFINITY) {
+    w_p = 0.0f;
+    w_t = 0.0f;
+    return -INFINITY;
+  }
+  const float L = M + logf(expf(lse_p - M) + expf(lse_t - M));
+  w_p = expf(lse_p - L);
+  w_t = expf(lse_t - L);
+  return L;
+}
+
 struct AttnArgs {
   const void* q;
   int64_t qsb, qss, qsh;
@@ -64,9 +81,11 @@ struct AttnArgs {
   float scale;      // softmax scale
   float sl2e;       // scale * log2(e)
   int mask;         // ca_mask
-  // online-max outputs
+  // online-max outputs; fold != 0: o and lse hold a prior partial on entry and are
+  // replaced by its LSE merge with this chunk's partial
   float* o;
   float* lse;
+  int fold;
   // const-max inputs/outputs
   const float* c;
   float* acc;

@@ -71,7 +71,10 @@ class RingPass:
     """One rank's share of ring attention: q resident, cp chunks arriving one per step.
 
     variant "online": every step emits a partial (o_s, lse_s) with ring_attn_step and
-                      the partials are merged once with lse_merge;
+                      the partials are merged once with lse_merge; with fold=True each
+                      step instead merges its partial in place into its compute stream's
+                      running partial (ring_attn_step_fold), and the streams' running
+                      partials (one or two) are merged at the end;
     variant "constmax" with sink_theta: keys whose norm exceeds sink_theta x the mean key
                       norm (at most sink_cap per head) leave the bound and the fold, and are
                       attended exactly in a second partial merged by LSE;
@@ -89,9 +92,11 @@ class RingPass:
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
                  scale=None, prefetch_depth=2, out_dtype=torch.float32, copy_stream=None,
-                 compute_streams=None, split=False, sink_theta=None, sink_cap=32):
+                 compute_streams=None, split=False, sink_theta=None, sink_cap=32, fold=False):
         if variant not in ("online", "constmax"):
             raise ValueError(f"unknown variant {variant!r}")
+        if fold and variant != "online":
+            raise ValueError("fold applies to the online variant")
         if variant == "constmax" and causal:
             raise ValueError("the const-max method is non-causal")
         if layout not in LAYOUTS:
@@ -132,8 +137,11 @@ class RingPass:
             self.ws += [self.ws[0]] * (2 - len(self.ws))
         self.live_steps = [s for s in range(self.cp) if self.masks[s] is not None]
         assert self.live_steps, "a rank always sees its own chunk"
+        self.fold = bool(fold)
+        # one compute stream folding into an fp32 output needs no final merge
+        self.fold_direct = self.fold and compute_streams == 1 and out_dtype == torch.float32
         if variant == "online":
-            n = len(self.live_steps)
+            n = compute_streams if self.fold else len(self.live_steps)
             self.o_parts = torch.empty((max(n, 1), B, H, Sq, D), dtype=torch.float32, device=dev)
             self.lse_parts = torch.empty((max(n, 1), B, H, Sq), dtype=torch.float32, device=dev)
         else:
@@ -202,6 +210,7 @@ class RingPass:
         for t in range(1, min(self.depth, cp - 1) + 1):
             self._issue_copy(t)
         slot = 0
+        started = [False, False]   # fold: running partial of each compute stream begun
         for s in range(cp):
             t = s + self.depth
             if s >= 1 and t < cp:
@@ -218,7 +227,14 @@ class RingPass:
                 if timing_events is not None:
                     timing_events[s][0].record(st)
                 if self.variant == "online":
-                    if self.masks[s] is not None:
+                    if self.masks[s] is not None and self.fold:
+                        a = 1 if second else 0
+                        o_dst, l_dst = ((self.out, self.lse) if self.fold_direct
+                                        else (self.o_parts[a], self.lse_parts[a]))
+                        api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s], out=o_dst,
+                                           lse=l_dst, workspace=ws, fold=started[a])
+                        started[a] = True
+                    elif self.masks[s] is not None:
                         api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s],
                                            out=self.o_parts[slot], lse=self.lse_parts[slot], workspace=ws)
                         slot += 1
@@ -237,7 +253,11 @@ class RingPass:
             self.consumed[s].record(st)
         if self.aux_stream is not None:
             cs.wait_stream(self.aux_stream)
-        if self.variant == "online":
+        if self.variant == "online" and self.fold:
+            if not self.fold_direct:
+                n = 2 if started[1] else 1   # stream 0 always runs step 0, the rank's own chunk
+                api.lse_merge(self.o_parts[:n], self.lse_parts[:n], out=self.out, lse_out=self.lse)
+        elif self.variant == "online":
             api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
         elif self.sink_theta is not None:
             api.sink_attention_partial(self.q, self.k_pool, self.v_pool, self.sinks, scale=self.scale,
@@ -249,12 +269,12 @@ class RingPass:
 
 
 def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous", causal=False,
-                   variant="online", scale=None, prefetch_depth=2, split=False):
+                   variant="online", scale=None, prefetch_depth=2, split=False, fold=False, compute_streams=None):
     """Convenience: rank ``rank``'s output for global [B, S, H, D] inputs."""
     check_divisible(q_global.shape[1], cp)
     q = shard(q_global, cp, rank, layout)
     kp = chunk_pool(k_global, cp, layout)
     vp = chunk_pool(v_global, cp, layout)
     rp = RingPass(q, kp, vp, rank, layout=layout, causal=causal, variant=variant, scale=scale,
-                  prefetch_depth=prefetch_depth, split=split)
+                  prefetch_depth=prefetch_depth, split=split, fold=fold, compute_streams=compute_streams)
     return rp.run()

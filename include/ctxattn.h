@@ -91,8 +91,8 @@ typedef struct {
  *   lse    OUT [B, H, Sq] fp32, contiguous: log sum_j exp(scale * q_i . k_j)
  *   workspace, workspace_bytes
  *          optional device scratch (see ring_attn_workspace_size). NULL: one workgroup
- *          per 128 query rows. Given, and the call is one that one workgroup per 128 rows
- *          would leave the device's workgroup slots more than a tenth idle: the call's
+ *          per 256 query rows (bf16). Given, and the call is one that one workgroup per
+ *          256 rows would leave the device's workgroup slots more than a tenth idle: the call's
  *          (query tile, key tile) iterations are cut into equal ranges, one per workgroup
  *          the device holds at once, and query tiles split between ranges are combined in
  *          the library, in key order (results do not depend on timing). The workspace must
@@ -109,6 +109,30 @@ ca_status ring_attn_step(const void* q, ca_strides q_strides,
                          float softmax_scale, int mask,
                          float* o, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ring_attn_step_fold -- ring_attn_step whose partial is merged in place into a prior
+ * one: the incremental form of the LSE merge of per-chunk partials. The rows of o and
+ * lse hold a partial (O_p, lse_p) of the same queries on entry (e.g. an earlier chunk's
+ * ring_attn_step output); on return they hold its merge with this chunk's (O_t, lse_t):
+ * M = max(lse_p, lse_t), L = M + log(e^(lse_p - M) + e^(lse_t - M)),
+ * O = e^(lse_p - L) O_p + e^(lse_t - L) O_t, lse = L; a row empty on both sides stays
+ * O = 0, lse = -inf. Folding the chunks of a ring one after another gives the n-way
+ * lse_merge of their partials up to rounding.
+ * Source: "Sharding the Input" (ring attention: each block's result rescaled by the
+ * running log-sum-exp and combined), and the DCP page's merge of partial outputs by
+ * their LSE.
+ *
+ * Arguments, layouts, support and errors: as ring_attn_step, with o and lse IN/OUT
+ * (contiguous fp32; lse_p may be -inf). A call reads each row of o and lse once and
+ * writes it once; calls into the same o / lse must not overlap in time.
+ */
+ca_status ring_attn_step_fold(const void* q, ca_strides q_strides,
+                              const void* k, const void* v, ca_strides kv_strides,
+                              int dtype, int B, int H, int Sq, int Sk, int D,
+                              float softmax_scale, int mask,
+                              float* o, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * ring_attn_workspace_size -- bytes of step workspace that ring_attn_step and

@@ -90,6 +90,44 @@ def test_split_step_is_deterministic_and_leaves_workspace_ready(dev, mask):
     check("reused workspace", o3, l3, ro, rl)
 
 
+@pytest.mark.parametrize("dtype,D,split", [("bf16", 128, False), ("bf16", 128, True), ("fp32", 64, False)])
+@pytest.mark.parametrize("m1,m2,Sq,Sk1,Sk2", [("none", "none", 300, 200, 333), ("causal_strict", "causal_strict", 260, 260, 260),
+                                              ("causal_incl", "none", 300, 300, 1), ("none", "causal_strict", 129, 0, 129)])
+def test_step_fold_matches_attention_over_both_chunks(dev, dtype, D, split, m1, m2, Sq, Sk1, Sk2):
+    """A partial over chunk 1, then chunk 2 folded into it in place: attention over both
+    chunks' keys (each under its own mask). Covers rows empty on one side and on both sides
+    (causal_strict twice: row 0 stays O = 0, LSE = -inf) and an empty first chunk."""
+    ca = _ca()
+    B, H = 2, 3
+    say(f"fold dtype={dtype} D={D} split={split} m1={m1} m2={m2} Sq={Sq} Sk1={Sk1} Sk2={Sk2}")
+    q, _, _ = _inputs(dev, B, Sq, H, D, dtype, 300)
+    _, k1, v1 = _inputs(dev, B, Sk1, H, D, dtype, 400)
+    _, k2, v2 = _inputs(dev, B, Sk2, H, D, dtype, 500)
+    ws = ca.step_workspace(q, k2, m2) if split else None
+    o, l = ca.ring_attn_step(q, k1, v1, mask=m1, workspace=ca.step_workspace(q, k1, m1) if split else None)
+    o2, l2 = ca.ring_attn_step(q, k2, v2, mask=m2, out=o, lse=l, workspace=ws, fold=True)
+    torch.cuda.synchronize()
+    assert o2.data_ptr() == o.data_ptr() and l2.data_ptr() == l.data_ptr()
+    scale = oracle.default_scale(D)
+    a1 = _allowed(m1, Sq, Sk1)
+    a2 = _allowed(m2, Sq, Sk2)
+    a1 = np.ones((Sq, Sk1), bool) if a1 is None else a1
+    a2 = np.ones((Sq, Sk2), bool) if a2 is None else a2
+    k = torch.cat([k1, k2], dim=1)
+    v = torch.cat([v1, v2], dim=1)
+    ro, rl = oracle.attention_heads(q, k, v, scale, allowed=np.concatenate([a1, a2], axis=1))
+    check("fold", o, l, ro, rl)
+    if m1 == "causal_strict" and m2 == "causal_strict":
+        assert np.all(to_np(l)[:, :, 0] == -np.inf) and np.all(to_np(o)[:, :, 0] == 0)
+
+
+def test_step_fold_requires_prior(dev):
+    ca = _ca()
+    q, k, v = _inputs(dev, 1, 64, 2, 128, "bf16", 7)
+    with pytest.raises(ValueError):
+        ca.ring_attn_step(q, k, v, fold=True)
+
+
 def test_step_explicit_scale_and_empty_chunk(dev):
     ca = _ca()
     q, k, v = _inputs(dev, 1, 70, 2, 128, "bf16", 300)
@@ -232,7 +270,7 @@ def test_lse_merge_matches_oracle(dev):
 
 # ---------------------------------------------------------------- ring passes
 
-def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=None, split=False):
+def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=None, split=False, **kw):
     ca = _ca()
     wl = wl.scaled(S=S, **({"H": H} if H else {}))
     layout = layout or wl.layout
@@ -242,9 +280,9 @@ def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=
     S_all = np.arange(S)
     for r in ranks:
         say(f"ring {wl.name} S={S} cp={wl.cp} rank={r} variant={variant} layout={layout} causal={causal} "
-            f"depth={depth} split={split}")
+            f"depth={depth} split={split} {kw}")
         o, l = ca.ring.ring_attention(t["q"], t["k"], t["v"], wl.cp, r, layout=layout, causal=causal,
-                                      variant=variant, prefetch_depth=depth, split=split)
+                                      variant=variant, prefetch_depth=depth, split=split, **kw)
         torch.cuda.synchronize()
         rows = (oracle.contiguous_tokens if layout == "contiguous" else oracle.striped_tokens)(S, wl.cp, r)
         allowed = oracle.causal_allowed(rows, S_all) if causal else None
@@ -277,6 +315,16 @@ def test_striped_causal_ring_scaled_all_ranks(dev):
 def test_contiguous_causal_ring_scaled(dev):
     wl = workloads.workload("striped_causal_128k")
     _ring_case(dev, wl, 8 * 136, ranks=(0, 3, 7), variant="online", layout="contiguous", causal=True, H=2)
+
+
+@pytest.mark.parametrize("streams,split", [(1, False), (2, False), (1, True), (2, True)])
+@pytest.mark.parametrize("layout,causal", [("contiguous", False), ("striped", True), ("contiguous", True)])
+def test_ring_fold_matches_oracle(dev, streams, split, layout, causal):
+    """Steps folded in place (ring_attn_step_fold) per compute stream, then the streams'
+    running partials merged: the same result as merging every step's partial at the end."""
+    wl = workloads.workload("wan22_cp8_online")
+    _ring_case(dev, wl, 8 * 136, ranks=(0, 5), variant="online", layout=layout, causal=causal, H=2, split=split,
+               fold=True, compute_streams=streams)
 
 
 @pytest.mark.parametrize("depth", [2, 3])
