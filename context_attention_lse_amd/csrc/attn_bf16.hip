@@ -103,12 +103,6 @@ __device__ __forceinline__ void phase_end() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-#ifndef VECTOR_PRIO_ON
-#define VECTOR_PRIO_ON
-#define VECTOR_PRIO_OFF
-#define MATRIX_PRIO_ON
-#define MATRIX_PRIO_OFF
-#endif
 
 // End of a matrix phase: this wave's LDS reads have returned (the buffers they read may be
 // refilled two phases later), then the workgroup barrier.
@@ -609,14 +603,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       constexpr int BUF = decltype(bufc)::value;
       constexpr int NEXT = (BUF + 1) % NBUF;
       constexpr int FREE = (BUF + NBUF - 1) % NBUF;
-      VECTOR_PRIO_ON;
       issue(std::integral_constant<int, FREE>{}, min(j + NBUF - 1, nk - 1));
       softmax(j);
-      VECTOR_PRIO_OFF;
       phase_end<NBUF - 3>();
-      MATRIX_PRIO_ON;
       matrix_phase(std::integral_constant<int, NEXT>{}, true, true);
-      MATRIX_PRIO_OFF;
       reads_end_barrier();
     };
     using I0 = std::integral_constant<int, 0>;
