@@ -5,6 +5,8 @@
 //                  into [B, H] (the ring's all_reduce(max) becomes this fold on one GPU);
 //  const_max_bound: c_i = sqrt(scale^2 * kmax_sq * |q_i|^2) per query row.
 // Both read their input once with 16-byte loads, several rows in flight per lane group.
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace ctxattn {
@@ -73,11 +75,13 @@ __global__ void fill_kernel(float* p, int n, float v) {
   if (i < n) p[i] = v;
 }
 
-// grid: (ceil(S / KTOK), B); a workgroup takes KTOK tokens of every head. Per-head maxima
-// gather in LDS, then one global atomicMax per head per block. Squared norms are
-// non-negative floats, whose bit patterns order like ints, so the max is exact and
-// independent of arrival order.
-constexpr int KTOK = 32;   // tokens (of every head) per key-norm workgroup
+// grid: (G, B) with G at most a few workgroups per CU; workgroup x takes the tiles of KTOK
+// tokens (of every head) x, x + G, ... Per-head maxima gather in LDS, then one global
+// atomicMax per head per workgroup. Squared norms are non-negative floats, whose bit
+// patterns order like ints, so the max is exact and independent of arrival order. The
+// stride keeps every workgroup busy to the end (one tile per workgroup left a partly filled
+// second round of workgroups for long key runs).
+constexpr int KTOK = 32;   // tokens (of every head) per key-norm tile
 
 template <bool BF16>
 __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64_t sb, int64_t ss, int64_t sh,
@@ -88,23 +92,24 @@ __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64
   __syncthreads();
   const int grp = threadIdx.x >> 4;
   const int lane16 = threadIdx.x & 15;
-  const int t0 = blockIdx.x * KTOK;
-  const int rows = min(KTOK, S - t0) * H;   // this workgroup's (token, head) rows, token major
-  for (int r0 = 0; r0 < rows; r0 += GROUPS * RIF) {
-    RowPiece<BF16> r[RIF];
+  for (int t0 = blockIdx.x * KTOK; t0 < S; t0 += gridDim.x * KTOK) {
+    const int rows = min(KTOK, S - t0) * H;   // this tile's (token, head) rows, token major
+    for (int r0 = 0; r0 < rows; r0 += GROUPS * RIF) {
+      RowPiece<BF16> r[RIF];
 #pragma unroll
-    for (int u = 0; u < RIF; ++u) {
-      const int p = r0 + u * GROUPS + grp;
-      const int pc = p < rows ? p : 0;
-      const int i = pc / H, h = pc - i * H;
-      r[u] = load_piece<BF16>(k, b * sb + int64_t(t0 + i) * ss + int64_t(h) * sh, lane16, D);
-    }
+      for (int u = 0; u < RIF; ++u) {
+        const int p = r0 + u * GROUPS + grp;
+        const int pc = p < rows ? p : 0;
+        const int i = pc / H, h = pc - i * H;
+        r[u] = load_piece<BF16>(k, b * sb + int64_t(t0 + i) * ss + int64_t(h) * sh, lane16, D);
+      }
 #pragma unroll
-    for (int u = 0; u < RIF; ++u) {
-      const int p = r0 + u * GROUPS + grp;
-      // p is uniform over the 16 lanes of a group, so the reduction runs with all 16 active
-      const float v = group16_sum(piece_sqnorm<BF16>(r[u]));
-      if (p < rows && lane16 == 0) atomicMax(&smax[p - (p / H) * H], __float_as_int(v));
+      for (int u = 0; u < RIF; ++u) {
+        const int p = r0 + u * GROUPS + grp;
+        // p is uniform over the 16 lanes of a group, so the reduction runs with all 16 active
+        const float v = group16_sum(piece_sqnorm<BF16>(r[u]));
+        if (p < rows && lane16 == 0) atomicMax(&smax[p - (p / H) * H], __float_as_int(v));
+      }
     }
   }
   __syncthreads();
@@ -168,7 +173,13 @@ hipError_t launch_key_sqnorm_max(const void* k, int64_t sb, int64_t ss, int64_t 
     if (e != hipSuccess) return e;
   }
   if (S == 0 || B == 0) return hipSuccess;
-  dim3 grid(unsigned((S + KTOK - 1) / KTOK), B);
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t tiles = (int64_t(S) + KTOK - 1) / KTOK;
+  const int64_t per_b = std::max<int64_t>(1, (int64_t(4) * cus + B - 1) / B);   // about 4 workgroups per CU
+  dim3 grid(unsigned(std::min(tiles, per_b)), B);
   const size_t lds = size_t(H) * sizeof(int);
   if (bf16)
     hipLaunchKernelGGL((key_sqnorm_max_kernel<true>), grid, dim3(NT), lds, s, k, sb, ss, sh, S, H, D, kmax_sq);
