@@ -2,8 +2,9 @@
 benchmark times (RingPass / DcpDecode with their defaults), on sampled output rows that the
 oracle computes one by one against the full key range.
 
-Rows are sampled per head with a fixed seed and always include the first rows, the ragged
-last 128-row tile and the last row; every sampled row is checked element by element."""
+Rows are sampled per head with a fixed seed and always include the first rows, both sides of
+the 256-row query-tile edges, the ragged last tile and the last row; every sampled row is
+checked element by element."""
 
 import numpy as np
 import pytest
@@ -27,21 +28,21 @@ def ca():
 
 
 def _rows(n, seed, k=24):
-    last_tile = (n - 1) // 128 * 128
-    return gen.sample_rows(n, k, seed, include=(0, 1, 127, 128, last_tile, n - 2, n - 1))
+    last_tile = (n - 1) // 256 * 256
+    return gen.sample_rows(n, k, seed, include=(0, 1, 255, 256, last_tile - 1, last_tile, n - 2, n - 1))
 
 
-def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q):
+def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q, **ring_kw):
     wl = workloads.workload(name)
     dev = torch.device("cuda:0")
-    say(f"full-size {name} variant={variant} rank={rank} S={wl.S} cp={wl.cp} H={wl.H}")
+    say(f"full-size {name} variant={variant} rank={rank} S={wl.S} cp={wl.cp} H={wl.H} {ring_kw}")
     t = gen.ring_inputs(wl, dev)
     q = ca.ring.shard(t["q"], wl.cp, rank, wl.layout)
     if contiguous_q:
         q = q.contiguous()
     kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
-    rp = ca.ring.RingPass(q, kp, vp, rank, layout=wl.layout, causal=wl.causal, variant=variant)
+    rp = ca.ring.RingPass(q, kp, vp, rank, layout=wl.layout, causal=wl.causal, variant=variant, **ring_kw)
     o, lse = rp.run()
     torch.cuda.synchronize()
     tok = (oracle.contiguous_tokens if wl.layout == "contiguous" else oracle.striped_tokens)(wl.S, wl.cp, rank)
@@ -59,7 +60,19 @@ def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q):
 
 
 def test_wan22_cp8_online_fullsize(ca):
-    _ring_fullsize(ca, "wan22_cp8_online", "online", 0, heads=(0, 4, 9), contiguous_q=False)
+    # the headline's launch configuration: key-split steps alternating two compute streams
+    _ring_fullsize(ca, "wan22_cp8_online", "online", 0, heads=(0, 4, 9), contiguous_q=False, split=True,
+                   compute_streams=2)
+
+
+def test_wan22_cp8_online_fullsize_unsplit(ca):
+    _ring_fullsize(ca, "wan22_cp8_online", "online", 5, heads=(2, 7), contiguous_q=False)
+
+
+def test_wan22_720p_constmax_sinks_fullsize(ca):
+    """The sink-robust pass as timed (theta 4): exact attention is the target whether or not
+    any key qualifies as a sink."""
+    _ring_fullsize(ca, "wan22_720p_constmax", "constmax", 0, heads=(0, 39), contiguous_q=True, sink_theta=4.0)
 
 
 @pytest.mark.parametrize("variant", ["constmax", "online"])
@@ -94,4 +107,60 @@ def test_dcp_decode_fullsize(ca):
         fo, fl = oracle.decode_full(d["q"][b].cpu(), kb, vb, scale)
         check(f"seq {b} (ctx {s1 - s0}) merged", o[b], lse[b], fo, fl)
     del d, shards, run
+    torch.cuda.empty_cache()
+
+
+def test_dcp_decode_active_fullsize(ca):
+    """The decode leg with a current token, as timed: N resident tokens per sequence on the
+    shards plus the new token at position N on its owner shard; the merged result against
+    attention over all N + 1 tokens."""
+    wl = workloads.workload("dcp_decode_gqa")
+    dev = torch.device("cuda:0")
+    say(f"full-size {wl.name} with current token")
+    d = gen.decode_inputs(wl, dev)
+    shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], d["ctx"], r, wl.shards,
+                                       wl.interleave, wl.block_size, d["block_rand"]) for r in range(wl.shards)]
+    run = ca.dcp.DcpDecode(d["q"], shards)
+    prior = torch.tensor([int(n) for n in d["ctx"]], dtype=torch.int32, device=dev)
+    k_cur = gen.normal((wl.B, wl.Hkv, wl.D), 1000 * wl.seed + 21, dev, torch.bfloat16)
+    v_cur = gen.normal((wl.B, wl.Hkv, wl.D), 1000 * wl.seed + 22, dev, torch.bfloat16)
+    o, lse = run.run_active(prior, k_cur, v_cur, wl.interleave)
+    torch.cuda.synchronize()
+    ctx = d["ctx"]
+    scale = oracle.default_scale(wl.D)
+    for b in sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 5}):
+        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
+        kb = torch.cat([d["k_seq"][s0:s1], k_cur[b:b + 1]]).cpu()
+        vb = torch.cat([d["v_seq"][s0:s1], v_cur[b:b + 1]]).cpu()
+        fo, fl = oracle.decode_full(d["q"][b].cpu(), kb, vb, scale)
+        check(f"seq {b} (ctx {s1 - s0} + current) merged", o[b], lse[b], fo, fl)
+    del d, shards, run
+    torch.cuda.empty_cache()
+
+
+def test_dcp_prefill_fullsize(ca):
+    """The prefill leg as timed: 8192 new tokens after 65536 prior ones, 32 query heads over 8
+    KV heads, DCP 2 interleaving blocks of 16. Sampled chunk rows against attention over the
+    prior tokens and the chunk's tokens up to the row."""
+    S, P, Hq, Hkv, D, W, I = 8192, 65536, 32, 8, 128, 2, 16
+    dev = torch.device("cuda:0")
+    say(f"full-size dcp prefill S={S} after {P}")
+    q = gen.normal((1, S, Hq, D), 901, dev, torch.bfloat16)
+    k_all = gen.normal((P + S, Hkv, D), 902, dev, torch.bfloat16)
+    v_all = gen.normal((P + S, Hkv, D), 903, dev, torch.bfloat16)
+    caches = [ca.dcp.build_shard_cache(k_all, v_all, np.array([0, P]), np.array([P]), r, W, I, 16) for r in range(W)]
+    run = ca.dcp.DcpPrefill(q, k_all[P:].unsqueeze(0), v_all[P:].unsqueeze(0), caches, P, I)
+    o, lse = run.run()
+    torch.cuda.synchronize()
+    scale = oracle.default_scale(D)
+    kh_all = oracle.to_f64(k_all.cpu())
+    vh_all = oracle.to_f64(v_all.cpu())
+    for h in (0, 13, 31):
+        rows = _rows(S, 31 * h)
+        hk = h // (Hq // Hkv)
+        qh = oracle.to_f64(q[0, rows, h].cpu())
+        allowed = np.arange(P + S)[None, :] <= (P + rows)[:, None]
+        ro, rl = oracle.attention(qh, kh_all[:, hk], vh_all[:, hk], scale, allowed)
+        check(f"prefill head {h} ({len(rows)} rows)", o[h, rows], lse[h, rows], ro, rl)
+    del q, k_all, v_all, caches, run
     torch.cuda.empty_cache()
