@@ -1,8 +1,9 @@
 // bf16 MFMA attention step kernels for gfx950: one query block against one K/V chunk.
 //
 // Online-max mode: flash-style running row max / row sum / rescaled accumulator,
-// emitting the chunk's normalised partial and per-row LSE ("Kernel reference:
-// ring_attention_const_max_fwd", Design: the online-max path and its running max).
+// emitting the chunk's normalised partial and per-row LSE, or merging it by the LSE rule
+// into a prior partial held in the outputs ("Kernel reference: ring_attention_const_max_fwd",
+// Design: the online-max path and its running max; sharding page, ring attention).
 // Const-max mode: p = exp(s - c_i) with the fixed per-row bound and a pure-addition
 // fold into an fp32 accumulator, normalised once with the 1e-37 clamp (same page,
 // Design "A static bound makes the ring reduction pure addition", Implementation
@@ -14,12 +15,13 @@
 //  * keys stream through LDS in tiles of 32 held in a ring of NBUF buffers, copied from
 //    HBM straight into LDS (global_load_lds_dwordx4: no staging registers, one scalar
 //    base per tile plus a fixed per-lane offset), NBUF - 1 tiles ahead of use;
-//  * ping-pong: on a SIMD, one wave's matrix phase (the scores of tile j+1, K Q^T, and
-//    the output update of tile j, V^T P^T: 16 MFMAs) runs while the other wave does the
-//    softmax of tile j on the VALU and reads the next fragments from LDS. A single wave
-//    cannot overlap its own MFMAs with its VALU work, two waves on one SIMD can; the
-//    phases are held in step by one workgroup barrier per phase, waves 4..7 starting
-//    one phase behind waves 0..3;
+//  * ping-pong: on a SIMD, one wave's matrix phase (the output update of tile j, V^T P^T,
+//    and the scores of tile j+1, K Q^T: 16 MFMAs, with the K and V fragment reads of tile
+//    j+1 spread between them) runs while the other wave does the softmax of tile j on the
+//    VALU, with no LDS reads. Two waves give the MFMA/VALU overlap whatever order the
+//    compiler gives each wave's instructions (one wave overlaps its own only where its
+//    stream interleaves them). The phases are held in step by one workgroup barrier per
+//    phase, waves 4..7 starting one phase behind waves 0..3;
 //  * LDS rows are dense (256 B) with XOR-swizzled 16-byte chunks so that both read
 //    patterns are bank-conflict free: K chunk c of row r sits at c ^ (r & 15), V chunk
 //    c at c ^ (4(r & 3) + 2((r >> 1) & 1));
