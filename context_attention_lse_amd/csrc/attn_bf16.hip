@@ -696,6 +696,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
 
   // ---- combine the segments of the tiles this wave arrived at last, in key order
   // (deterministic sums). Done after the tile loop, so none of the loop's state is live here.
+  // The records are read two at a time with every load of both in flight before any is
+  // used (each record is 64 registers a lane; two of them and the accumulator fit), so a
+  // tile of n segments costs ceil(n / 2) trips to the coherence point. Each pair is weighted
+  // by its own maximum and folded into the running one by the LSE rule.
   for (int ci = 0; ci < ncomb; ++ci) {
     const int tix = ci == 0 ? comb_tile[0] : comb_tile[1];
     const int64_t tile_start = ci == 0 ? comb_start[0] : comb_start[1];
@@ -706,36 +710,55 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     const int w_last = range_owner(sp, tile_start + tile_iters(MASK, qb, nkt) - 1);
     float c2 = 0.0f;
     if (MODE == MODE_CONSTMAX) c2 = a.c[int64_t(bh) * Sq + min(row, Sq - 1)] * kLog2e;
-    float M = -INFINITY;
-    if (MODE == MODE_ONLINE)
-      for (int wq = w_first; wq <= w_last; ++wq)
-        M = fmaxf(M, __hip_atomic_load(sp.pml + (segment_slot(sp, wq, tile_start) * NW + w) * 128 + lane,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float M = -INFINITY;   // running max of the records folded so far (online mode)
     float L = 0.0f;
     floatx16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    for (int wq = w_first; wq <= w_last; ++wq) {
-      const int64_t rec = segment_slot(sp, wq, tile_start) * NW + w;
-      float wt = 1.0f;
-      if (MODE == MODE_ONLINE) {
-        const float mq = __hip_atomic_load(sp.pml + rec * 128 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        wt = mq == -INFINITY ? 0.0f : exp2f(mq - M);
+    for (int wb = w_first; wb <= w_last; wb += 2) {
+      uint64_t buf[2][32];
+      float bm[2], bl[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bm[u] = -INFINITY;
+        bl[u] = 0.0f;
+        if (wb + u > w_last) continue;
+        const int64_t rec = segment_slot(sp, wb + u, tile_start) * NW + w;
+        if (MODE == MODE_ONLINE)
+          bm[u] = __hip_atomic_load(sp.pml + rec * 128 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bl[u] = __hip_atomic_load(sp.pml + rec * 128 + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // 8-byte agent-scope loads, 32 per record and lane
+        const uint64_t* po = reinterpret_cast<const uint64_t*>(sp.po + rec * (64 * 64) + lane * 4);
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          buf[u][i] = __hip_atomic_load(po + (i / 2) * 128 + (i % 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      L += wt * __hip_atomic_load(sp.pml + rec * 128 + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // 8-byte agent-scope loads: 32 per record and lane, all in flight at once
-      const uint64_t* po = reinterpret_cast<const uint64_t*>(sp.po + rec * (64 * 64) + lane * 4);
+      float wt[2] = {1.0f, 1.0f};
+      if (MODE == MODE_ONLINE) {
+        const float Mb = fmaxf(M, fmaxf(bm[0], bm[1]));
+        const float alpha = M == Mb ? 1.0f : exp2f(M - Mb);   // M = -inf < Mb: alpha = 0
+        L *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const uint64_t bits = __hip_atomic_load(po + (db * 4 + r / 4) * 128 + (r % 4) / 2, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-          o[db][r] += wt * __uint_as_float(uint32_t(bits));
-          o[db][r + 1] += wt * __uint_as_float(uint32_t(bits >> 32));
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) wt[u] = bm[u] == -INFINITY ? 0.0f : exp2f(bm[u] - Mb);
+        M = Mb;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (wb + u > w_last) continue;
+        L += wt[u] * bl[u];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int db = i / 8, r = 2 * (i % 8);
+          o[db][r] += wt[u] * __uint_as_float(uint32_t(buf[u][i]));
+          o[db][r + 1] += wt[u] * __uint_as_float(uint32_t(buf[u][i] >> 32));
         }
+      }
     }
     store_rows<MODE>(a, bh, Sq, row, hl, o, L, M, c2);
   }
