@@ -41,8 +41,10 @@
 // Key-split schedule (when the caller passes a workspace and one workgroup per query tile
 // would leave over a tenth of the device's workgroup slots idle, e.g. 160 tiles on 256
 // CUs): the (query tile, key tile) iterations of the whole call are laid end to end and
-// cut into G equal ranges, G = the number of workgroups the device holds at once (or fewer
-// for small calls), so every workgroup does the same work and the grid fills the machine.
+// cut into G ranges of equal cost, G = the number of workgroups the device holds at once
+// (or fewer for small calls), so every workgroup does the same work and the grid fills the
+// machine. The cost of a range is its iterations plus a fixed charge for each query tile
+// that starts inside it (a segment's Q load, copy prologue and partial or final store).
 // A query tile whose keys fall into several ranges is computed in segments; each segment
 // leaves its unnormalised partial (rows' output, running max and row sum) in the workspace
 // and bumps the tile's counter, and the workgroup that brings the counter to the segment
@@ -355,19 +357,53 @@ struct Split {
                    // segment and wave, lane-interleaved so every 16-byte store is one contiguous 1 KB
   float* pml;      // [2G][NW][2][64 lanes] partial running max (log2 units) and full row sum
   int G;           // logical workgroups
-  int64_t T;       // iterations (query tile x key tile) of the whole call
+  int C;           // cost of a query tile's start, in iterations (see range_begin)
+  int64_t V;       // weighted length of the call: T iterations + C per query tile
   int64_t per_bh;  // iterations of one (batch, head)
 };
 
-__device__ __forceinline__ int64_t range_begin(const Split& sp, int w) { return sp.T * w / sp.G; }
-// The workgroup whose range holds iteration x: the largest w with range_begin(w) <= x.
-__device__ __forceinline__ int range_owner(const Split& sp, int64_t x) {
-  return int((int64_t(sp.G) * (x + 1) + sp.T - 1) / sp.T) - 1;
+// The ranges are cut by weight, not by iteration count: every query tile is followed by C
+// units of weight that belong to no iteration, standing for the cost of a segment boundary
+// (publishing or combining a partial, a second Q load and copy prologue). A range that holds
+// a tile boundary thus gets about C fewer iterations than one inside a single tile, and the
+// workgroups finish together. Iteration x of global query tile g sits at weight x + C*g;
+// the cuts are at V*w/G.
+__device__ __forceinline__ int64_t weight_of(const Split& sp, int64_t x, int g) { return x + int64_t(sp.C) * g; }
+
+// First iteration of workgroup w's range: the first iteration whose weight reaches V*w/G
+// (a cut inside a tile's trailing C units moves to the next tile's start).
+template <int MASK>
+__device__ __forceinline__ int64_t range_begin(const Split& sp, int nqb, int nkt, int w) {
+  const int64_t P = sp.V * w / sp.G;
+  const int64_t bh_w = sp.per_bh + int64_t(sp.C) * nqb;   // weight of one (batch, head)
+  const int64_t bh = P / bh_w;
+  const int64_t r = P - bh * bh_w;
+  int qb;
+  if (MASK == CA_MASK_NONE) {
+    qb = int(r / (nkt + sp.C));
+  } else {
+    int lo = 0, hi = nqb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tiles_prefix(MASK, mid, nkt) + int64_t(sp.C) * mid <= r) lo = mid; else hi = mid - 1;
+    }
+    qb = lo;
+  }
+  const int64_t t0 = tiles_prefix(MASK, qb, nkt);
+  const int64_t off = r - t0 - int64_t(sp.C) * qb;
+  const int len = tile_iters(MASK, qb, nkt);
+  return bh * sp.per_bh + (off < len ? t0 + off : tiles_prefix(MASK, qb + 1, nkt));
+}
+// The workgroup whose range holds iteration x of global query tile g: the largest w whose
+// cut weight V*w/G is at most x's weight.
+__device__ __forceinline__ int range_owner(const Split& sp, int64_t x, int g) {
+  return int((int64_t(sp.G) * (weight_of(sp, x, g) + 1) + sp.V - 1) / sp.V) - 1;
 }
 // Record of workgroup w's segment of the tile starting at iteration tile_start: its first
 // segment (slot 2w) unless the tile began before w's range (then its last, 2w + 1).
-__device__ __forceinline__ int64_t segment_slot(const Split& sp, int w, int64_t tile_start) {
-  return 2 * int64_t(w) + (range_begin(sp, w) >= tile_start ? 0 : 1);
+template <int MASK>
+__device__ __forceinline__ int64_t segment_slot(const Split& sp, int nqb, int nkt, int w, int64_t tile_start) {
+  return 2 * int64_t(w) + (range_begin<MASK>(sp, nqb, nkt, w) >= tile_start ? 0 : 1);
 }
 
 template <int MODE, int MASK, bool SPLIT>
@@ -418,8 +454,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
 
   int64_t it = 0, it_end = 1;
   if (SPLIT) {
-    it = range_begin(sp, logical);
-    it_end = range_begin(sp, logical + 1);
+    it = range_begin<MASK>(sp, nqb, nkt, logical);
+    it_end = range_begin<MASK>(sp, nqb, nkt, logical + 1);
   }
   // Tiles this wave combines once its own range is done (at most its first and last
   // segment's tiles): tile index bh * nqb + qb and the tile's first iteration.
@@ -657,8 +693,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       continue;
     }
     const int tile_iters_n = tile_iters(MASK, qb, nkt);
-    const int w_first = range_owner(sp, tile_start);
-    const int w_last = range_owner(sp, tile_start + tile_iters_n - 1);
+    const int w_first = range_owner(sp, tile_start, bh * nqb + qb);
+    const int w_last = range_owner(sp, tile_start + tile_iters_n - 1, bh * nqb + qb);
     if (w_first == w_last) {   // the whole tile lies in this workgroup's range
       store_rows<MODE>(a, bh, Sq, row, hl, o, lrow, m_ref, c2);
       continue;
@@ -670,7 +706,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     // (vmcnt 0) before the counter moves, and the combiner loads only after it has seen the
     // final count.
     {
-      const int64_t rec = segment_slot(sp, logical, tile_start) * NW + w;
+      const int64_t rec = segment_slot<MASK>(sp, nqb, nkt, logical, tile_start) * NW + w;
       float* po = sp.po + rec * (64 * 64) + lane * 4;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -706,8 +742,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     const int bh = tix / nqb;
     const int qb = tix - bh * nqb;
     const int row = qb * BQ + w * 32 + li;
-    const int w_first = range_owner(sp, tile_start);
-    const int w_last = range_owner(sp, tile_start + tile_iters(MASK, qb, nkt) - 1);
+    const int w_first = range_owner(sp, tile_start, tix);
+    const int w_last = range_owner(sp, tile_start + tile_iters(MASK, qb, nkt) - 1, tix);
     float c2 = 0.0f;
     if (MODE == MODE_CONSTMAX) c2 = a.c[int64_t(bh) * Sq + min(row, Sq - 1)] * kLog2e;
     float M = -INFINITY;   // running max of the records folded so far (online mode)
@@ -725,7 +761,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
         bm[u] = -INFINITY;
         bl[u] = 0.0f;
         if (wb + u > w_last) continue;
-        const int64_t rec = segment_slot(sp, wb + u, tile_start) * NW + w;
+        const int64_t rec = segment_slot<MASK>(sp, nqb, nkt, wb + u, tile_start) * NW + w;
         if (MODE == MODE_ONLINE)
           bm[u] = __hip_atomic_load(sp.pml + rec * 128 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         bl[u] = __hip_atomic_load(sp.pml + rec * 128 + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -778,6 +814,8 @@ int resident_workgroups() {
 }
 
 constexpr int64_t kMinItersPerWorkgroup = 8;
+// Weight of a query tile's start in the key-split cuts, in iterations (range_begin).
+constexpr int kTileStartCost = 8;
 // Splitting pays where one workgroup per query tile would leave more than this share of the
 // device's workgroup slots idle over the call (the last, partly filled round of tiles).
 constexpr double kMaxIdleShare = 0.10;
@@ -827,7 +865,8 @@ hipError_t launch_one(const AttnArgs& a, const Plan& p, hipStream_t s) {
     sp.po = reinterpret_cast<float*>(ws + p.cnt_bytes);
     sp.pml = reinterpret_cast<float*>(ws + p.cnt_bytes + p.po_bytes);
     sp.G = p.G;
-    sp.T = p.T;
+    sp.C = kTileStartCost;
+    sp.V = p.T + int64_t(kTileStartCost) * a.B * a.H * p.nqb;
     sp.per_bh = p.per_bh;
     nwork = p.G;
   }
