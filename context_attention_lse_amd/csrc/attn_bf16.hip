@@ -840,7 +840,20 @@ Plan make_plan(int B, int H, int Sq, int Sk, int mask) {
   const int64_t rounds = (tiles + slots - 1) / slots;
   p.split = double(rounds * slots - tiles) > kMaxIdleShare * double(rounds * slots);
   if (!p.split) return p;
-  const int64_t g = std::min<int64_t>(slots, (p.T + kMinItersPerWorkgroup - 1) / kMinItersPerWorkgroup);
+  int64_t g = std::min<int64_t>(slots, (p.T + kMinItersPerWorkgroup - 1) / kMinItersPerWorkgroup);
+  if (mask == CA_MASK_NONE && g == slots) {
+    // Equal query tiles: a count that cuts every pair of tiles into the same k ranges,
+    // G = tiles * k / 2, puts the cuts at the same places in every pair, so no tile holds
+    // more segments than its neighbours (with G = 1.6 tiles, three in five tiles hold three
+    // segments; with 1.5, every tile holds two). Taken when it idles under a tenth of the
+    // slots.
+    for (int64_t k = (2 * slots) / tiles; k >= 2; --k) {
+      if ((tiles * k) % 2 != 0) continue;
+      const int64_t gk = tiles * k / 2;
+      if (gk <= slots && double(gk) >= (1.0 - kMaxIdleShare) * double(slots)) g = gk;
+      break;
+    }
+  }
   p.G = int(std::max<int64_t>(1, g));
   p.cnt_bytes = (size_t(B) * H * p.nqb * NW * sizeof(int) + 255) & ~size_t(255);
   p.po_bytes = size_t(2) * p.G * NW * 64 * 64 * sizeof(float);
