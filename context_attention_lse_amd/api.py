@@ -80,13 +80,23 @@ def _ws(workspace):
 
 
 def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspace=None, stream=None,
-                   fold=False):
+                   fold=False, hop=None):
     """Online-max attention of q [B, Sq, H, D] against one K/V chunk [B, Sk, H, D].
     Returns (o [B, H, Sq, D] fp32, lse [B, H, Sq] fp32). With ``workspace`` (from
     step_workspace) the key range is split over a grid that fills the device. With
     ``fold``, ``out`` and ``lse`` (required) hold a prior partial of the same rows and
-    receive its LSE merge with this chunk's partial (ring_attn_step_fold)."""
+    receive its LSE merge with this chunk's partial (ring_attn_step_fold). ``hop`` =
+    (dst_k, dst_v, src_k, src_v), contiguous buffers of one size: the ring's next K/V hop,
+    copied by the same call (ring_attn_step_hop; not with ``fold``)."""
     _check_cuda(q, k, v, out, lse, workspace)
+    if hop is not None:
+        if fold:
+            raise ValueError("hop and fold do not combine")
+        _check_cuda(*hop)
+        nbytes = hop[2].numel() * hop[2].element_size()
+        for t in hop:
+            if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+                raise ValueError("hop buffers must be contiguous and of one size")
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
@@ -105,10 +115,12 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspa
         out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    _lib.call("ring_attn_step_fold" if fold else "ring_attn_step", _ptr(q), _strides(q), _ptr(k), _ptr(v),
-              _strides(k), _dtype_code(q),
-              B, H, Sq, Sk, D, _scale(scale), MASKS[mask] if isinstance(mask, str) else int(mask),
-              _ptr(out), _ptr(lse), *_ws(workspace), _stream(stream))
+    args = (_ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q), B, H, Sq, Sk, D, _scale(scale),
+            MASKS[mask] if isinstance(mask, str) else int(mask), _ptr(out), _ptr(lse), *_ws(workspace))
+    if hop is not None:
+        _lib.call("ring_attn_step_hop", *args, *(_ptr(t) for t in hop), nbytes, _stream(stream))
+    else:
+        _lib.call("ring_attn_step_fold" if fold else "ring_attn_step", *args, _stream(stream))
     return out, lse
 
 

@@ -96,13 +96,29 @@ const char* ca_last_error(void) { return g_err; }
 
 const char* ca_version(void) { return "0.1.0"; }
 
+// A ring hop (kv_chunk_copy's job) carried by a step call; bytes == 0: none.
+struct Hop {
+  void* dk;
+  void* dv;
+  const void* sk;
+  const void* sv;
+  size_t bytes;
+};
+
+// Workgroups that carry a ring hop inside a step launch.
+constexpr int kHopWorkgroups = 16;
+
 static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides qs, const void* k, const void* v,
                                      ca_strides kvs, int dtype, int B, int H, int Sq, int Sk, int D,
                                      float softmax_scale, int mask, float* o, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream, int fold) {
+                                     size_t workspace_bytes, void* stream, int fold, Hop hop = Hop{}) {
   CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
   if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
-  if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
+  if (int64_t(B) * H * Sq == 0) {   // no rows: only the hop, if any
+    if (hop.bytes == 0) return hip_status(hipSuccess, "");
+    return hip_status(ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, static_cast<hipStream_t>(stream)),
+                      name);
+  }
   if (!o || !lse) return fail(CA_ERR_NULL, "o and lse are required");
   if (!aligned16(o)) return fail(CA_ERR_SHAPE, "o must be 16-byte aligned");
   ctxattn::AttnArgs a{};
@@ -117,6 +133,19 @@ static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides
   a.fold = fold;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hop.bytes > 0) {
+    // In the step's own launch when its last round leaves enough CUs free, else as a
+    // separate copy ahead of it on the same stream.
+    if (dtype == CA_BF16 &&
+        ctxattn::attn_bf16_idle_slots(B, H, Sq, Sk, mask, a.ws != nullptr) >= kHopWorkgroups) {
+      a.hop_sk = hop.sk; a.hop_sv = hop.sv; a.hop_dk = hop.dk; a.hop_dv = hop.dv;
+      a.hop_units = int64_t(hop.bytes / 16);
+      a.hop_wgs = kHopWorkgroups;
+    } else {
+      hipError_t e = ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, s);
+      if (e != hipSuccess) return hip_status(e, name);
+    }
+  }
   hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
   return hip_status(e, name);
 }
@@ -133,6 +162,22 @@ ca_status ring_attn_step_fold(const void* q, ca_strides qs, const void* k, const
                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return ring_attn_step_impl("ring_attn_step_fold launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale,
                              mask, o, lse, workspace, workspace_bytes, stream, 1);
+}
+
+ca_status ring_attn_step_hop(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs, int dtype,
+                             int B, int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o,
+                             float* lse, void* workspace, size_t workspace_bytes, void* hop_dst_k, void* hop_dst_v,
+                             const void* hop_src_k, const void* hop_src_v, size_t hop_bytes, void* stream) {
+  if (hop_bytes > 0) {
+    if (!hop_dst_k || !hop_dst_v || !hop_src_k || !hop_src_v)
+      return fail(CA_ERR_NULL, "ring_attn_step_hop: hop buffers are required when hop_bytes > 0");
+    if (hop_bytes % 16 || !aligned16(hop_dst_k) || !aligned16(hop_dst_v) || !aligned16(hop_src_k) ||
+        !aligned16(hop_src_v))
+      return fail(CA_ERR_SHAPE, "ring_attn_step_hop: hop pointers must be 16-byte aligned and hop_bytes a multiple of 16");
+  }
+  return ring_attn_step_impl("ring_attn_step_hop launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale,
+                             mask, o, lse, workspace, workspace_bytes, stream, 0,
+                             Hop{hop_dst_k, hop_dst_v, hop_src_k, hop_src_v, hop_bytes});
 }
 
 ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask, size_t* bytes) {

@@ -406,12 +406,42 @@ __device__ __forceinline__ int64_t segment_slot(const Split& sp, int nqb, int nk
   return 2 * int64_t(w) + (range_begin<MASK>(sp, nqb, nkt, w) >= tile_start ? 0 : 1);
 }
 
+// The ring hop of a launch that carries one: workgroup cw of a.hop_wgs copies its grid-stride
+// share of K then V, 16 bytes a lane, HOP_UNROLL vectors in flight per lane. The hop's
+// workgroups come last in the grid, so they take the CUs the step's workgroups leave free.
+constexpr int HOP_UNROLL = 16;
+__device__ __forceinline__ void hop_copy(const AttnArgs& a, int cw) {
+  const floatx4* sk = static_cast<const floatx4*>(a.hop_sk);
+  const floatx4* sv = static_cast<const floatx4*>(a.hop_sv);
+  floatx4* dk = static_cast<floatx4*>(a.hop_dk);
+  floatx4* dv = static_cast<floatx4*>(a.hop_dv);
+  const int64_t units = a.hop_units, total = 2 * units;
+  const int64_t stride = int64_t(a.hop_wgs) * NT * HOP_UNROLL;
+  for (int64_t base = int64_t(cw) * NT * HOP_UNROLL + threadIdx.x; base < total; base += stride) {
+    floatx4 x[HOP_UNROLL];
+#pragma unroll
+    for (int u = 0; u < HOP_UNROLL; ++u) {
+      const int64_t i = base + int64_t(u) * NT;
+      if (i < total) x[u] = __builtin_nontemporal_load(i < units ? sk + i : sv + (i - units));
+    }
+#pragma unroll
+    for (int u = 0; u < HOP_UNROLL; ++u) {
+      const int64_t i = base + int64_t(u) * NT;
+      if (i < total) __builtin_nontemporal_store(x[u], i < units ? dk + i : dv + (i - units));
+    }
+  }
+}
+
 template <int MODE, int MASK, bool SPLIT>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
-  const int logical = xcd_logical_id(blockIdx.x, gridDim.x, nwork);
+  if (a.hop_wgs > 0 && int(blockIdx.x) >= int(gridDim.x) - a.hop_wgs) {
+    hop_copy(a, int(blockIdx.x) - (int(gridDim.x) - a.hop_wgs));
+    return;
+  }
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x - a.hop_wgs, nwork);
   if (logical < 0) return;
 
   const int tid = threadIdx.x;
@@ -883,8 +913,8 @@ hipError_t launch_one(const AttnArgs& a, const Plan& p, hipStream_t s) {
     sp.per_bh = p.per_bh;
     nwork = p.G;
   }
-  if (nwork == 0) return hipSuccess;
-  const int grid = round_up8(nwork);
+  if (nwork == 0 && a.hop_wgs == 0) return hipSuccess;
+  const int grid = round_up8(nwork) + a.hop_wgs;
   hipLaunchKernelGGL((attn_step_bf16<MODE, MASK, SPLIT>), dim3(grid), dim3(NT), LDS_BYTES, s, a, p.nqb, p.nkt,
                      nwork, sp);
   return hipGetLastError();
@@ -901,6 +931,15 @@ hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
 
 size_t attn_bf16_workspace_bytes(int B, int H, int Sq, int Sk, int mask) {
   return make_plan(B, H, Sq, Sk, mask).bytes();
+}
+
+int attn_bf16_idle_slots(int B, int H, int Sq, int Sk, int mask, bool with_workspace) {
+  const Plan p = make_plan(B, H, Sq, Sk, mask);
+  const int64_t slots = resident_workgroups();
+  const int64_t nwork = (with_workspace && p.split) ? p.G : int64_t(B) * H * p.nqb;
+  if (nwork == 0) return int(slots);
+  const int64_t last = nwork - (nwork - 1) / slots * slots;   // work items of the last round
+  return int(slots - last);
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s) {

@@ -108,6 +108,15 @@ struct AttnArgs {
   int64_t key_offset;
   // per (batch, head) key count (bf16 path, no key split): keys [0, min(Sk, sk_of_bh[bh]))
   const int32_t* sk_of_bh;
+  // ring hop carried by the same launch (bf16 path): hop_units 16-byte vectors of K and of
+  // V copied from hop_sk / hop_sv to hop_dk / hop_dv by hop_wgs workgroups appended to the
+  // grid (0: no hop)
+  const void* hop_sk;
+  const void* hop_sv;
+  void* hop_dk;
+  void* hop_dv;
+  int64_t hop_units;
+  int hop_wgs;
 };
 
 // Internal mask (bf16 path, online-max only): the keys are rank R's slice of a chunk
@@ -206,5 +215,8 @@ struct SegmentedArgs {
 size_t segmented_workspace_bytes(int Hq, int Hkv, int S, int D, int prior);
 hipError_t launch_segmented(const SegmentedArgs& g, hipStream_t s);
 hipError_t launch_kv_copy(void* dk, void* dv, const void* sk, const void* sv, size_t bytes, hipStream_t s);
+// Workgroups of a bf16 step launch that would sit idle over its last round of workgroups
+// (the device's slots minus the last round's work items).
+int attn_bf16_idle_slots(int B, int H, int Sq, int Sk, int mask, bool with_workspace);
 
 }  // namespace ctxattn

@@ -93,7 +93,7 @@ class RingPass:
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
                  scale=None, prefetch_depth=2, out_dtype=torch.float32, copy_stream=None,
-                 compute_streams=None, split=False, sink_theta=None, sink_cap=32, fold=False):
+                 compute_streams=None, split=False, sink_theta=None, sink_cap=32, fold=False, fused_hops=False):
         if variant not in ("online", "constmax"):
             raise ValueError(f"unknown variant {variant!r}")
         if fold and variant != "online":
@@ -111,6 +111,14 @@ class RingPass:
         self.out_dtype = out_dtype
         self.depth = max(1, min(int(prefetch_depth), max(1, self.cp - 1)))
         self.nbuf = self.depth + 1
+        # fused hops: step s carries the hop of chunk s + 2 (ring_attn_step_hop). Its buffer was
+        # last read by step s - 2, which ran before it on the same compute stream; four
+        # buffers keep that true with two compute streams.
+        self.fused_hops = bool(fused_hops)
+        if self.fused_hops:
+            if variant != "online" or fold:
+                raise ValueError("fused hops apply to the online variant without fold")
+            self.depth, self.nbuf = 2, 4
         B, Sq, H, D = q.shape
         chunk_shape = tuple(k_pool.shape[1:])
         dev = q.device
@@ -203,6 +211,8 @@ class RingPass:
         each step's kernel on the stream that runs it."""
         cs = torch.cuda.current_stream()
         cp = self.cp
+        if self.fused_hops:
+            return self._run_fused(cs, timing_events)
         if self.variant == "constmax":
             self.prologue()
         self.copy_stream.wait_stream(cs)
@@ -269,13 +279,54 @@ class RingPass:
         return self.out, self.lse
 
 
+    def _hop_buffers(self, t):
+        kd, vd = self._chunk(t)
+        src = ring_source_rank(self.rank, t, self.cp)
+        return kd, vd, self.k_pool[src], self.v_pool[src]
+
+    def _run_fused(self, cs, timing_events):
+        """run() with every hop carried by a step call: step s also moves chunk s + 2 into its
+        buffer (on the CUs the step leaves free, or just ahead of it), so no copy stream is
+        used and the two compute streams never wait on each other. Chunk 1 is moved by a
+        plain copy ahead of step 1."""
+        cp = self.cp
+        if self.aux_stream is not None:
+            self.aux_stream.wait_stream(cs)
+        streams = [self.aux_stream if (self.aux_stream is not None and s % 2 == 1) else cs for s in range(cp)]
+        if cp > 1:
+            with torch.cuda.stream(streams[1]):
+                api.kv_chunk_copy(*self._hop_buffers(1))
+        slot = 0
+        for s in range(cp):
+            st = streams[s]
+            hop = self._hop_buffers(s + 2) if s + 2 < cp else None
+            k, v = self._chunk(s)
+            with torch.cuda.stream(st):
+                if timing_events is not None:
+                    timing_events[s][0].record(st)
+                if self.masks[s] is not None:
+                    api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s], out=self.o_parts[slot],
+                                       lse=self.lse_parts[slot], workspace=self.ws[1 if st is not cs else 0], hop=hop)
+                    slot += 1
+                elif hop is not None:
+                    api.kv_chunk_copy(*hop)
+                if timing_events is not None:
+                    timing_events[s][1].record(st)
+        if self.aux_stream is not None:
+            cs.wait_stream(self.aux_stream)
+        api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
+        return self.out, self.lse
+
+
 def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous", causal=False,
-                   variant="online", scale=None, prefetch_depth=2, split=False, fold=False, compute_streams=None):
+                   variant="online", scale=None, prefetch_depth=2, split=False, fold=False, compute_streams=None,
+                   fused_hops=False):
     """Convenience: rank ``rank``'s output for global [B, S, H, D] inputs."""
     check_divisible(q_global.shape[1], cp)
     q = shard(q_global, cp, rank, layout)
     kp = chunk_pool(k_global, cp, layout)
     vp = chunk_pool(v_global, cp, layout)
     rp = RingPass(q, kp, vp, rank, layout=layout, causal=causal, variant=variant, scale=scale,
-                  prefetch_depth=prefetch_depth, split=split, fold=fold, compute_streams=compute_streams)
+                  prefetch_depth=prefetch_depth, split=split, fold=fold, compute_streams=compute_streams,
+                  fused_hops=fused_hops)
     return rp.run()

@@ -93,8 +93,9 @@ typedef struct {
  *          optional device scratch (see ring_attn_workspace_size). NULL: one workgroup
  *          per 256 query rows (bf16). Given, and the call is one that one workgroup per
  *          256 rows would leave the device's workgroup slots more than a tenth idle: the call's
- *          (query tile, key tile) iterations are cut into equal ranges, one per workgroup
- *          the device holds at once, and query tiles split between ranges are combined in
+ *          (query tile, key tile) iterations are cut into ranges of equal cost (each query
+ *          tile's start counts as a few iterations), about one per workgroup the device
+ *          holds at once, and query tiles split between ranges are combined in
  *          the library, in key order (results do not depend on timing). The workspace must
  *          be 256-byte aligned and all zero before its first use; every call leaves it
  *          ready for the next. Calls that may run at the same time need separate
@@ -133,6 +134,37 @@ ca_status ring_attn_step_fold(const void* q, ca_strides q_strides,
                               float softmax_scale, int mask,
                               float* o, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ring_attn_step_hop -- ring_attn_step and, in the same call, the ring's next K/V hop
+ * (what kv_chunk_copy does): hop_bytes bytes copied from hop_src_k to hop_dst_k and
+ * from hop_src_v to hop_dst_v. Where the step's last round of workgroups leaves CUs
+ * free (a key-split step cut into fewer ranges than the device holds; the last, partly
+ * filled round of an unsplit one), the copy runs in the same launch on those CUs, so
+ * the hop overlaps the step without a stream of its own; otherwise it is an ordinary
+ * copy launched just ahead of the step on the same stream. Either way both are done
+ * when work queued after the call on the stream starts.
+ * Source: kernel reference page, Implementation, the ring loop (the next chunk moves
+ * while the current one is computed); "Sharding the Input", ring attention.
+ *
+ * Arguments, layouts, support and errors: as ring_attn_step, plus
+ *   hop_dst_k, hop_dst_v  OUT device buffers of hop_bytes each
+ *   hop_src_k, hop_src_v  IN device buffers of hop_bytes each
+ *   hop_bytes             0: no hop (the call is ring_attn_step); else a multiple of 16,
+ *                         with all four pointers 16-byte aligned (CA_ERR_SHAPE), non-NULL
+ *                         (CA_ERR_NULL)
+ * The destinations must not overlap the sources or any input, output or workspace of
+ * the step (they are written while the step runs). Bytes move unchanged (bit copy).
+ */
+ca_status ring_attn_step_hop(const void* q, ca_strides q_strides,
+                             const void* k, const void* v, ca_strides kv_strides,
+                             int dtype, int B, int H, int Sq, int Sk, int D,
+                             float softmax_scale, int mask,
+                             float* o, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             void* hop_dst_k, void* hop_dst_v,
+                             const void* hop_src_k, const void* hop_src_v, size_t hop_bytes,
+                             void* stream);
 
 /*
  * ring_attn_workspace_size -- bytes of step workspace that ring_attn_step and
