@@ -1,9 +1,10 @@
 """Benchmark of the context-parallel attention hot path on one MI355X.
 
 Headline (``value``): one rank's ring pass of the Wan2.2-shaped workload (10 heads of
-128, S = 32768 over cp = 8, local 4096 queries): 8 online-max steps, each fed by a
-double-buffered K/V chunk copy, then the LSE merge. value = algorithmic TFLOP/s of the
-whole pass (4*H*Sq*S*D flops), inputs resident in HBM when timing starts.
+128, S = 32768 over cp = 8, local 4096 queries): 8 online-max steps, every K/V chunk after
+the rank's own moved into a receive buffer (the ring hop; each step carries the hop of the
+chunk two steps ahead), then the LSE merge. value = algorithmic TFLOP/s of the whole pass
+(4*H*Sq*S*D flops), inputs resident in HBM when timing starts.
 
 Also reported (``workloads``): the const-max ring on the 720p share (40 heads,
 local 9450), the striped causal ring at S = 128k (all 8 ranks' passes), DCP decode
@@ -128,9 +129,10 @@ def headline(args, torch, ca, workloads, gen, dev):
     kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
     del t
-    # key-split steps (each fills the device) on two compute streams, so one step's drain
-    # overlaps the next step's start
-    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=True, compute_streams=2)
+    # key-split steps on two compute streams, so one step's drain overlaps the next step's
+    # start; each step carries the hop of the chunk two steps ahead on the CUs it leaves free
+    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=True, compute_streams=2,
+                          fused_hops=True)
     Sq = wl.local_S
     flops_pass = ring_flops(wl.H, Sq, wl.S, wl.D)
     flops_step = ring_flops(wl.H, Sq, wl.local_S, wl.D)

@@ -87,8 +87,15 @@ class RingPass:
     compute stream by default. Otherwise steps keep one workgroup per query tile and online
     steps alternate two compute streams, so a step can fill the CUs the previous one leaves
     idle as it drains. compute_streams overrides either default. On the Wan2.2 share (160
-    query tiles of 256 rows per step) the fastest pass is split steps on two streams: 0.86 ms,
-    against 0.90 ms unsplit on one stream, 0.94 ms split on one and 0.96 ms unsplit on two.
+    query tiles of 256 rows per step) the fastest pass was split steps on two streams: 0.86 ms,
+    against 0.90 ms unsplit on one stream, 0.94 ms split on one and 0.96 ms unsplit on two
+    (timed with hops on the copy stream, before the split's regular cuts).
+
+    fused_hops=True (online, no fold): each step call carries the hop of the chunk two steps
+    ahead (ring_attn_step_hop), on the CUs the step leaves free when there are any, instead of
+    a copy stream. A step fills every CU's register file, so a copy kernel on its own stream
+    runs only between steps; carried by the step it costs nothing there. On the Wan2.2 share
+    (240 ranges, 16 CUs free) the pass went from 806 to 779 us.
     """
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",

@@ -60,8 +60,15 @@ def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q, **ring_kw):
 
 
 def test_wan22_cp8_online_fullsize(ca):
-    # the headline's launch configuration: key-split steps alternating two compute streams
+    # the headline's launch configuration: key-split steps alternating two compute streams,
+    # each carrying the hop of the chunk two steps ahead
     _ring_fullsize(ca, "wan22_cp8_online", "online", 0, heads=(0, 4, 9), contiguous_q=False, split=True,
+                   compute_streams=2, fused_hops=True)
+
+
+def test_wan22_cp8_online_fullsize_copy_stream(ca):
+    # the same with the hops on a copy stream
+    _ring_fullsize(ca, "wan22_cp8_online", "online", 3, heads=(1, 8), contiguous_q=False, split=True,
                    compute_streams=2)
 
 
