@@ -49,8 +49,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "bb0c2b73635d7b3a",
-                                        "fetch_kib": 58628.2, "write_kib": 64920.0},
+    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "82ac9e615e4caf61",
+                                        "fetch_kib": 58130.2, "write_kib": 64920.0},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "2a888486a0688b34",
                                   "fetch_kib": 2774629.6 + 22236.4, "write_kib": 47159.9 + 1040.0},
 }
