@@ -73,12 +73,18 @@ def test_step_hop_rejects_bad_buffers(ca):
     assert e.value.status == ca._lib.CA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("wl_name,S,ranks,streams,H", [("wan22_cp8_online", 8 * 328, (0, 5), 2, None),
-                                                       ("wan22_cp8_online", 8 * 328, (3,), 1, None),
-                                                       ("striped_causal_128k", 8 * 200, (0, 7), 2, 2)])
-def test_ring_fused_hops_matches_oracle(ca, wl_name, S, ranks, streams, H):
+@pytest.mark.parametrize("wl_name,S,ranks,streams,H,layout", [
+    ("wan22_cp8_online", 8 * 328, (0, 5), 2, None, None),
+    ("wan22_cp8_online", 8 * 328, (3,), 1, None, None),
+    ("striped_causal_128k", 8 * 200, (0, 7), 2, 2, None),
+    # contiguous causal: rank 0 sees only its own chunk, so every later step is empty and
+    # its hop moves as a plain copy on that step's stream
+    ("striped_causal_128k", 8 * 200, (0, 5), 2, 2, "contiguous")])
+def test_ring_fused_hops_matches_oracle(ca, wl_name, S, ranks, streams, H, layout):
     dev = torch.device("cuda:0")
     wl = workloads.workload(wl_name).scaled(S=S, **({"H": H} if H else {}))
+    if layout is not None:
+        wl = wl.scaled(layout=layout)
     t = gen.ring_inputs(wl, dev)
     scale = oracle.default_scale(wl.D)
     for r in ranks:
