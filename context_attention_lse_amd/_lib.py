@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 # Every symbol include/ctxattn.h declares.
 EXPORTS = (
-    "ring_attn_step", "ring_attn_step_fold", "ring_attn_step_hop", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "lse_merge",
+    "ring_attn_step", "ring_attn_step_fold", "ring_attn_step_hop", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "ring_attn_const_max_step_hop", "lse_merge",
     "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error",
     "ca_version", "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
     "ring_attn_const_max_step_sinks", "sink_attention_partial", "sink_attention_workspace_size",
@@ -51,6 +51,8 @@ SIGNATURES = {
     "const_max_bound": [_vp, ca_strides, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp],
     "ring_attn_const_max_step": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
                                  _vp, _i, _vp, _vp, _sz, _vp],
+    "ring_attn_const_max_step_hop": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                     _i, _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _sz, _vp],
     "lse_merge": [_i, _vp, _vp, _i64, _i, _vp, _i, _vp, _vp],
     "dcp_decode_partial": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp],
     "dcp_decode_partial_active": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,

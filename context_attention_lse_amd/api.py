@@ -79,6 +79,16 @@ def _ws(workspace):
     return _ptr(workspace), workspace.numel()
 
 
+def _hop_bytes(hop):
+    """Checks a hop (dst_k, dst_v, src_k, src_v) and returns its size in bytes."""
+    _check_cuda(*hop)
+    nbytes = hop[2].numel() * hop[2].element_size()
+    for t in hop:
+        if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
+            raise ValueError("hop buffers must be contiguous and of one size")
+    return nbytes
+
+
 def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspace=None, stream=None,
                    fold=False, hop=None):
     """Online-max attention of q [B, Sq, H, D] against one K/V chunk [B, Sk, H, D].
@@ -92,11 +102,7 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspa
     if hop is not None:
         if fold:
             raise ValueError("hop and fold do not combine")
-        _check_cuda(*hop)
-        nbytes = hop[2].numel() * hop[2].element_size()
-        for t in hop:
-            if t.numel() * t.element_size() != nbytes or not t.is_contiguous():
-                raise ValueError("hop buffers must be contiguous and of one size")
+        nbytes = _hop_bytes(hop)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
@@ -205,12 +211,17 @@ def const_max_acc_size(B, H, Sq, D) -> int:
 
 
 def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dtype=torch.float32,
-                             scale=None, workspace=None, stream=None, sinks=None, key_offset=0):
+                             scale=None, workspace=None, stream=None, sinks=None, key_offset=0, hop=None):
     """One const-max ring step. acc: fp32 tensor of const_max_acc_size floats (None allowed
     when phase == INIT|FINAL). On the FINAL phase returns (o [B, H, Sq, D], lse [B, H, Sq]).
     ``workspace`` as for ring_attn_step. ``sinks`` (the dict from const_max_sink_prologue)
-    leaves the listed keys out; ``key_offset`` is this chunk's first key index."""
+    leaves the listed keys out; ``key_offset`` is this chunk's first key index. ``hop`` as for
+    ring_attn_step (ring_attn_const_max_step_hop; not with ``sinks``)."""
     _check_cuda(q, k, v, c, acc, out, lse, workspace)
+    if hop is not None:
+        if sinks is not None:
+            raise ValueError("hop and sinks do not combine")
+        nbytes = _hop_bytes(hop)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
@@ -227,7 +238,11 @@ def ring_attn_const_max_step(q, k, v, c, acc, phase, out=None, lse=None, out_dty
             lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     o_args = (_ptr(out) if final else None, _DT.get(out.dtype, CA_FP32) if final else CA_FP32,
               _ptr(lse) if final else None)
-    if sinks is None:
+    if hop is not None:
+        _lib.call("ring_attn_const_max_step_hop", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k),
+                  _dtype_code(q), B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase), *o_args,
+                  *_ws(workspace), *(_ptr(t) for t in hop), nbytes, _stream(stream))
+    elif sinks is None:
         _lib.call("ring_attn_const_max_step", _ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q),
                   B, H, Sq, Sk, D, _scale(scale), _ptr(c), _ptr(acc), int(phase), *o_args, *_ws(workspace),
                   _stream(stream))

@@ -105,8 +105,32 @@ struct Hop {
   size_t bytes;
 };
 
-// Workgroups that carry a ring hop inside a step launch.
-constexpr int kHopWorkgroups = 16;
+// Workgroups that carry a ring hop inside a step launch: as many as the step's last round
+// leaves free, from kMinHopWorkgroups (fewer: the copy runs ahead of the step instead) up to
+// kMaxHopWorkgroups.
+constexpr int kMinHopWorkgroups = 16;
+constexpr int kMaxHopWorkgroups = 64;
+
+// Attaches a hop to a bf16 step launch when its last round leaves enough CUs free, else
+// launches it as an ordinary copy ahead of the step on the same stream.
+static hipError_t attach_hop(ctxattn::AttnArgs& a, const Hop& hop, int dtype, int mask, hipStream_t s) {
+  if (hop.bytes == 0) return hipSuccess;
+  const int idle = dtype == CA_BF16 ? ctxattn::attn_bf16_idle_slots(a.B, a.H, a.Sq, a.Sk, mask, a.ws != nullptr) : 0;
+  if (idle < kMinHopWorkgroups) return ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, s);
+  a.hop_sk = hop.sk; a.hop_sv = hop.sv; a.hop_dk = hop.dk; a.hop_dv = hop.dv;
+  a.hop_units = int64_t(hop.bytes / 16);
+  a.hop_wgs = idle < kMaxHopWorkgroups ? idle : kMaxHopWorkgroups;
+  return hipSuccess;
+}
+
+// Validates the hop arguments of a *_hop entry point.
+static ca_status check_hop(const char* fn, const Hop& hop) {
+  if (hop.bytes == 0) return CA_OK;
+  if (!hop.dk || !hop.dv || !hop.sk || !hop.sv) return fail(CA_ERR_NULL, "%s: hop buffers are required when hop_bytes > 0", fn);
+  if (hop.bytes % 16 || !aligned16(hop.dk) || !aligned16(hop.dv) || !aligned16(hop.sk) || !aligned16(hop.sv))
+    return fail(CA_ERR_SHAPE, "%s: hop pointers must be 16-byte aligned and hop_bytes a multiple of 16", fn);
+  return CA_OK;
+}
 
 static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides qs, const void* k, const void* v,
                                      ca_strides kvs, int dtype, int B, int H, int Sq, int Sk, int D,
@@ -133,20 +157,9 @@ static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides
   a.fold = fold;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hop.bytes > 0) {
-    // In the step's own launch when its last round leaves enough CUs free, else as a
-    // separate copy ahead of it on the same stream.
-    if (dtype == CA_BF16 &&
-        ctxattn::attn_bf16_idle_slots(B, H, Sq, Sk, mask, a.ws != nullptr) >= kHopWorkgroups) {
-      a.hop_sk = hop.sk; a.hop_sv = hop.sv; a.hop_dk = hop.dk; a.hop_dv = hop.dv;
-      a.hop_units = int64_t(hop.bytes / 16);
-      a.hop_wgs = kHopWorkgroups;
-    } else {
-      hipError_t e = ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, s);
-      if (e != hipSuccess) return hip_status(e, name);
-    }
-  }
-  hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
+  hipError_t e = attach_hop(a, hop, dtype, mask, s);
+  if (e != hipSuccess) return hip_status(e, name);
+  e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
   return hip_status(e, name);
 }
 
@@ -168,16 +181,10 @@ ca_status ring_attn_step_hop(const void* q, ca_strides qs, const void* k, const 
                              int B, int H, int Sq, int Sk, int D, float softmax_scale, int mask, float* o,
                              float* lse, void* workspace, size_t workspace_bytes, void* hop_dst_k, void* hop_dst_v,
                              const void* hop_src_k, const void* hop_src_v, size_t hop_bytes, void* stream) {
-  if (hop_bytes > 0) {
-    if (!hop_dst_k || !hop_dst_v || !hop_src_k || !hop_src_v)
-      return fail(CA_ERR_NULL, "ring_attn_step_hop: hop buffers are required when hop_bytes > 0");
-    if (hop_bytes % 16 || !aligned16(hop_dst_k) || !aligned16(hop_dst_v) || !aligned16(hop_src_k) ||
-        !aligned16(hop_src_v))
-      return fail(CA_ERR_SHAPE, "ring_attn_step_hop: hop pointers must be 16-byte aligned and hop_bytes a multiple of 16");
-  }
+  const Hop hop{hop_dst_k, hop_dst_v, hop_src_k, hop_src_v, hop_bytes};
+  CA_TRY(check_hop("ring_attn_step_hop", hop));
   return ring_attn_step_impl("ring_attn_step_hop launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale,
-                             mask, o, lse, workspace, workspace_bytes, stream, 0,
-                             Hop{hop_dst_k, hop_dst_v, hop_src_k, hop_src_v, hop_bytes});
+                             mask, o, lse, workspace, workspace_bytes, stream, 0, hop);
 }
 
 ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask, size_t* bytes) {
@@ -226,10 +233,14 @@ ca_status const_max_step_impl(const void* q, ca_strides qs, const void* k, const
                               int B, int H, int Sq, int Sk, int D, float softmax_scale, const float* c, float* acc,
                               int phase, void* o, int o_dtype, float* lse, void* workspace, size_t workspace_bytes,
                               const int32_t* sink_idx, const int32_t* sink_cnt, int sink_cap, int64_t key_offset,
-                              void* stream) {
+                              void* stream, Hop hop = Hop{}) {
   CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
   if (phase < 0 || phase > (CA_PHASE_INIT | CA_PHASE_FINAL)) return fail(CA_ERR_SHAPE, "unknown phase %d", phase);
-  if (int64_t(B) * H * Sq == 0) return hip_status(hipSuccess, "");
+  if (int64_t(B) * H * Sq == 0) {   // no rows: only the hop, if any
+    if (hop.bytes == 0) return hip_status(hipSuccess, "");
+    return hip_status(ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, static_cast<hipStream_t>(stream)),
+                      "ring_attn_const_max_step_hop");
+  }
   if (!c) return fail(CA_ERR_NULL, "the bound c is required");
   const bool init = phase & CA_PHASE_INIT, final_ = phase & CA_PHASE_FINAL;
   if (!(init && final_) && !acc) return fail(CA_ERR_NULL, "acc is required unless phase is INIT|FINAL");
@@ -252,7 +263,9 @@ ca_status const_max_step_impl(const void* q, ca_strides qs, const void* k, const
   a.sink_idx = sink_idx; a.sink_cnt = sink_cnt; a.sink_cap = sink_cap; a.key_offset = key_offset;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, s);
+  hipError_t e = attach_hop(a, hop, dtype, CA_MASK_NONE, s);
+  if (e != hipSuccess) return hip_status(e, "ring_attn_const_max_step launch");
+  e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, s);
   return hip_status(e, "ring_attn_const_max_step launch");
 }
 
@@ -266,6 +279,17 @@ ca_status ring_attn_const_max_step(const void* q, ca_strides qs, const void* k, 
                                    void* workspace, size_t workspace_bytes, void* stream) {
   return const_max_step_impl(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale, c, acc, phase, o, o_dtype, lse,
                              workspace, workspace_bytes, nullptr, nullptr, 0, 0, stream);
+}
+
+ca_status ring_attn_const_max_step_hop(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs,
+                                       int dtype, int B, int H, int Sq, int Sk, int D, float softmax_scale,
+                                       const float* c, float* acc, int phase, void* o, int o_dtype, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* hop_dst_k, void* hop_dst_v,
+                                       const void* hop_src_k, const void* hop_src_v, size_t hop_bytes, void* stream) {
+  const Hop hop{hop_dst_k, hop_dst_v, hop_src_k, hop_src_v, hop_bytes};
+  CA_TRY(check_hop("ring_attn_const_max_step_hop", hop));
+  return const_max_step_impl(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D, softmax_scale, c, acc, phase, o, o_dtype, lse,
+                             workspace, workspace_bytes, nullptr, nullptr, 0, 0, stream, hop);
 }
 
 ca_status ring_attn_const_max_step_sinks(const void* q, ca_strides qs, const void* k, const void* v,

@@ -91,7 +91,7 @@ class RingPass:
     against 0.90 ms unsplit on one stream, 0.94 ms split on one and 0.96 ms unsplit on two
     (timed with hops on the copy stream, before the split's regular cuts).
 
-    fused_hops=True (online, no fold): each step call carries the hop of the chunk two steps
+    fused_hops=True (no fold, no sinks): each step call carries the hop of the chunk two steps
     ahead (ring_attn_step_hop), on the CUs the step leaves free when there are any, instead of
     a copy stream. A step fills every CU's register file, so a copy kernel on its own stream
     runs only between steps; carried by the step it costs nothing there. On the Wan2.2 share
@@ -123,8 +123,8 @@ class RingPass:
         # buffers keep that true with two compute streams.
         self.fused_hops = bool(fused_hops)
         if self.fused_hops:
-            if variant != "online" or fold:
-                raise ValueError("fused hops apply to the online variant without fold")
+            if fold or sink_theta is not None:
+                raise ValueError("fused hops do not combine with fold or sinks")
             self.depth, self.nbuf = 2, 4
         B, Sq, H, D = q.shape
         chunk_shape = tuple(k_pool.shape[1:])
@@ -297,6 +297,8 @@ class RingPass:
         used and the two compute streams never wait on each other. Chunk 1 is moved by a
         plain copy ahead of step 1."""
         cp = self.cp
+        if self.variant == "constmax":
+            self.prologue()
         if self.aux_stream is not None:
             self.aux_stream.wait_stream(cs)
         streams = [self.aux_stream if (self.aux_stream is not None and s % 2 == 1) else cs for s in range(cp)]
@@ -311,9 +313,14 @@ class RingPass:
             with torch.cuda.stream(st):
                 if timing_events is not None:
                     timing_events[s][0].record(st)
-                if self.masks[s] is not None:
+                ws = self.ws[1 if st is not cs else 0]
+                if self.variant == "constmax":
+                    phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
+                    api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out, lse=self.lse,
+                                                 scale=self.scale, workspace=ws, hop=hop)
+                elif self.masks[s] is not None:
                     api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s], out=self.o_parts[slot],
-                                       lse=self.lse_parts[slot], workspace=self.ws[1 if st is not cs else 0], hop=hop)
+                                       lse=self.lse_parts[slot], workspace=ws, hop=hop)
                     slot += 1
                 elif hop is not None:
                     api.kv_chunk_copy(*hop)
@@ -321,7 +328,8 @@ class RingPass:
                     timing_events[s][1].record(st)
         if self.aux_stream is not None:
             cs.wait_stream(self.aux_stream)
-        api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
+        if self.variant == "online":
+            api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
         return self.out, self.lse
 
 

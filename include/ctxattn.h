@@ -236,6 +236,24 @@ ca_status ring_attn_const_max_step(const void* q, ca_strides q_strides,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ring_attn_const_max_step_hop -- ring_attn_const_max_step and, in the same call, the
+ * ring's next K/V hop, exactly as ring_attn_step_hop adds one to ring_attn_step (in the
+ * step's launch on the CUs its last round leaves free, else as a copy just ahead of it).
+ * Source: kernel reference page, Implementation, the ring loop.
+ * Arguments, layouts, support and errors: as ring_attn_const_max_step, plus the hop
+ * arguments of ring_attn_step_hop with the same requirements.
+ */
+ca_status ring_attn_const_max_step_hop(const void* q, ca_strides q_strides,
+                                       const void* k, const void* v, ca_strides kv_strides,
+                                       int dtype, int B, int H, int Sq, int Sk, int D,
+                                       float softmax_scale, const float* c, float* acc, int phase,
+                                       void* o, int o_dtype, float* lse,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* hop_dst_k, void* hop_dst_v,
+                                       const void* hop_src_k, const void* hop_src_v, size_t hop_bytes,
+                                       void* stream);
+
+/*
  * const_max_sink_prologue -- the bound prologue with sink keys taken out of the max.
  * Source: kernel reference page, "Adapting this kernel" (attention sinks: a handful of
  * keys whose norms dwarf the rest inflate max_j |k_j| for every row; excluding those keys

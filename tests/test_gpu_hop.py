@@ -96,3 +96,38 @@ def test_ring_fused_hops_matches_oracle(ca, wl_name, S, ranks, streams, H, layou
         allowed = oracle.causal_allowed(rows, np.arange(S)) if wl.causal else None
         ro, rl = oracle.attention_heads(t["q"][:, rows], t["k"], t["v"], scale, allowed=allowed)
         check(f"rank {r}", o, l, ro, rl)
+
+
+@pytest.mark.parametrize("phase", [1, 0, 2, 3])
+def test_const_max_step_hop_matches_step(ca, phase):
+    # 720p-like share scaled down: 4 heads x 1000 rows unsplit (CUs free: in the launch)
+    say(f"const-max step_hop phase={phase}")
+    q, k, v = _qkv(1, 1000, 900, 4, 720)
+    c = ca.api.const_max_bound(q, ca.api.key_sqnorm_max(k))
+    n = ca.api.const_max_acc_size(1, 4, 1000, 128)
+    acc0 = gen.normal((n,), 721, q.device, torch.float32).abs()
+    acc1 = acc0.clone()
+    r0 = ca.api.ring_attn_const_max_step(q, k, v, c, acc0, phase)
+    src_k = torch.randint(-2**31, 2**31 - 1, (300_001 * 4,), dtype=torch.int32, device=q.device)
+    src_v = torch.randint(-2**31, 2**31 - 1, (300_001 * 4,), dtype=torch.int32, device=q.device)
+    dst_k, dst_v = torch.zeros_like(src_k), torch.zeros_like(src_v)
+    r1 = ca.api.ring_attn_const_max_step(q, k, v, c, acc1, phase, hop=(dst_k, dst_v, src_k, src_v))
+    torch.cuda.synchronize()
+    assert torch.equal(dst_k, src_k) and torch.equal(dst_v, src_v), "hop bytes differ"
+    if phase & 2:
+        assert torch.equal(r0[0], r1[0]) and torch.equal(r0[1], r1[1])
+    if phase != 3:
+        assert torch.equal(acc0, acc1)
+
+
+def test_ring_const_max_fused_hops_matches_oracle(ca):
+    dev = torch.device("cuda:0")
+    wl = workloads.workload("wan22_720p_constmax").scaled(S=8 * 300, H=4)
+    t = gen.ring_inputs(wl, dev)
+    scale = oracle.default_scale(wl.D)
+    rows = oracle.contiguous_tokens(wl.S, wl.cp, 0)
+    say(f"const-max ring fused hops {wl.name} S={wl.S}")
+    o, l = ca.ring.ring_attention(t["q"], t["k"], t["v"], wl.cp, 0, variant="constmax", fused_hops=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_heads(t["q"][:, rows], t["k"], t["v"], scale)
+    check("rank 0", o, l, ro, rl)
