@@ -84,7 +84,9 @@ def test_wan22_720p_constmax_sinks_fullsize(ca):
 
 @pytest.mark.parametrize("variant", ["constmax", "online"])
 def test_wan22_720p_fullsize(ca, variant):
-    _ring_fullsize(ca, "wan22_720p_constmax", variant, 0, heads=(0, 21, 39), contiguous_q=True)
+    # the bench's launch configurations: const-max steps carry their hops, online ones do not
+    _ring_fullsize(ca, "wan22_720p_constmax", variant, 0, heads=(0, 21, 39), contiguous_q=True,
+                   fused_hops=(variant == "constmax"))
 
 
 @pytest.mark.parametrize("rank", [0, 3, 7])
