@@ -428,7 +428,11 @@ ca_status decode_launch(const char* name, const void* q, const void* k_pool, con
   if (!q || !o || !lse || (!local_lens && !prior_lens))
     return fail(CA_ERR_NULL, "q, o, lse and the sequence lengths are required");
   if (!local_lens && (!k_cur || !v_cur)) return fail(CA_ERR_NULL, "k_cur and v_cur are required");
-  if (max_blocks > 0 && num_blocks > 0 && (!k_pool || !v_pool || !block_table))
+  // an empty pool has no block to stand in for missing ones: a caller with no resident
+  // blocks passes max_blocks = 0
+  if (max_blocks > 0 && num_blocks == 0)
+    return fail(CA_ERR_SHAPE, "the block table has %d entries per sequence but the pool has no block", max_blocks);
+  if (max_blocks > 0 && (!k_pool || !v_pool || !block_table))
     return fail(CA_ERR_NULL, "k_pool, v_pool and block_table are required");
   if (!aligned16(q) || !aligned16(o) || (k_pool && !aligned16(k_pool)) || (v_pool && !aligned16(v_pool)) ||
       (k_cur && !aligned16(k_cur)) || (v_cur && !aligned16(v_cur)))

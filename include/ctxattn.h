@@ -100,8 +100,9 @@ typedef struct {
  *          be 256-byte aligned and all zero before its first use; every call leaves it
  *          ready for the next. Calls that may run at the same time need separate
  *          workspaces. Ignored by the fp32 path and by calls that do not split.
- * Supported: D in {64, 128} (fp32), D == 128 (bf16); MHA (same H for q and kv).
- * Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
+ * Supported: D in {64, 128} (fp32), D == 128 (bf16; the kernel reference page's
+ * Interface asserts d == 128 for this kernel, so bf16 D == 64 returns
+ * CA_ERR_UNSUPPORTED); MHA (same H for q and kv). Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
  * CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_WORKSPACE (too small), CA_ERR_HIP.
  */
 ca_status ring_attn_step(const void* q, ca_strides q_strides,
@@ -343,12 +344,20 @@ ca_status lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t
  *   k_pool       [num_blocks, Hkv, block_size, D] bf16: token-major blocks
  *   v_pool       [num_blocks, Hkv, D, block_size] bf16: d-major blocks (this
  *                library's V cache layout: each block's values stored transposed
- *                so that a block feeds the P.V matrix product without a shuffle)
+ *                so that a block feeds the P.V matrix product without a shuffle).
+ *                A cache kept token-major per block ([num_blocks, block_size, Hkv, D],
+ *                as paged-attention servers commonly hold it) is not read directly:
+ *                its writer stores each new token's K row at k_pool[blk, h, slot, :]
+ *                and its V row at v_pool[blk, h, :, slot] (a D-element scatter with
+ *                stride block_size), once per token at cache-write time; an existing
+ *                token-major cache is converted once by that same permutation.
  *   block_table  [B, max_blocks] int32: physical block of the sequence's shard-local
  *                block j (shard-local token t is slot t % block_size of block
  *                t / block_size); entries past the sequence's blocks are ignored;
  *                an id outside [0, num_blocks) reads as an all-zero block
- *   num_blocks   blocks in k_pool and v_pool
+ *   num_blocks   blocks in k_pool and v_pool; at least 1 when max_blocks > 0
+ *                (CA_ERR_SHAPE otherwise: an empty pool has no block to read, so a
+ *                caller with nothing resident passes max_blocks = 0)
  *   local_lens   [B] int32: tokens of each sequence resident on this shard
  *                (local_filled); values are clamped to [0, max_blocks * block_size]
  *   o            OUT [B, Hq, D] fp32 partial output; lse OUT [B, Hq] fp32

@@ -4,10 +4,23 @@ import sys
 
 import numpy as np
 
-# Tolerances against the fp64 oracle for bf16 inputs (and used for fp32 too):
-# max |dO| <= 2e-2, max |dLSE| <= 1e-3 (natural log).
+# Tolerances against the fp64 oracle for bf16 inputs: max |dO| <= 2e-2, max |dLSE| <= 1e-3
+# (natural log).
 TOL_O = 2e-2
 TOL_LSE = 1e-3
+# fp32 inputs (the fp32 path: fp32 products and sums, accurate exp and log). A score
+# s = scale * q.k over D <= 128 terms of unit-variance values carries at most about
+# D * 2^-24 * |q||k| * scale ~ 1e-4 of rounding in the worst case (|q||k| ~ D), typically
+# ~1e-6; the row sums of <= ~1000 terms add a relative ~1e-4 worst case. The bar sits at
+# the worst case, two orders of magnitude above the typical error, so a regression of the
+# fp32 path that the bf16 bar would hide still fails.
+TOL_O_F32 = 1e-4
+TOL_LSE_F32 = 1e-4
+
+
+def tol(dtype):
+    """(output bar, LSE bar) for an input dtype name ("bf16" or "fp32")."""
+    return (TOL_O_F32, TOL_LSE_F32) if dtype == "fp32" else (TOL_O, TOL_LSE)
 
 
 def say(msg):
@@ -32,10 +45,11 @@ def max_err(got, want):
     return float(np.abs(got[fin] - want[fin]).max())
 
 
-def check(name, o, lse, o_ref, lse_ref, tol_o=TOL_O, tol_lse=TOL_LSE):
+def check(name, o, lse, o_ref, lse_ref, tol_o=TOL_O, tol_lse=TOL_LSE, quiet=False):
     eo = max_err(o, o_ref)
     el = max_err(lse, lse_ref) if lse is not None else 0.0
-    say(f"  {name}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    if not quiet:
+        say(f"  {name}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
     assert eo <= tol_o, f"{name}: output error {eo} > {tol_o}"
     assert el <= tol_lse, f"{name}: LSE error {el} > {tol_lse}"
     return eo, el

@@ -1,22 +1,32 @@
 """HIP path vs the fp64 oracle at the workloads' full sizes, in the launch configuration the
-benchmark times (RingPass / DcpDecode with their defaults), on sampled output rows that the
-oracle computes one by one against the full key range.
+benchmark times (RingPass / DcpDecode with the benchmark's options).
 
-Rows are sampled per head with a fixed seed and always include the first rows, both sides of
-the 256-row query-tile edges, the ragged last tile and the last row; every sampled row is
-checked element by element."""
+Coverage, element by element against the oracle (the kernel reference page, "Adapting this
+kernel": validate against exact attention computed on the CPU):
+- Wan2.2 share (S = 32768, cp = 8, 10 heads): every row of every head of the pass;
+- 720p const-max (S = 75600, cp = 8, 40 heads): every row of heads 0 and 39, plus sampled
+  rows of every other head; the online pass on sampled rows;
+- striped causal S = 128k: every row of head 0 of rank 7, sampled rows of every head of
+  ranks 0, 3 and 7;
+- DCP decode (32 sequences, both shards): every sequence's shard partials and merged
+  result, with and without the current token;
+- DCP prefill chunk: sampled rows of three heads.
+Sampled rows always include the first rows, both sides of the 256-row query-tile edges,
+the ragged last tile and the last row."""
 
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gpu_util import check, say
+from gpu_util import check, say, to_np
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
+
+ROW_CHUNK = 1024   # oracle rows per call (bounds the causal mask's memory)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +42,9 @@ def _rows(n, seed, k=24):
     return gen.sample_rows(n, k, seed, include=(0, 1, 255, 256, last_tile - 1, last_tile, n - 2, n - 1))
 
 
-def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q, **ring_kw):
+def _ring_pass(ca, name, variant, rank, contiguous_q, **ring_kw):
+    """Runs one rank's ring pass as the benchmark does; returns the inputs (on the GPU),
+    the outputs (on the host) and the rank's global token positions."""
     wl = workloads.workload(name)
     dev = torch.device("cuda:0")
     say(f"full-size {name} variant={variant} rank={rank} S={wl.S} cp={wl.cp} H={wl.H} {ring_kw}")
@@ -45,56 +57,110 @@ def _ring_fullsize(ca, name, variant, rank, heads, contiguous_q, **ring_kw):
     rp = ca.ring.RingPass(q, kp, vp, rank, layout=wl.layout, causal=wl.causal, variant=variant, **ring_kw)
     o, lse = rp.run()
     torch.cuda.synchronize()
-    tok = (oracle.contiguous_tokens if wl.layout == "contiguous" else oracle.striped_tokens)(wl.S, wl.cp, rank)
-    scale = oracle.default_scale(wl.D)
-    for h in heads:
-        rows = _rows(wl.local_S, 17 * h + rank)
-        qh = oracle.to_f64(t["q"][0, tok[rows], h])
-        kh = oracle.to_f64(t["k"][0, :, h])
-        vh = oracle.to_f64(t["v"][0, :, h])
-        allowed = oracle.causal_allowed(tok[rows], np.arange(wl.S)) if wl.causal else None
-        ro, rl = oracle.attention(qh, kh, vh, scale, allowed)
-        check(f"{name} {variant} rank {rank} head {h} ({len(rows)} rows)", o[0, h, rows], lse[0, h, rows], ro, rl)
-    del t, q, kp, vp, rp
+    o, lse = o.cpu(), lse.cpu()
+    del q, kp, vp, rp
     torch.cuda.empty_cache()
+    tok = (oracle.contiguous_tokens if wl.layout == "contiguous" else oracle.striped_tokens)(wl.S, wl.cp, rank)
+    return wl, t, o, lse, tok
 
 
-def test_wan22_cp8_online_fullsize(ca):
-    # the headline's launch configuration: key-split steps alternating two compute streams,
-    # each carrying the hop of the chunk two steps ahead
-    _ring_fullsize(ca, "wan22_cp8_online", "online", 0, heads=(0, 4, 9), contiguous_q=False, split=True,
-                   compute_streams=2, fused_hops=True)
+def _check_head(label, wl, t, o, lse, tok, h, rows):
+    """Rows ``rows`` of head h against the oracle over the full key range."""
+    scale = oracle.default_scale(wl.D)
+    kh = oracle.to_f64(t["k"][0, :, h])
+    vh = oracle.to_f64(t["v"][0, :, h])
+    eo = el = 0.0
+    for r0 in range(0, len(rows), ROW_CHUNK):
+        rr = rows[r0:r0 + ROW_CHUNK]
+        qh = oracle.to_f64(t["q"][0, tok[rr], h])
+        allowed = oracle.causal_allowed(tok[rr], np.arange(wl.S)) if wl.causal else None
+        ro, rl = oracle.attention(qh, kh, vh, scale, allowed)
+        e = check(f"{label} head {h} rows {rr[0]}..{rr[-1]}", o[0, h, rr], lse[0, h, rr], ro, rl, quiet=True)
+        eo, el = max(eo, e[0]), max(el, e[1])
+    say(f"  {label} head {h} ({len(rows)} rows): max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    return eo, el
+
+
+def _summary(label, errs):
+    eo = max(e[0] for e in errs)
+    el = max(e[1] for e in errs)
+    say(f"{label}: max|dO|={eo:.3e} max|dLSE|={el:.3e} over {len(errs)} head checks")
+
+
+def test_wan22_cp8_online_fullsize_every_row(ca):
+    # the Wan2.2 share in its timed form: key-split steps alternating two compute streams,
+    # each carrying the hop of the chunk two steps ahead; every row of every head
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 0, False, split=True, compute_streams=2,
+                                    fused_hops=True)
+    errs = [_check_head("wan22 online rank 0", wl, t, o, lse, tok, h, np.arange(wl.local_S)) for h in range(wl.H)]
+    _summary("wan22_cp8_online every row", errs)
 
 
 def test_wan22_cp8_online_fullsize_copy_stream(ca):
     # the same with the hops on a copy stream
-    _ring_fullsize(ca, "wan22_cp8_online", "online", 3, heads=(1, 8), contiguous_q=False, split=True,
-                   compute_streams=2)
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 3, False, split=True, compute_streams=2)
+    errs = [_check_head("wan22 copy stream rank 3", wl, t, o, lse, tok, h, _rows(wl.local_S, 17 * h + 3))
+            for h in range(wl.H)]
+    _summary("wan22_cp8_online copy stream", errs)
 
 
 def test_wan22_cp8_online_fullsize_unsplit(ca):
-    _ring_fullsize(ca, "wan22_cp8_online", "online", 5, heads=(2, 7), contiguous_q=False)
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 5, False)
+    errs = [_check_head("wan22 unsplit rank 5", wl, t, o, lse, tok, h, _rows(wl.local_S, 17 * h + 5))
+            for h in (2, 7)]
+    _summary("wan22_cp8_online unsplit", errs)
+
+
+def test_wan22_720p_constmax_fullsize(ca):
+    # the timed const-max pass (steps carry their hops): every row of heads 0 and 39, and
+    # sampled rows of every other head
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_720p_constmax", "constmax", 0, True, fused_hops=True)
+    errs = [_check_head("720p constmax", wl, t, o, lse, tok, h, np.arange(wl.local_S)) for h in (0, wl.H - 1)]
+    errs += [_check_head("720p constmax", wl, t, o, lse, tok, h, _rows(wl.local_S, 17 * h)) for h in range(1, wl.H - 1)]
+    _summary("wan22_720p_constmax", errs)
+
+
+def test_wan22_720p_online_fullsize(ca):
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_720p_constmax", "online", 0, True)
+    errs = [_check_head("720p online", wl, t, o, lse, tok, h, _rows(wl.local_S, 19 * h)) for h in range(0, wl.H, 3)]
+    _summary("wan22_720p online", errs)
 
 
 def test_wan22_720p_constmax_sinks_fullsize(ca):
     """The sink-robust pass as timed (theta 4): exact attention is the target whether or not
     any key qualifies as a sink."""
-    _ring_fullsize(ca, "wan22_720p_constmax", "constmax", 0, heads=(0, 39), contiguous_q=True, sink_theta=4.0)
-
-
-@pytest.mark.parametrize("variant", ["constmax", "online"])
-def test_wan22_720p_fullsize(ca, variant):
-    # the bench's launch configurations: const-max steps carry their hops, online ones do not
-    _ring_fullsize(ca, "wan22_720p_constmax", variant, 0, heads=(0, 21, 39), contiguous_q=True,
-                   fused_hops=(variant == "constmax"))
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_720p_constmax", "constmax", 0, True, sink_theta=4.0)
+    errs = [_check_head("720p sinks", wl, t, o, lse, tok, h, _rows(wl.local_S, 23 * h)) for h in (0, 17, 39)]
+    _summary("wan22_720p sink-robust", errs)
 
 
 @pytest.mark.parametrize("rank", [0, 3, 7])
 def test_striped_causal_128k_fullsize(ca, rank):
-    _ring_fullsize(ca, "striped_causal_128k", "online", rank, heads=(0, 31), contiguous_q=True)
+    wl, t, o, lse, tok = _ring_pass(ca, "striped_causal_128k", "online", rank, True)
+    errs = []
+    if rank == 7:
+        errs.append(_check_head(f"striped rank {rank}", wl, t, o, lse, tok, 0, np.arange(wl.local_S)))
+    heads = range(1 if rank == 7 else 0, wl.H)
+    errs += [_check_head(f"striped rank {rank}", wl, t, o, lse, tok, h, _rows(wl.local_S, 29 * h + rank, k=8))
+             for h in heads]
+    _summary(f"striped_causal_128k rank {rank}", errs)
 
 
-def test_dcp_decode_fullsize(ca):
+def test_contiguous_causal_128k_fullsize(ca):
+    """The contiguous causal contrast the benchmark times: rank 6 (six full chunks, its own
+    triangle, one empty step) on sampled rows of four heads."""
+    wl, t, o, lse, tok = _ring_pass(ca, "contiguous_causal_128k", "online", 6, True)
+    errs = [_check_head("contiguous causal rank 6", wl, t, o, lse, tok, h, _rows(wl.local_S, 31 * h, k=16))
+            for h in (0, 11, 22, 31)]
+    _summary("contiguous causal 128k rank 6", errs)
+
+
+# ---------------------------------------------------------------- DCP decode, every sequence
+
+@pytest.fixture(scope="module")
+def decode_run(ca):
+    """Both shards' partials and the merged result of the timed decode step, with and
+    without the current token, copied to the host; the inputs stay on the GPU."""
     wl = workloads.workload("dcp_decode_gqa")
     dev = torch.device("cuda:0")
     say(f"full-size {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} shards={wl.shards}")
@@ -103,48 +169,64 @@ def test_dcp_decode_fullsize(ca):
                                        wl.interleave, wl.block_size, d["block_rand"]) for r in range(wl.shards)]
     run = ca.dcp.DcpDecode(d["q"], shards)
     o, lse = run.run()
-    torch.cuda.synchronize()
-    ctx = d["ctx"]
-    picks = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 13})
-    scale = oracle.default_scale(wl.D)
-    for b in picks:
-        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
-        kb, vb = d["k_seq"][s0:s1].cpu(), d["v_seq"][s0:s1].cpu()
-        for r in range(wl.shards):
-            po, pl = oracle.decode_shard_partial(d["q"][b].cpu(), kb, vb, r, wl.interleave, wl.shards, scale)
-            check(f"seq {b} (ctx {s1 - s0}) shard {r}", run.o_parts[r, b], run.lse_parts[r, b], po, pl)
-        fo, fl = oracle.decode_full(d["q"][b].cpu(), kb, vb, scale)
-        check(f"seq {b} (ctx {s1 - s0}) merged", o[b], lse[b], fo, fl)
-    del d, shards, run
-    torch.cuda.empty_cache()
-
-
-def test_dcp_decode_active_fullsize(ca):
-    """The decode leg with a current token, as timed: N resident tokens per sequence on the
-    shards plus the new token at position N on its owner shard; the merged result against
-    attention over all N + 1 tokens."""
-    wl = workloads.workload("dcp_decode_gqa")
-    dev = torch.device("cuda:0")
-    say(f"full-size {wl.name} with current token")
-    d = gen.decode_inputs(wl, dev)
-    shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], d["ctx"], r, wl.shards,
-                                       wl.interleave, wl.block_size, d["block_rand"]) for r in range(wl.shards)]
-    run = ca.dcp.DcpDecode(d["q"], shards)
+    res = {"o": o.cpu(), "lse": lse.cpu(), "o_parts": run.o_parts.cpu(), "lse_parts": run.lse_parts.cpu()}
     prior = torch.tensor([int(n) for n in d["ctx"]], dtype=torch.int32, device=dev)
     k_cur = gen.normal((wl.B, wl.Hkv, wl.D), 1000 * wl.seed + 21, dev, torch.bfloat16)
     v_cur = gen.normal((wl.B, wl.Hkv, wl.D), 1000 * wl.seed + 22, dev, torch.bfloat16)
-    o, lse = run.run_active(prior, k_cur, v_cur, wl.interleave)
+    oa, la = run.run_active(prior, k_cur, v_cur, wl.interleave)
+    res.update({"o_act": oa.cpu(), "lse_act": la.cpu(), "k_cur": k_cur.cpu(), "v_cur": v_cur.cpu()})
     torch.cuda.synchronize()
-    ctx = d["ctx"]
-    scale = oracle.default_scale(wl.D)
-    for b in sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 5}):
-        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
-        kb = torch.cat([d["k_seq"][s0:s1], k_cur[b:b + 1]]).cpu()
-        vb = torch.cat([d["v_seq"][s0:s1], v_cur[b:b + 1]]).cpu()
-        fo, fl = oracle.decode_full(d["q"][b].cpu(), kb, vb, scale)
-        check(f"seq {b} (ctx {s1 - s0} + current) merged", o[b], lse[b], fo, fl)
-    del d, shards, run
+    del shards, run
     torch.cuda.empty_cache()
+    res.update({"wl": wl, "d": d})
+    yield res
+    del res, d
+    torch.cuda.empty_cache()
+
+
+def _decode_group(q_rows, k_tok, v_tok, keep, scale):
+    """The query heads of one GQA group against the group's K/V head restricted to the
+    tokens ``keep`` selects (all when None): oracle attention, one row per query head."""
+    if keep is not None:
+        k_tok, v_tok = k_tok[keep], v_tok[keep]
+    return oracle.attention(q_rows, k_tok, v_tok, scale)
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_dcp_decode_fullsize_every_sequence(decode_run, part):
+    """Sequences 8*part .. 8*part+7: each shard's partial (the tokens the slot mapping deals
+    to it), the merged result (attention over all N tokens), and the merged result with the
+    current token at position N."""
+    wl, d = decode_run["wl"], decode_run["d"]
+    G = wl.Hq // wl.Hkv
+    scale = oracle.default_scale(wl.D)
+    worst = [0.0, 0.0]
+    for b in range(8 * part, 8 * part + 8):
+        s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
+        N = s1 - s0
+        shard = oracle.dcp_shard_of_position(np.arange(N), wl.interleave, wl.shards)
+        q_b = oracle.to_f64(d["q"][b])
+        for hk in range(wl.Hkv):
+            hs = slice(hk * G, (hk + 1) * G)
+            k_tok = oracle.to_f64(d["k_seq"][s0:s1, hk])
+            v_tok = oracle.to_f64(d["v_seq"][s0:s1, hk])
+            checks = []
+            for r in range(wl.shards):
+                po, pl = _decode_group(q_b[hs], k_tok, v_tok, shard == r, scale)
+                checks.append((f"seq {b} kv head {hk} shard {r}", decode_run["o_parts"][r, b, hs],
+                               decode_run["lse_parts"][r, b, hs], po, pl))
+            fo, fl = _decode_group(q_b[hs], k_tok, v_tok, None, scale)
+            checks.append((f"seq {b} kv head {hk} merged", decode_run["o"][b, hs], decode_run["lse"][b, hs], fo, fl))
+            k_all = np.concatenate([k_tok, oracle.to_f64(decode_run["k_cur"][b, hk])[None]])
+            v_all = np.concatenate([v_tok, oracle.to_f64(decode_run["v_cur"][b, hk])[None]])
+            ao, al = _decode_group(q_b[hs], k_all, v_all, None, scale)
+            checks.append((f"seq {b} kv head {hk} merged with current token", decode_run["o_act"][b, hs],
+                           decode_run["lse_act"][b, hs], ao, al))
+            for name, go, gl, ro, rl in checks:
+                e = check(name, go, gl, ro, rl, quiet=True)
+                worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+        say(f"  seq {b} (ctx {N}): checked; running max|dO|={worst[0]:.3e} max|dLSE|={worst[1]:.3e}")
+    say(f"dcp_decode_gqa sequences {8 * part}..{8 * part + 7}: max|dO|={worst[0]:.3e} max|dLSE|={worst[1]:.3e}")
 
 
 def test_dcp_prefill_fullsize(ca):

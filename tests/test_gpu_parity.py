@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL_LSE, TOL_O, check, max_err, say, to_np
+from gpu_util import TOL_LSE, TOL_O, check, max_err, say, to_np, tol
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -64,7 +64,7 @@ def test_step_partial_matches_oracle(dev, dtype, D, split, mask, Sq, Sk):
     torch.cuda.synchronize()
     scale = oracle.default_scale(D)
     ro, rl = oracle.attention_heads(q, k, v, scale, allowed=_allowed(mask, Sq, Sk))
-    check("step", o, l, ro, rl)
+    check("step", o, l, ro, rl, *tol(dtype))
     if mask == "causal_strict":
         assert np.all(to_np(l)[:, :, 0] == -np.inf) and np.all(to_np(o)[:, :, 0] == 0)
 
@@ -116,7 +116,7 @@ def test_step_fold_matches_attention_over_both_chunks(dev, dtype, D, split, m1, 
     k = torch.cat([k1, k2], dim=1)
     v = torch.cat([v1, v2], dim=1)
     ro, rl = oracle.attention_heads(q, k, v, scale, allowed=np.concatenate([a1, a2], axis=1))
-    check("fold", o, l, ro, rl)
+    check("fold", o, l, ro, rl, *tol(dtype))
     if m1 == "causal_strict" and m2 == "causal_strict":
         assert np.all(to_np(l)[:, :, 0] == -np.inf) and np.all(to_np(o)[:, :, 0] == 0)
 
@@ -200,8 +200,10 @@ def test_const_max_steps_match_oracle(dev, dtype, D, split, out_dtype):
     for h in range(H):
         ro[0, h], rl[0, h], _ = oracle.const_max(q[0, :, h], [x[0, :, h] for x in ks], [x[0, :, h] for x in vs], scale)
         eo_[0, h], el_[0, h] = oracle.attention(q[0, :, h], k[0, :, h], v[0, :, h], scale)
-    check("const-max vs oracle const_max", o, l, ro, rl)
-    check("const-max vs exact attention", o, l, eo_, el_)
+    # a bf16 output carries its own rounding (2^-9 relative): the bf16 bar on O then
+    bar_o = tol(dtype)[0] if out_dtype == "fp32" else TOL_O
+    check("const-max vs oracle const_max", o, l, ro, rl, bar_o, tol(dtype)[1])
+    check("const-max vs exact attention", o, l, eo_, el_, bar_o, tol(dtype)[1])
 
 
 def test_const_max_single_chunk_without_accumulator(dev):
@@ -287,7 +289,7 @@ def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=
         rows = (oracle.contiguous_tokens if layout == "contiguous" else oracle.striped_tokens)(S, wl.cp, r)
         allowed = oracle.causal_allowed(rows, S_all) if causal else None
         ro, rl = oracle.attention_heads(t["q"][:, rows], t["k"], t["v"], scale, allowed=allowed)
-        check(f"rank {r}", o, l, ro, rl)
+        check(f"rank {r}", o, l, ro, rl, *tol(wl.dtype))
 
 
 def test_tiny_fp32_ring_full_config(dev):
@@ -604,3 +606,32 @@ def test_const_max_sinks_over_cap_keeps_the_plain_bound(dev):
     s = ca.const_max_sink_prologue(kp, 4.0, sink_cap=3)
     torch.cuda.synchronize()
     assert sorted(s["sink_idx"][0, 0, :int(s["sink_cnt"][0, 0])].tolist()) == [5, 333, 610]
+
+
+def test_const_max_sinks_pass_is_repeatable(dev):
+    """Five passes of the sink-robust ring on the same inputs. The threshold's norm sum is
+    accumulated with float atomics, so a key within rounding of theta x mean could flip
+    between runs; the planted sinks (60-90x) and the ordinary keys (about 1x) sit far from
+    the threshold (4x), so every pass must select the same sorted lists, and with the same
+    lists the bound, the fold and the sink partial are the same launches on the same data:
+    identical outputs, bit for bit, each matching exact attention."""
+    ca = _ca()
+    sinks = [(5, 0, 60.0), (333, 0, 90.0), (610, 1, 75.0)]
+    q, k, v = _sink_ring_inputs(dev, sinks)
+    qs = ca.ring.shard(q, 4, 2, "contiguous")
+    kp = ca.ring.chunk_pool(k, 4, "contiguous")
+    vp = ca.ring.chunk_pool(v, 4, "contiguous")
+    ref_o, ref_l = oracle.attention_heads(qs, k, v, oracle.default_scale(128))
+    first = None
+    for p in range(5):
+        rp = ca.ring.RingPass(qs, kp, vp, 2, variant="constmax", sink_theta=4.0)
+        o, l = rp.run()
+        torch.cuda.synchronize()
+        lists = [sorted(rp.sinks["sink_idx"][0, h, :int(rp.sinks["sink_cnt"][0, h])].tolist()) for h in range(2)]
+        assert lists == [[5, 333], [610]], lists
+        cur = (o.clone(), l.clone())
+        if first is None:
+            first = cur
+            check("sink-robust pass 0 vs exact", o[0], l[0], ref_o[0], ref_l[0])
+        else:
+            assert torch.equal(cur[0], first[0]) and torch.equal(cur[1], first[1]), f"pass {p} differs"

@@ -86,6 +86,13 @@ WORKLOADS = {
         name="striped_causal_128k", B=1, H=32, D=128, S=131072, cp=8, dtype="bf16", seed=5,
         qk_norm=False, H_total=32, layout="striped", causal=True, ranks=tuple(range(8)),
         variants=("online",)),
+    # Contrast of the striped workload (not one of the five): the same causal attention with
+    # contiguous shards, where rank r sees r full chunks, its own triangle and cp - 1 - r empty
+    # steps, so the work per rank grows with r.
+    "contiguous_causal_128k": RingWorkload(
+        name="contiguous_causal_128k", B=1, H=32, D=128, S=131072, cp=8, dtype="bf16", seed=5,
+        qk_norm=False, H_total=32, layout="contiguous", causal=True, ranks=tuple(range(8)),
+        variants=("online",)),
 }
 
 
