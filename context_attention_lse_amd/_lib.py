@@ -26,6 +26,7 @@ EXPORTS = (
     "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error",
     "ca_version", "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
     "ring_attn_const_max_step_sinks", "sink_attention_partial", "sink_attention_workspace_size",
+    "dcp_decode_partial_noalloc",
 )
 
 
@@ -55,6 +56,7 @@ SIGNATURES = {
                                      _i, _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _sz, _vp],
     "lse_merge": [_i, _vp, _vp, _i64, _i, _vp, _i, _vp, _vp],
     "dcp_decode_partial": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp],
+    "dcp_decode_partial_noalloc": [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp],
     "dcp_decode_partial_active": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
                                   _vp, _vp, _sz, _vp],
     "dcp_decode_workspace_size": [_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],

@@ -315,6 +315,32 @@ def dcp_decode_partial(q, k_pool, v_pool, block_table, local_lens, scale=None, o
     return out, lse
 
 
+def dcp_decode_partial_noalloc(q, k_pool, v_pool, block_table, local_lens, scale=None, out=None, lse=None,
+                               stream=None):
+    """dcp_decode_partial without a workspace: the library's fixed per-GPU scratch holds the
+    split partials, and the C call allocates nothing (the outputs are allocated here only if
+    not given). Calls that may overlap in time on one GPU race on that scratch."""
+    _check_cuda(q, k_pool, v_pool, block_table, local_lens, out, lse)
+    B, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_pool.shape
+    if tuple(v_pool.shape) != (NB, Hkv, D, bs):
+        raise ValueError(f"v_pool must be [NB, Hkv, D, block_size], got {tuple(v_pool.shape)}")
+    for t in (q, k_pool, v_pool, block_table, local_lens):
+        if not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous")
+    if block_table.dtype != torch.int32 or local_lens.dtype != torch.int32:
+        raise TypeError("block_table and local_lens must be int32")
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise TypeError("decode q and pools must be bfloat16")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _lib.call("dcp_decode_partial_noalloc", _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(local_lens),
+              B, Hq, Hkv, D, bs, block_table.shape[1], NB, _scale(scale), _ptr(out), _ptr(lse), _stream(stream))
+    return out, lse
+
+
 def dcp_decode_partial_active(q, k_pool, v_pool, block_table, prior_lens, k_cur, v_cur, rank, world,
                               interleave=16, scale=None, out=None, lse=None, workspace=None, stream=None):
     """One DCP shard's decode step with the current token gated to its owner. q [B, Hq, D]

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -474,6 +475,66 @@ ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_po
   return decode_launch("dcp_decode_partial launch", q, k_pool, v_pool, block_table, local_lens, nullptr, nullptr,
                        nullptr, 0, 1, 1, B, Hq, Hkv, D, block_size, max_blocks, num_blocks, softmax_scale, o, lse,
                        workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of dcp_decode_partial_noalloc: the split partials that dcp_decode_partial keeps in
+// its caller's workspace. One copy per GPU the library runs on, held until the process ends.
+// In host code `scratch` is only a stand-in for the symbol: kernels and copies use the
+// device address that hipGetSymbolAddress gives for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(80) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device, looked up once per device (with that
+// device current) and kept.
+ca_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CA_ERR_UNSUPPORTED, "device %d outside the first %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ca_status dcp_decode_partial_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* local_lens, int B, int Hq, int Hkv,
+                                     int D, int block_size, int max_blocks, int num_blocks, float softmax_scale,
+                                     float* o, float* lse, void* stream) {
+  if (B > 0 && !local_lens) return fail(CA_ERR_NULL, "local_lens is required");
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (B > 0 && Hq > 0 && Hkv > 0 && D > 0 && block_size > 0 && max_blocks >= 0) {
+    const size_t need = ctxattn::decode_workspace_bytes(B, Hq, D, block_size, max_blocks);
+    if (need > kNoAllocScratchBytes)
+      return fail(CA_ERR_WORKSPACE,
+                  "dcp_decode_partial_noalloc: these sizes need %zu bytes of scratch, above its fixed %zu "
+                  "(B * Hq * ceil(max_blocks * block_size / 1024) * (D + 1) * 4 bytes); use dcp_decode_partial "
+                  "with a workspace", need, kNoAllocScratchBytes);
+    CA_TRY(scratch_of_current_device(&ws));
+    ws_bytes = kNoAllocScratchBytes;
+  }
+  return decode_launch("dcp_decode_partial_noalloc launch", q, k_pool, v_pool, block_table, local_lens, nullptr,
+                       nullptr, nullptr, 0, 1, 1, B, Hq, Hkv, D, block_size, max_blocks, num_blocks, softmax_scale, o,
+                       lse, ws, ws_bytes, stream);
 }
 
 ca_status dcp_decode_partial_active(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,

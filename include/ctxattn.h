@@ -372,6 +372,29 @@ ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_po
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dcp_decode_partial_noalloc -- dcp_decode_partial for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments, results and kernels as dcp_decode_partial, minus
+ * the workspace: the split partials go to a fixed scratch array of the library, 80 MiB on
+ * each GPU it runs on, allocated when the library's device code is loaded and held until
+ * the process ends. The call allocates nothing (no hipMalloc, no allocating library call).
+ *   Limit: B * Hq * ceil(max_blocks * block_size / 1024) * (D + 1) * 4 bytes must fit in
+ *   80 MiB (e.g. B = 32, Hq = 64, D = 128 allows max_blocks up to 5056 blocks of 16), else
+ *   CA_ERR_WORKSPACE with the sizes in the message.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap in time on one
+ *   GPU (different streams, or other threads) race and must be serialised by the caller;
+ *   calls in order on one stream are safe. Nothing in the scratch needs clearing between
+ *   calls (every split partial that a call reads, the call writes first).
+ * Errors: as dcp_decode_partial, with CA_ERR_WORKSPACE for sizes over the limit and
+ * CA_ERR_HIP if the scratch's device address cannot be found.
+ */
+ca_status dcp_decode_partial_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* local_lens,
+                                     int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                                     int num_blocks, float softmax_scale, float* o, float* lse,
+                                     void* stream);
+
+/*
  * dcp_decode_partial_active -- one DCP shard's decode step with the page's two-part
  * mask: the prior tokens this shard holds plus the current decode token, which only
  * the shard owning its position attends, so that the merged result counts it once.

@@ -73,6 +73,9 @@ def test_rejections_without_gpu():
     assert b"no block" in lib.ca_last_error()
     assert lib.dcp_decode_partial_active(_fake(), None, None, None, _fake(), _fake(), _fake(), 0, 2, 16, 2, 64, 8, 128,
                                          16, 8, 0, 0.0, _fake(), _fake(), _fake(), 1 << 30, None) == _lib.CA_ERR_SHAPE
+    # the no-allocation decode: sizes over its fixed scratch are refused before any device call
+    assert lib.dcp_decode_partial_noalloc(*args, 64, 64, 8, 128, 16, 8192, 100, 0.0, _fake(), _fake(), None) == _lib.CA_ERR_WORKSPACE
+    assert b"scratch" in lib.ca_last_error()
     n = ctypes.c_size_t(0)
     assert lib.dcp_decode_workspace_size(32, 64, 128, 16, 4096, ctypes.byref(n)) == _lib.CA_OK
     assert n.value == 32 * 64 * 64 * 129 * 4   # 64 splits of 1024 tokens
