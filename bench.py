@@ -3,8 +3,9 @@
 Headline (``value``): causal striped ring attention at S = 128k (32 heads of 128, cp = 8,
 token t on rank t mod 8, 16384 local tokens per rank). One step is every rank's ring
 pass run one after another on this GPU: per rank 8 online-max steps under the per-step
-causal mask of the striped layout, the K/V hops into rotating receive buffers on a copy
-stream, and the LSE merge of the rank's partials. value = algorithmic TFLOP/s of the
+causal mask of the striped layout, each merged by the LSE rule into the rank's running
+partial as it finishes (ring_attn_step_fold), with the K/V hops into rotating receive
+buffers on a copy stream. value = algorithmic TFLOP/s of the
 step, 4*H*D*(S(S+1)/2) flops (only the visible query-key pairs count), inputs resident in
 HBM when timing starts.
 
@@ -220,24 +221,36 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
     o = torch.empty((1, wl.H, n, wl.D), dtype=torch.float32, device=dev)
     lse = torch.empty((1, wl.H, n), dtype=torch.float32, device=dev)
     reps = 10
+    # in the pass, step 0 (the rank's own chunk) writes the running partial and every later
+    # step folds its partial into it (ring_attn_step_fold): the roofline times that form
     incl = lambda: ca.ring_attn_step(qs[7], kp[7], vp[7], mask="causal_incl", out=o, lse=lse)  # noqa: E731
+    incl_fold = lambda: ca.ring_attn_step(qs[7], kp[6], vp[6], mask="causal_incl", out=o, lse=lse,  # noqa: E731
+                                          fold=True)
     k_incl = timed(torch, incl, reps)
-    clk_incl = clock.measure(torch, incl)
+    incl()
+    k_fold = timed(torch, incl_fold, reps)
+    clk_incl = clock.measure(torch, incl_fold)
     fl_incl = causal_flops(wl.H, wl.D, n)
     out["roofline"] = kernel_roofline(
-        k_incl, fl_incl, "attn_step_bf16<0, 1, false> (ring_attn_step, mask causal_incl)",
+        k_fold, fl_incl, "attn_step_bf16<0, 1, false> (ring_attn_step_fold, mask causal_incl)",
         f"{fl_incl / 1e12:.4f} TFLOP = 4*H*D*Sq*(Sq+1)/2 visible pairs, H=32 Sq=Sk=16384 D=128",
-        key="attn_step_bf16/striped_causal_128k_incl",
-        note=f"mean of {reps} back-to-back launches on one stream (rank 7's queries against its own chunk)")
+        key="attn_step_bf16/striped_causal_128k_incl_fold",
+        note=f"mean of {reps} back-to-back launches on one stream: rank 7's queries against rank 6's chunk, "
+             "folded into the running partial as the pass does")
     out["roofline"]["clock_mhz"] = clk_incl
-    # rank 0's queries against rank 7's chunk: a STRICT step
-    k_strict = timed(torch, lambda: ca.ring_attn_step(qs[0], kp[7], vp[7], mask="causal_strict", out=o, lse=lse), reps)
+    # rank 0's queries against rank 7's chunk: a STRICT step, folded
+    incl()
+    k_strict = timed(torch, lambda: ca.ring_attn_step(qs[0], kp[7], vp[7], mask="causal_strict", out=o, lse=lse,
+                                                       fold=True), reps)
     del o, lse
 
     log("[bench] headline: every rank's ring pass")
     copy_stream = torch.cuda.Stream()
-    rps = [ca.ring.RingPass(qs[r], kp, vp, r, layout="striped", causal=True, copy_stream=copy_stream)
-           for r in range(wl.cp)]
+    # one compute stream folding each step into the running partial (no final merge), hops on a
+    # copy stream: 16.2-16.3 ms per rank against 16.5-16.6 with two compute streams and the
+    # 8-way merge (interleaved A/B, ranks 0 and 7)
+    rps = [ca.ring.RingPass(qs[r], kp, vp, r, layout="striped", causal=True, copy_stream=copy_stream, fold=True,
+                            compute_streams=1) for r in range(wl.cp)]
 
     def step():
         for rp in rps:
@@ -276,25 +289,22 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
     torch.cuda.synchronize()
     per_rank = [sum(ev[k][r][0].elapsed_time(ev[k][r][1]) for k in range(nrep)) / nrep for r in range(wl.cp)]
     mean = sum(per_rank) / len(per_rank)
-    # the merge of one rank's 8 partials, alone
-    rp0 = rps[0]
-    k_merge = timed(torch, lambda: ca.lse_merge(rp0.o_parts[:wl.cp], rp0.lse_parts[:wl.cp], out=rp0.out,
-                                                lse_out=rp0.lse), 5)
-    n_incl = sum(r + 1 for r in range(wl.cp))           # steps whose source rank <= the query rank
-    n_strict = wl.cp * wl.cp - n_incl
-    kernels_ms = n_incl * k_incl + n_strict * k_strict + wl.cp * k_merge
+    n_fold_incl = sum(r for r in range(wl.cp))           # folded steps whose source rank <= the query rank
+    n_strict = wl.cp * wl.cp - wl.cp - n_fold_incl
+    kernels_ms = wl.cp * k_incl + n_fold_incl * k_fold + n_strict * k_strict
     out.update({
         "ms": ms, "tflops": total / (ms * 1e-3) / 1e12, "flops": total, "clock_mhz": clk,
         "per_rank_ms": [round(x, 3) for x in per_rank],
         "rank_balance_max_over_mean": round(max(per_rank) / mean, 4),
         "ring_parallel_tflops": round(total / (wl.cp * max(per_rank) * 1e-3) / 1e12, 2),
-        "step_kernels": {"incl_ms": round(k_incl, 4), "strict_ms": round(k_strict, 4), "merge_ms": round(k_merge, 4),
-                         "incl_steps": n_incl, "strict_steps": n_strict,
+        "step_kernels": {"incl_ms": round(k_incl, 4), "incl_fold_ms": round(k_fold, 4),
+                         "strict_fold_ms": round(k_strict, 4), "incl_steps": wl.cp, "incl_fold_steps": n_fold_incl,
+                         "strict_fold_steps": n_strict,
                          "strict_tflops": round(causal_flops(wl.H, wl.D, n, True) / (k_strict * 1e-3) / 1e12, 2)},
         "exposed_ms": round(ms - kernels_ms, 3),
-        "exposed_note": ("step time minus the sum of its kernels timed alone (36 INCL + 28 STRICT steps, 8 merges): "
-                         "the hop copies and launch gaps the overlap of the two compute streams and the copy "
-                         "stream did not hide (negative: the streams overlapped the kernels' own tails)"),
+        "exposed_note": ("step time minus the sum of its kernels timed alone (8 INCL steps, 28 folded INCL and 28 "
+                         "folded STRICT steps): the hop copies on the copy stream and launch gaps that the steps "
+                         "did not hide"),
         "hop_bytes_per_step": int(2 * kp[0].numel() * kp.element_size() * (wl.cp - 1) * wl.cp),
     })
     # outputs kept for the parity check: rank, head, rows -> host copies taken in the cpu leg
@@ -658,7 +668,8 @@ def cpu_baseline_leg(h, kept, budget_s=12.0):
 def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
     """Back-to-back launches of one kernel on one stream with a workload's inputs (for a
     profiler run of that kernel alone); prints its roofline figures. Kernels:
-    incl, strict  the headline's step kernel under the INCL / STRICT mask (32 heads, 16384^2)
+    incl, strict  the headline's step kernel under the INCL / STRICT mask (32 heads, 16384^2),
+                  folding into a running partial as the pass does
     wan22         the Wan2.2 share's key-split step (10 heads, 4096^2)
     constmax      the 720p const-max step, accumulate phase (40 heads, 9450^2)
     online720     the 720p online step
@@ -679,7 +690,10 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
         o = torch.empty((1, wl.H, n, wl.D), dtype=torch.float32, device=dev)
         lse = torch.empty((1, wl.H, n), dtype=torch.float32, device=dev)
         mask = "causal_incl" if name == "incl" else "causal_strict"
-        fn = lambda: ca.ring_attn_step(q, kp[src], vp[src], mask=mask, out=o, lse=lse)  # noqa: E731
+        # the pass's form: the step's partial folded into the running one
+        ca.ring_attn_step(q, kp[r], vp[r], mask="causal_incl", out=o, lse=lse)
+        src = 6 if name == "incl" else 7
+        fn = lambda: ca.ring_attn_step(q, kp[src], vp[src], mask=mask, out=o, lse=lse, fold=True)  # noqa: E731
         work = causal_flops(wl.H, wl.D, n, strict=(name == "strict"))
         unit, per = "flop", f"4*H*D*visible pairs, H=32 Sq=Sk=16384 D=128, mask {mask}"
     elif name == "wan22":
@@ -812,7 +826,8 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "heads": wl.H, "head_dim": wl.D, "global_seq": wl.S,
                    "cp": wl.cp, "local_seq": wl.local_S, "layout": "striped", "causal": True,
                    "ranks_per_step": wl.cp, "ring_steps_per_rank": wl.cp, "flops_per_step": h["flops"]},
-        "step": "every rank's ring pass (8 steps with hops on a copy stream, LSE merge), ranks one after another",
+        "step": "every rank's ring pass (8 steps, each folded by the LSE rule into the running partial; hops on a "
+                "copy stream), ranks one after another",
         "frac_bf16_peak": round(h["tflops"] / PEAK_BF16_TFLOPS, 4),
         "roofline": h["roofline"],
         "clock_mhz": h["clock_mhz"],

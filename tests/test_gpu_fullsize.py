@@ -7,7 +7,7 @@ kernel": validate against exact attention computed on the CPU):
 - 720p const-max (S = 75600, cp = 8, 40 heads): every row of heads 0 and 39, plus sampled
   rows of every other head; the online pass on sampled rows;
 - striped causal S = 128k: every row of head 0 of rank 7, sampled rows of every head of
-  ranks 0, 3 and 7;
+  ranks 0, 3 and 7 (folded steps, as timed), and of four heads of rank 5 (merged partials);
 - DCP decode (32 sequences, both shards): every sequence's shard partials and merged
   result, with and without the current token;
 - DCP prefill chunk: sampled rows of three heads.
@@ -136,7 +136,9 @@ def test_wan22_720p_constmax_sinks_fullsize(ca):
 
 @pytest.mark.parametrize("rank", [0, 3, 7])
 def test_striped_causal_128k_fullsize(ca, rank):
-    wl, t, o, lse, tok = _ring_pass(ca, "striped_causal_128k", "online", rank, True)
+    # the timed form: one compute stream folding each step into the running partial, hops on
+    # a copy stream
+    wl, t, o, lse, tok = _ring_pass(ca, "striped_causal_128k", "online", rank, True, fold=True, compute_streams=1)
     errs = []
     if rank == 7:
         errs.append(_check_head(f"striped rank {rank}", wl, t, o, lse, tok, 0, np.arange(wl.local_S)))
@@ -144,6 +146,14 @@ def test_striped_causal_128k_fullsize(ca, rank):
     errs += [_check_head(f"striped rank {rank}", wl, t, o, lse, tok, h, _rows(wl.local_S, 29 * h + rank, k=8))
              for h in heads]
     _summary(f"striped_causal_128k rank {rank}", errs)
+
+
+def test_striped_causal_128k_fullsize_merged_partials(ca):
+    """The same ring with two compute streams and the 8-way merge of the steps' partials."""
+    wl, t, o, lse, tok = _ring_pass(ca, "striped_causal_128k", "online", 5, True)
+    errs = [_check_head("striped rank 5 merged", wl, t, o, lse, tok, h, _rows(wl.local_S, 37 * h, k=16))
+            for h in (0, 9, 18, 31)]
+    _summary("striped_causal_128k rank 5, merged partials", errs)
 
 
 def test_contiguous_causal_128k_fullsize(ca):
