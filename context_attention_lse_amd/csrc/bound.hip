@@ -31,13 +31,16 @@ __device__ __forceinline__ RowPiece<BF16> load_piece(const void* base, int64_t o
   RowPiece<BF16> r;
   r.a = floatx4{0.f, 0.f, 0.f, 0.f};
   r.b = r.a;
+  // Non-temporal loads: the rows are read once and streamed past the caches (the 774 MB key
+  // pool of the 720p ring: 171 us with ordinary loads, 154 us with these, bound kernel included)
   if (lane16 * 8 < D) {
     if (BF16) {
-      r.a = *reinterpret_cast<const floatx4*>(static_cast<const uint16_t*>(base) + off + lane16 * 8);
+      r.a = __builtin_nontemporal_load(
+          reinterpret_cast<const floatx4*>(static_cast<const uint16_t*>(base) + off + lane16 * 8));
     } else {
       const floatx4* p = reinterpret_cast<const floatx4*>(static_cast<const float*>(base) + off + lane16 * 8);
-      r.a = p[0];
-      r.b = p[1];
+      r.a = __builtin_nontemporal_load(p);
+      r.b = __builtin_nontemporal_load(p + 1);
     }
   }
   return r;
@@ -120,8 +123,9 @@ __global__ __launch_bounds__(NT) void key_sqnorm_max_kernel(const void* k, int64
 // grid: (ceil(Sq / TOK), B): c_i = sqrt(scale^2 * kmax_sq[b,h] * |q_i|^2). A workgroup
 // takes TOK consecutive tokens of every head: it reads their rows in memory order (token
 // major), keeps |q|^2 in LDS as [head][token], and writes c one head at a time, so the
-// [B, H, Sq] output goes out in runs of TOK consecutive floats.
-constexpr int TOK = 16;
+// [B, H, Sq] output goes out in runs of TOK consecutive floats. Eight tokens give the 720p
+// share 1182 workgroups, a fuller last round than 591 of sixteen.
+constexpr int TOK = 8;
 
 template <bool BF16>
 __global__ __launch_bounds__(NT) void const_max_bound_kernel(const void* q, int64_t sb, int64_t ss, int64_t sh,

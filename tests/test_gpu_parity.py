@@ -246,9 +246,12 @@ def test_const_max_sink_collapse_follows_the_clamp(dev):
     assert max_err(o[0, 0, : Sq // 2], eo[: Sq // 2]) <= TOL_O
 
 
-def test_lse_merge_matches_oracle(dev):
+@pytest.mark.parametrize("n,D", [(5, 128), (8, 128), (11, 128), (13, 64)])
+def test_lse_merge_matches_oracle(dev, n, D):
+    """n <= 8 takes the kernel's one-trip path (every load of a row in flight at once),
+    n > 8 the general one."""
     ca = _ca()
-    n, rows, D = 5, 1000, 128
+    rows = 1000
     g = torch.Generator().manual_seed(3)
     o = torch.randn((n, rows, D), generator=g)
     lse = torch.randn((n, rows), generator=g) * 4 + 2
