@@ -731,10 +731,16 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     }
 
     // ---- publish this segment's partial, count it; the last arrival combines all of them.
-    // Records move through agent-coherent accesses (relaxed agent-scope atomic stores and
-    // loads), so no L2 write-back or invalidation is needed: the stores have completed
-    // (vmcnt 0) before the counter moves, and the combiner loads only after it has seen the
-    // final count.
+    // Ordering. Every record byte moves through device-coherent accesses: the stores are
+    // written through to the device's coherence point (sc1, the form of a relaxed agent-scope
+    // atomic store) and the combiner's loads read from it (relaxed agent-scope atomic loads),
+    // so no cached copy of a record is ever read. The publisher waits for its stores to
+    // complete (vmcnt 0) before its counter increment, and the combiner issues its loads only
+    // after its own increment has returned the final count; the counter's increments are
+    // agent-scope atomics on one address, so they are totally ordered. Hence every record
+    // load follows every record store of the tile. A release/acquire pair would add a
+    // write-back and an invalidation of this XCD's whole L2 (buffer_wbl2, buffer_inv), which
+    // only data held in that cache needs.
     {
       const int64_t rec = segment_slot<MASK>(sp, nqb, nkt, logical, tile_start) * NW + w;
       float* po = sp.po + rec * (64 * 64) + lane * 4;
@@ -759,6 +765,9 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     ++ncomb;
   }
   if (!SPLIT) return;
+  // Compiler barrier: no record load below may be moved above the counter increments that
+  // selected the tiles (the loads are relaxed atomics, which the compiler could otherwise reorder).
+  asm volatile("" ::: "memory");
 
   // ---- combine the segments of the tiles this wave arrived at last, in key order
   // (deterministic sums). Done after the tile loop, so none of the loop's state is live here.
