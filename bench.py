@@ -61,18 +61,18 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/striped_causal_128k_incl": {"source": "attn_bf16.hip", "sha256": "82ac9e615e4caf61",
-                                                "fetch_kib": 479584.7, "write_kib": 267378.9},
-    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "82ac9e615e4caf61",
-                                        "fetch_kib": 58418.7, "write_kib": 64920.0},
-    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "82ac9e615e4caf61",
-                                           "fetch_kib": 332234.9, "write_kib": 190640.2},
-    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "2a888486a0688b34",
-                                  "fetch_kib": 2774911.0 + 22155.5, "write_kib": 47162.1 + 1040.0},
-    "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "499394719fe584c2",
-                                      "fetch_kib": 779643.0, "write_kib": 190476.9},
-    "const_max_bound/wan22_720p_constmax": {"source": "bound.hip", "sha256": "86b670ab1f950cb1",
-                                            "fetch_kib": 378048.4 + 47295.6, "write_kib": 160.0 + 2030.6},
+    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "e32bb24080a4d7c9",
+                                                     "fetch_kib": 609671.6, "write_kib": 265233.1},
+    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "e32bb24080a4d7c9",
+                                        "fetch_kib": 58632.6, "write_kib": 64920.0},
+    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "e32bb24080a4d7c9",
+                                           "fetch_kib": 332279.8, "write_kib": 190637.6},
+    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "490993acea1ee964",
+                                  "fetch_kib": 2775091.0 + 22155.5, "write_kib": 47439.2 + 1040.0},
+    "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
+                                      "fetch_kib": 779655.5, "write_kib": 190477.2},
+    "const_max_bound/wan22_720p_constmax": {"source": "bound.hip", "sha256": "5c362a4869e5af73",
+                                            "fetch_kib": 378047.6 + 47347.7, "write_kib": 160.0 + 2584.7},
 }
 
 

@@ -42,9 +42,15 @@ __device__ __forceinline__ void load_pair(PairRegs& r, const uint16_t* kp, const
     const uint16_t* kb = kp + ((blk * Hkv + hkv) * BS + c16) * D + 8 * g;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = *reinterpret_cast<const uint4*>(kb + 32 * cc);
+    // V rows stream past the caches (non-temporal): 2.9% faster per shard than ordinary loads;
+    // the same for K was 7% slower (interleaved A/B on the decode workload)
     const uint16_t* vb = vp + ((blk * Hkv + hkv) * D + c16) * BS + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) r.v[bi][db] = *reinterpret_cast<const uint2*>(vb + 16 * BS * db);
+    for (int db = 0; db < 8; ++db) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + 16 * BS * db));
+      r.v[bi][db] = make_uint2(t[0], t[1]);
+    }
   }
 }
 
