@@ -188,7 +188,7 @@ __device__ __forceinline__ float online_update(const floatx16& s, float sl2e, fl
   tmax = xor32_max(tmax);
   const float t2 = tmax * sl2e;
   const bool move = t2 > m_ref + kRescaleSlack;
-  if (__any(move)) {
+  if (__builtin_expect(__any(move), 0)) {   // rare once the first tiles are in
     const float m_new = move ? t2 : m_ref;
     const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
     l_part *= alpha;
@@ -546,16 +546,17 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     // keys of this (batch, head): the whole chunk, or its own count
     const int Skb = a.sk_of_bh ? min(Sk, max(a.sk_of_bh[bh], 0)) : Sk;
     if (!SPLIT) k1 = min(k1, (Skb + BK - 1) / BK);
-    // keys this lane's row may see, and the fewest any row of this wave may see
+    // keys this lane's row may see, and the fewest any row of this wave may see (wave-uniform:
+    // held in a scalar register, so the per-tile mask test is a scalar compare and branch)
     const int lane_lim = min(Skb, row_key_limit<MASK>(a, row));
-    const int wave_lim = min(Skb, row_key_limit<MASK>(a, row_w0));
+    const int wave_lim = __builtin_amdgcn_readfirstlane(min(Skb, row_key_limit<MASK>(a, row_w0)));
     const int nk = max(k1 - k0, 0);   // key tiles of this segment
     // sink keys to leave out: lane l holds this head's l-th sink as a chunk-local index
     int my_sink = INT_MIN;
     bool has_sinks = false;
     if (a.sink_idx != nullptr) {
       const int cnt = min(a.sink_cnt[bh], a.sink_cap);
-      has_sinks = cnt > 0;
+      has_sinks = __builtin_amdgcn_readfirstlane(cnt) > 0;
       if (lane < cnt) my_sink = int(a.sink_idx[int64_t(bh) * a.sink_cap + lane] - a.key_offset);
       settle(my_sink);
     }
@@ -582,7 +583,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       const char* kt = kbase + key0 * kss_bytes;
       const char* vt = vbase + key0 * kss_bytes;
       uint32_t ko = koff, vo = voff;
-      if (key0 + BK > Skb) {
+      if (__builtin_expect(key0 + BK > Skb, 0)) {   // the chunk's last tile only
         const int rr = max(0, min(crow, Skb - 1 - key0));
         ko = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ k_swz(crow)) << 4);
         vo = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ v_swz(crow)) << 4);
@@ -644,10 +645,14 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       }
     };
     // Softmax of the segment's tile j (scores in s): probabilities into p, row sum into l_part.
+    // The rare paths (masks, sinks, a moving maximum, the chunk's last tile in `issue`) are
+    // marked unlikely, so a full tile runs its vector phase without a taken branch: a taken
+    // branch costs the wave an instruction refetch, on the phase that sets the pace (8% of the
+    // cycles of a causal step).
     auto softmax = [&](int j) {
       const int key0 = (k0 + j) * BK;
-      if (key0 + BK > wave_lim) apply_mask(s, key0, hl, lane_lim);
-      if (has_sinks) {
+      if (__builtin_expect(key0 + BK > wave_lim, 0)) apply_mask(s, key0, hl, lane_lim);
+      if (__builtin_expect(has_sinks, 0)) {
         const uint64_t m = __ballot(my_sink >= key0 && my_sink < key0 + BK);
         if (m) mask_sinks(s, key0, hl, m, my_sink);
       }
