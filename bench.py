@@ -28,7 +28,9 @@ every workload's GPU outputs with the oracle and reports the errors as ``parity`
 the only part of this file that runs the oracle.
 
 ``clock_mhz`` per leg: the GPU's shader clock sampled through amdsmi while the leg's
-timed loop runs (null where amdsmi cannot read it).
+timed loop runs, with the socket power of the same window (``socket_power_w``; null where
+amdsmi cannot read them). The MFMA legs run at the board's power limit, so their clock is
+whatever that power allows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
                        [--only wan22,constmax,decode,prefill,tiny,contrast,copy]
@@ -122,11 +124,17 @@ class ClockSampler:
             self.handle, self.err = None, repr(e)[:120]
 
     def read(self):
+        """(shader clock in MHz, socket power in W or None)."""
         m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
         xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 65535]
-        if xs:
-            return sum(xs) / len(xs)
-        return float(m["current_gfxclk"])
+        clk = sum(xs) / len(xs) if xs else float(m["current_gfxclk"])
+        pw = None
+        for key in ("current_socket_power", "average_socket_power"):
+            v = m.get(key)
+            if isinstance(v, (int, float)) and 0 < v < 65535:
+                pw = float(v)
+                break
+        return clk, pw
 
     def __call__(self, fn):
         """Runs fn() while sampling every 5 ms; returns (fn's result, clock summary or None)."""
@@ -153,8 +161,11 @@ class ClockSampler:
         fresh = [x for i, x in enumerate(samples) if any(y != samples[0] for y in samples[:i + 1])]
         if not fresh:
             return res, None
-        return res, {"mean": round(sum(fresh) / len(fresh)), "min": round(min(fresh)), "max": round(max(fresh)),
-                     "readings": len(set(fresh))}
+        clks = [c for c, _ in fresh]
+        pws = [p for _, p in fresh if p is not None]
+        return res, {"mean": round(sum(clks) / len(clks)), "min": round(min(clks)), "max": round(max(clks)),
+                     "readings": len(set(fresh)),
+                     "socket_power_w": round(sum(pws) / len(pws)) if pws else None}
 
     def measure(self, torch, fn, min_s=1.3):
         """Repeats fn (GPU work on the current stream) for at least min_s and returns the
