@@ -57,18 +57,18 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch),
 # scaled by the plain-copy calibration: the copy kernel moving 2 GiB in and 2 GiB out read
-# FETCH_SIZE = 1048587 KiB and WRITE_SIZE = 2097204 KiB, so fetch x 2.0, write x 1.0
+# FETCH_SIZE = 1048597 KiB and WRITE_SIZE = 2097152 KiB, so fetch x 2.0, write x 1.0
 # (profiles/kv_copy__calibration.txt).
 # Each entry holds for the kernel source whose sha256 prefix it names; after an edit of that
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "e32bb24080a4d7c9",
-                                                     "fetch_kib": 609671.6, "write_kib": 265233.1},
-    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "e32bb24080a4d7c9",
-                                        "fetch_kib": 58632.6, "write_kib": 64920.0},
-    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "e32bb24080a4d7c9",
-                                           "fetch_kib": 332279.8, "write_kib": 190637.6},
+    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
+                                                     "fetch_kib": 613346.8, "write_kib": 265395.6},
+    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
+                                        "fetch_kib": 57099.05, "write_kib": 63000.0},
+    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
+                                           "fetch_kib": 331893.2, "write_kib": 190621.1},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "490993acea1ee964",
                                   "fetch_kib": 2775091.0 + 22155.5, "write_kib": 47439.2 + 1040.0},
     "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
