@@ -34,7 +34,7 @@ whatever that power allows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
                        [--only wan22,constmax,decode,prefill,tiny,contrast,copy]
-                       [--roofline-only [incl|strict|wan22|constmax|online720|merge|bound|decode|copy]]
+                       [--roofline-only [incl|strict|wan22|wan22split|constmax|online720|merge|bound|decode|copy]]
 
 Warm-up: W untimed steps, then more until the warm-up has kept the GPU busy for at least
 one second, so the clock has settled whatever W is (after a few tens of milliseconds of
@@ -65,8 +65,10 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
                                                      "fetch_kib": 613346.8, "write_kib": 265395.6},
-    "attn_step_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
-                                        "fetch_kib": 57099.05, "write_kib": 63000.0},
+    "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
+                                              "fetch_kib": 21608.0, "write_kib": 20654.8},
+    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
+                                                 "fetch_kib": 57099.1, "write_kib": 63000.0},
     "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
                                            "fetch_kib": 331893.2, "write_kib": 190621.1},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "490993acea1ee964",
@@ -326,6 +328,25 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
 
 # ------------------------------------------------------------------ workloads
 
+def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev):
+    """The Wan2.2 pass's step form without its hops and merge: unsplit steps over chunks
+    0..n-1, step s on compute stream s % 2, so two launches are in flight as in the pass.
+    Returns fn() (launches on the current stream's work order) and the launch count."""
+    cur = torch.cuda.current_stream()
+    aux = torch.cuda.Stream(device=dev)
+    outs = [(torch.empty(o_shape, dtype=torch.float32, device=dev),
+             torch.empty(o_shape[:-1], dtype=torch.float32, device=dev)) for _ in range(2)]
+
+    def fn():
+        aux.wait_stream(cur)
+        for s in range(n_steps):
+            st = cur if s % 2 == 0 else aux
+            with torch.cuda.stream(st):
+                ca.ring_attn_step(q, kp[s], vp[s], out=outs[s % 2][0], lse=outs[s % 2][1])
+        cur.wait_stream(aux)
+    return fn, n_steps
+
+
 def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     wl = workloads.workload("wan22_cp8_online")
     log(f"[bench] {wl.name}")
@@ -333,26 +354,39 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout)
     kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
-    # key-split steps on two compute streams, so one step's drain overlaps the next step's
-    # start; each step carries the hop of the chunk two steps ahead on the CUs it leaves free
-    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=True, compute_streams=2,
+    # unsplit steps, two in flight on two compute streams (160 query tiles each: one step
+    # alone leaves 96 of 256 CUs idle, two fill them); each step carries the hop of the
+    # chunk two steps ahead. Key-split steps (each alone fills the device) ran the pass 10%
+    # slower: their segments' partial stores and combines cost more than the overlap gives.
+    rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=False, compute_streams=2,
                           fused_hops=True)
     ms = timed(torch, rp.run, max(10, args.steps), warm_calls=max(10, args.warmup))
     clk = clock.measure(torch, rp.run)
-    o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
-    lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
-    k_ms = timed(torch, lambda: ca.ring_attn_step(q, kp[0], vp[0], out=o, lse=lse, workspace=rp.ws[0]), 30)
     fl_step = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D)
     fl = ring_flops(wl.H, wl.local_S, wl.S, wl.D)
+    pairs, n = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev)
+    p_ms = timed(torch, pairs, max(5, args.steps // 2)) / n
+    # the key-split form a single step uses (one launch at a time, filling the device)
+    ws = ca.step_workspace(q, kp[0])
+    o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
+    k_ms = timed(torch, lambda: ca.ring_attn_step(q, kp[0], vp[0], out=o, lse=lse, workspace=ws), 30)
     rp.run()
     return {"workload": wl.name, "config": "B=1 H=10 D=128 S=32768 cp=8 local=4096 bf16, QK RMS-normed, rank 0",
             "ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "clock_mhz": clk,
-            "form": "key-split steps on two compute streams, hops carried by the steps",
-            "roofline": kernel_roofline(k_ms, fl_step, "attn_step_bf16<0, 0, true> (ring_attn_step, key-split)",
+            "form": "unsplit steps, two in flight on two compute streams, hops carried by the steps, 8-way LSE merge",
+            "roofline": kernel_roofline(p_ms, fl_step,
+                                        "attn_step_bf16<0, 0, false> (ring_attn_step, two launches in flight)",
                                         f"{fl_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
-                                        key="attn_step_bf16/wan22_cp8_online",
-                                        note="mean of 30 back-to-back launches on one stream"),
+                                        key="attn_step_bf16/wan22_cp8_online_pairs",
+                                        note="effective time per launch: the pass's 8 steps without hops or merge, "
+                                             "alternating over two streams, total / 8"),
+            "keysplit_step": {"kernel_ms": round(k_ms, 4), "tflops": round(fl_step / (k_ms * 1e-3) / 1e12, 2),
+                              "frac_bf16_peak": round(fl_step / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "traffic": traffic("attn_step_bf16/wan22_cp8_online_keysplit"),
+                              "note": "attn_step_bf16<0, 0, true>: the same step cut into 240 key ranges with a "
+                                      "workspace (the form one step alone uses); mean of 30 back-to-back launches"},
             "_keep": {"wl": wl, "t": t, "out": rp.out, "lse": rp.lse}}
 
 
@@ -681,7 +715,10 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
     profiler run of that kernel alone); prints its roofline figures. Kernels:
     incl, strict  the headline's step kernel under the INCL / STRICT mask (32 heads, 16384^2),
                   folding into a running partial as the pass does
-    wan22         the Wan2.2 share's key-split step (10 heads, 4096^2)
+    wan22         the Wan2.2 share's unsplit step as its pass runs it: 8 launches (chunks 0..7)
+                  alternating over two streams, two in flight (10 heads, 4096^2); the figures
+                  are per launch (total / 8)
+    wan22split    the same step cut into key ranges (the form one step alone uses)
     constmax      the 720p const-max step, accumulate phase (40 heads, 9450^2)
     online720     the 720p online step
     merge         the 720p 8-way LSE merge (8 x 40 x 9450 rows of 128)
@@ -707,19 +744,24 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
         fn = lambda: ca.ring_attn_step(q, kp[src], vp[src], mask=mask, out=o, lse=lse, fold=True)  # noqa: E731
         work = causal_flops(wl.H, wl.D, n, strict=(name == "strict"))
         unit, per = "flop", f"4*H*D*visible pairs, H=32 Sq=Sk=16384 D=128, mask {mask}"
-    elif name == "wan22":
+    elif name in ("wan22", "wan22split"):
         wl = workloads.workload("wan22_cp8_online")
         t = gen.ring_inputs(wl, dev)
         q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout)
         kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
         vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
-        ws = ca.step_workspace(q, kp[0])
-        o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
-        lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
-        fn = lambda: ca.ring_attn_step(q, kp[0], vp[0], out=o, lse=lse, workspace=ws)  # noqa: E731
         work = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D)
-        unit, per = "flop", "4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128, key-split"
-        reps = 30
+        if name == "wan22":
+            fn, launches = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev)
+            unit, per = "flop", "4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128, unsplit, two launches in flight"
+            reps = 5
+        else:
+            ws = ca.step_workspace(q, kp[0])
+            o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
+            lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
+            fn = lambda: ca.ring_attn_step(q, kp[0], vp[0], out=o, lse=lse, workspace=ws)  # noqa: E731
+            unit, per = "flop", "4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128, key-split"
+            reps = 30
     elif name in ("constmax", "online720", "merge", "bound"):
         wl = workloads.workload("wan22_720p_constmax")
         t = gen.ring_inputs(wl, dev)
@@ -775,6 +817,8 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
     else:
         raise SystemExit(f"unknown kernel {name!r}")
     ms = timed(torch, fn, reps)
+    if name == "wan22":
+        ms /= launches
     rate = work / (ms * 1e-3)
     if unit == "flop":
         res = {"bound": "mfma", "achieved": round(rate / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -794,7 +838,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--roofline-only", nargs="?", const="incl", default=None,
-                    choices=["incl", "strict", "wan22", "constmax", "online720", "merge", "bound", "decode", "copy"],
+                    choices=["incl", "strict", "wan22", "wan22split", "constmax", "online720", "merge", "bound",
+                             "decode", "copy"],
                     help="time one kernel alone, back to back (for profiling it); default: the headline's "
                          "INCL step kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -88,12 +88,21 @@ def _summary(label, errs):
 
 
 def test_wan22_cp8_online_fullsize_every_row(ca):
-    # the Wan2.2 share in its timed form: key-split steps alternating two compute streams,
-    # each carrying the hop of the chunk two steps ahead; every row of every head
-    wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 0, False, split=True, compute_streams=2,
+    # the Wan2.2 share in its timed form: unsplit steps alternating two compute streams (two
+    # in flight), each carrying the hop of the chunk two steps ahead; every row of every head
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 0, False, split=False, compute_streams=2,
                                     fused_hops=True)
     errs = [_check_head("wan22 online rank 0", wl, t, o, lse, tok, h, np.arange(wl.local_S)) for h in range(wl.H)]
     _summary("wan22_cp8_online every row", errs)
+
+
+def test_wan22_cp8_online_fullsize_keysplit_every_row(ca):
+    # the same pass with key-split steps (240 key ranges per step: every query tile is cut in
+    # two segments combined through the workspace); every row of every head
+    wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 0, False, split=True, compute_streams=2,
+                                    fused_hops=True)
+    errs = [_check_head("wan22 key-split rank 0", wl, t, o, lse, tok, h, np.arange(wl.local_S)) for h in range(wl.H)]
+    _summary("wan22_cp8_online key-split every row", errs)
 
 
 def test_wan22_cp8_online_fullsize_copy_stream(ca):
