@@ -71,8 +71,8 @@ TRAFFIC = {
                                                  "fetch_kib": 57099.1, "write_kib": 63000.0},
     "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "b848ea300c246fbe",
                                            "fetch_kib": 331893.2, "write_kib": 190621.1},
-    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "490993acea1ee964",
-                                  "fetch_kib": 2775091.0 + 22155.5, "write_kib": 47439.2 + 1040.0},
+    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "974e5a7d3ee9555e",
+                                  "fetch_kib": 2778068.0 + 14927.25, "write_kib": 31631.46 + 1040.01},
     "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
                                       "fetch_kib": 779655.5, "write_kib": 190477.2},
     "const_max_bound/wan22_720p_constmax": {"source": "bound.hip", "sha256": "5c362a4869e5af73",

@@ -443,8 +443,9 @@ ca_status decode_launch(const char* name, const void* q, const void* k_pool, con
     return fail(CA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(CA_ERR_SHAPE, "workspace must be 16-byte aligned");
   const int64_t max_tokens = int64_t(max_blocks) * block_size;
-  const int max_splits = int((max_tokens + ctxattn::kDecodeSplitTokens - 1) / ctxattn::kDecodeSplitTokens);
-  if (max_splits > 65535) return fail(CA_ERR_UNSUPPORTED, "too many blocks per sequence");
+  const int64_t max_splits64 = ctxattn::decode_grid_splits(max_tokens);
+  if (max_splits64 > 65535) return fail(CA_ERR_UNSUPPORTED, "too many blocks per sequence");
+  const int max_splits = int(max_splits64);
   ctxattn::DecodeArgs a{};
   a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.block_table = block_table; a.local_lens = local_lens;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.max_blocks = max_blocks;

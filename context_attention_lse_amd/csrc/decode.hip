@@ -3,8 +3,9 @@
 // the local KV shard and produce a partial output with its LSE).
 //
 // Work decomposition (bandwidth-bound: every resident K/V byte is read once):
-//  * grid (split, kv head, sequence); a split is 1024 shard-local tokens (64 blocks);
-//  * a workgroup is 4 waves; wave w streams 16 blocks of the split, two blocks per step,
+//  * grid (split, kv head, sequence); a split is 1536 shard-local tokens (96 blocks), and
+//    the grid holds an odd number of splits so every split index spreads over all XCDs;
+//  * a workgroup is 4 waves; wave w streams 24 blocks of the split, two blocks per step,
 //    with the loads of the next two steps in flight (a ring of three register sets);
 //  * the GQA group's query heads (<= 16) share each K/V block: scores are
 //    S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (rows = 16 tokens, cols = heads), so
@@ -22,8 +23,9 @@ constexpr int D = 128;
 constexpr int BS = 16;                          // tokens per cache block
 constexpr int NT = 256;
 constexpr int WAVES = NT / 64;
-constexpr int SPLIT_BLOCKS = kDecodeSplitTokens / BS;   // 64
-constexpr int WAVE_BLOCKS = SPLIT_BLOCKS / WAVES;       // 16
+constexpr int SPLIT_BLOCKS = kDecodeSplitTokens / BS;   // 96
+constexpr int WAVE_BLOCKS = SPLIT_BLOCKS / WAVES;       // 24
+static_assert(WAVE_BLOCKS % 2 == 0 && WAVE_BLOCKS <= 32, "block pairs per wave; one mask bit per block");
 constexpr float kRescaleSlack = 8.0f;
 
 struct PairRegs {
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
 
 size_t decode_workspace_bytes(int B, int Hq, int D_, int block_size, int max_blocks) {
   const int64_t max_tokens = int64_t(max_blocks) * block_size;
-  const int64_t splits = (max_tokens + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
+  const int64_t splits = decode_grid_splits(max_tokens);
   const int64_t rows = int64_t(B) * Hq * (splits > 0 ? splits : 1);
   return size_t(rows) * (size_t(D_) + 1) * sizeof(float);
 }

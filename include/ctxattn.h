@@ -378,8 +378,9 @@ ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_po
  * the workspace: the split partials go to a fixed scratch array of the library, 80 MiB on
  * each GPU it runs on, allocated when the library's device code is loaded and held until
  * the process ends. The call allocates nothing (no hipMalloc, no allocating library call).
- *   Limit: B * Hq * ceil(max_blocks * block_size / 1024) * (D + 1) * 4 bytes must fit in
- *   80 MiB (e.g. B = 32, Hq = 64, D = 128 allows max_blocks up to 5056 blocks of 16), else
+ *   Limit: B * Hq * splits * (D + 1) * 4 bytes, splits = ceil(max_blocks * block_size /
+ *   1536) made odd (what dcp_decode_workspace_size reports), must fit in
+ *   80 MiB (e.g. B = 32, Hq = 64, D = 128 allows max_blocks up to 7584 blocks of 16), else
  *   CA_ERR_WORKSPACE with the sizes in the message.
  *   Every call on one GPU shares that GPU's scratch: calls that may overlap in time on one
  *   GPU (different streams, or other threads) race and must be serialised by the caller;

@@ -78,7 +78,7 @@ def test_rejections_without_gpu():
     assert b"scratch" in lib.ca_last_error()
     n = ctypes.c_size_t(0)
     assert lib.dcp_decode_workspace_size(32, 64, 128, 16, 4096, ctypes.byref(n)) == _lib.CA_OK
-    assert n.value == 32 * 64 * 64 * 129 * 4   # 64 splits of 1024 tokens
+    assert n.value == 32 * 64 * 43 * 129 * 4   # 43 splits of 1536 tokens (an odd count)
     # chunk copy: misaligned pointer, size not a multiple of 16, empty copy
     assert lib.kv_chunk_copy(_fake(0x1008), _fake(), _fake(), _fake(), 4096, None) == _lib.CA_ERR_SHAPE
     assert lib.kv_chunk_copy(_fake(), _fake(0x2000), _fake(0x3000), _fake(0x4000), 4100, None) == _lib.CA_ERR_SHAPE
