@@ -26,15 +26,18 @@
 //    patterns are bank-conflict free: K chunk c of row r sits at c ^ (r & 15), V chunk
 //    c at c ^ (4(r & 3) + 2((r >> 1) & 1));
 //  * scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each
-//    lane holds 16 scores of one query row: the row max needs one exchange between
-//    lanes l and l^32 per tile (v_permlane32_swap) and nothing else;
+//    lane holds 16 scores of one query row: a row max or sum needs one exchange between
+//    lanes l and l^32 (v_permlane32_swap) and nothing else;
 //  * O^T = V^T P^T takes P straight from the score registers (B operand); V stays in
 //    natural [key][d] order in LDS and ds_read_b64_tr_b16 transposes it on the read
 //    (within 16 lanes, lane i element t <- lane i/4 + 4t's element i%4), fetching the
 //    keys in exactly the order the score registers hold them;
-//  * softmax uses exp2 with scale*log2(e) folded into one FMA per score; the running max
-//    moves only when a tile's max exceeds it by more than 8 (log2 units), so the
-//    accumulator rescale is rare and probabilities stay <= 256;
+//  * softmax uses exp2 with scale*log2(e) folded into one FMA per score. The online mode
+//    keeps a lazy reference max: a tile is exponentiated against the reference as it
+//    stands, and only when a lane's share of the tile's row sum comes out above 2^20 (or
+//    while some row of the wave has no reference yet) does the wave find the tile's row
+//    maxima, move the reference, rescale its accumulators and redo the tile. A full tile
+//    thus runs no max reduction at all, and probabilities stay <= 2^20;
 //  * causal masks: a workgroup visits key tiles up to its last row's diagonal; tiles
 //    past a wave's own diagonal are masked in full (every probability is 0).
 //
@@ -70,7 +73,8 @@ constexpr int TILE = BK * ROW;            // bf16 per tile and tensor (8 KB)
 constexpr int TILE_BYTES = TILE * 2;
 constexpr int V_OFF = NBUF * TILE_BYTES;  // byte offset of the V buffers
 constexpr size_t LDS_BYTES = size_t(NBUF) * 2 * TILE_BYTES;
-constexpr float kRescaleSlack = 8.0f;
+// Lane tile sums above this (as fp32 bits: 2^20; inf is above it too) move the reference max.
+constexpr uint32_t kSumCapBits = 0x49800000u;
 static_assert(BK * D / 8 == NT, "one 16-byte copy per lane per tile and tensor");
 
 enum { MODE_ONLINE = 0, MODE_CONSTMAX = 1 };
@@ -156,10 +160,11 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const uint16_t* lds0, int off_el) 
 }
 
 // Softmax numerators of the 16 scores a lane holds: p = exp2(s*sl2e - mu), packed to bf16 in
-// P.V operand order (kc = 0: registers 0..7, kc = 1: registers 8..15). The row-sum share of
-// the lane adds the fp32 values: summing the bf16-rounded ones instead would leave an LSE
-// error up to 2^-9 on rows that see only one or two keys.
-__device__ __forceinline__ void exp_pack(const floatx16& s, float sl2e, float mu, bf16x8 (&pb)[2], float& lsum) {
+// P.V operand order (kc = 0: registers 0..7, kc = 1: registers 8..15); returns the lane's
+// share of the tile's row sum. The sum adds the fp32 values: summing the bf16-rounded ones
+// instead would leave an LSE error up to 2^-9 on rows that see only one or two keys.
+__device__ __forceinline__ float exp_pack(const floatx16& s, float sl2e, float mu, bf16x8 (&pb)[2]) {
+  float pair[8];
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
     uint32_t w[4];
@@ -169,16 +174,18 @@ __device__ __forceinline__ void exp_pack(const floatx16& s, float sl2e, float mu
       const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sl2e, -mu));
       const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], sl2e, -mu));
       w[t] = pack_bf16x2(x0, x1);
-      lsum += x0 + x1;
+      pair[kc * 4 + t] = x0 + x1;
     }
     uint4 u = make_uint4(w[0], w[1], w[2], w[3]);
     pb[kc] = *reinterpret_cast<bf16x8*>(&u);
   }
+  return ((pair[0] + pair[1]) + (pair[2] + pair[3])) + ((pair[4] + pair[5]) + (pair[6] + pair[7]));
 }
 
-// Online-max bookkeeping for one tile; returns the exp2 offset mu.
-__device__ __forceinline__ float online_update(const floatx16& s, float sl2e, float& m_ref, float& l_part,
-                                               floatx16 (&o)[4]) {
+// Moves the online reference max to the running max of each row (the tile's row max if
+// that is larger) and rescales the row's accumulators to it.
+__device__ __forceinline__ void online_rebase(const floatx16& s, float sl2e, float& m_ref, float& l_part,
+                                              floatx16 (&o)[4]) {
   // a three-level tree of 3-input maxima (v_max3_f32; this file builds without NaN
   // semantics, so no canonicalising moves precede them)
   const float a0 = fmaxf(fmaxf(s[0], s[1]), s[2]), a1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
@@ -186,19 +193,14 @@ __device__ __forceinline__ float online_update(const floatx16& s, float sl2e, fl
   const float a4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
   float tmax = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), s[15]));
   tmax = xor32_max(tmax);
-  const float t2 = tmax * sl2e;
-  const bool move = t2 > m_ref + kRescaleSlack;
-  if (__builtin_expect(__any(move), 0)) {   // rare once the first tiles are in
-    const float m_new = move ? t2 : m_ref;
-    const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
-    l_part *= alpha;
+  const float m_new = fmaxf(m_ref, tmax * sl2e);
+  const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);   // -inf -> finite: 0
+  l_part *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    m_ref = m_new;
-  }
-  return (m_ref == -INFINITY) ? 0.0f : m_ref;
+    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+  m_ref = m_new;
 }
 
 // Keys a query row may see: every key j < row_key_limit(row) of the chunk (and j < Sk).
@@ -567,7 +569,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
 
-    float m_ref = -INFINITY;   // running reference max (log2 units), online mode
+    float m_ref = -INFINITY;   // reference max (log2 units), online mode
+    bool fresh = true;         // some row of this wave has no reference max yet (wave-uniform)
     float l_part = 0.0f;       // this lane's share of the row sum
     float c2 = 0.0f;           // const-max bound in log2 units
     if (MODE == MODE_CONSTMAX) {
@@ -656,10 +659,22 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
         const uint64_t m = __ballot(my_sink >= key0 && my_sink < key0 + BK);
         if (m) mask_sinks(s, key0, hl, m, my_sink);
       }
-      float mu;
-      if (MODE == MODE_ONLINE) mu = online_update(s, sl2e, m_ref, l_part, o);
-      else mu = c2;
-      exp_pack(s, sl2e, mu, p, l_part);
+      if (MODE == MODE_ONLINE) {
+        float t = 0.0f;
+        bool redo = fresh;
+        if (__builtin_expect(!fresh, 1)) {
+          t = exp_pack(s, sl2e, m_ref, p);
+          redo = __any(__float_as_uint(t) > kSumCapBits);   // t >= 0, or +inf
+        }
+        if (__builtin_expect(redo, 0)) {   // the first tiles, and a max that jumps by ~20
+          online_rebase(s, sl2e, m_ref, l_part, o);
+          fresh = __any(m_ref == -INFINITY);
+          t = exp_pack(s, sl2e, m_ref == -INFINITY ? 0.0f : m_ref, p);
+        }
+        l_part += t;
+      } else {
+        l_part += exp_pack(s, sl2e, c2, p);
+      }
     };
     // One tile j of the segment (buffer BUF = j % NBUF), in two phases.
     //  vector phase: start the copies of tile j + NBUF - 1 into the buffer tile j - 1 used,
