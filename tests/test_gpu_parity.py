@@ -69,6 +69,49 @@ def test_step_partial_matches_oracle(dev, dtype, D, split, mask, Sq, Sk):
         assert np.all(to_np(l)[:, :, 0] == -np.inf) and np.all(to_np(o)[:, :, 0] == 0)
 
 
+def _key_gain(pattern, Sk):
+    """Per-key factors on K that make the row maxima jump between key tiles (32 keys)."""
+    f = np.ones(Sk, np.float32)
+    if pattern == "rise":        # maxima up by ~8x then ~4x more, mid-tile both times
+        f[100:] = 8.0
+        f[613:] = 30.0
+    elif pattern == "fall":      # the largest scores in the first tile, small ones after
+        f[:32] = 30.0
+    elif pattern == "spike":     # one key far above the rest, late in the chunk
+        f[777 % Sk] = 60.0
+    return f
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("mask,Sq,Sk", [("none", 300, 1003), ("causal_incl", 1000, 1000)])
+@pytest.mark.parametrize("pattern", ["rise", "fall", "spike"])
+def test_step_reference_max_moves(dev, pattern, mask, Sq, Sk, split):
+    """Scores whose row maxima jump by far more than the lazy reference max tolerates
+    (a lane's tile sum above 2^20, i.e. a jump above ~14 in natural-log units) after the
+    first tiles, in the middle of a tile, or only in the first tile: the kernel moves its
+    reference, rescales and redoes the tile, and the result is still exact attention."""
+    ca = _ca()
+    B, H, D = 1, 3, 128
+    say(f"reference max pattern={pattern} mask={mask} Sq={Sq} Sk={Sk} split={split}")
+    q, _, _ = _inputs(dev, B, Sq, H, D, "bf16", 610)
+    _, k, v = _inputs(dev, B, Sk, H, D, "bf16", 620)
+    gain = torch.tensor(_key_gain(pattern, Sk), device=dev)
+    k = (k.float() * gain[None, :, None, None]).to(torch.bfloat16)
+    v = v.contiguous()   # K and V share strides
+    scale = oracle.default_scale(D)
+    # the inputs do force the rare path: some row's max over keys past the first tile is
+    # more than 14 above its max over the first tile (or, for "fall", far below it)
+    sc = torch.einsum("bqhd,bkhd->bhqk", q.float().cpu(), k.float().cpu()).numpy() * scale
+    first, rest = sc[..., :32].max(-1), sc[..., 32:].max(-1)
+    jump = (rest - first) if pattern != "fall" else (first - rest)
+    assert jump.max() > 14.0
+    ws = ca.step_workspace(q, k, mask) if split else None
+    o, l = ca.ring_attn_step(q, k, v, mask=mask, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_heads(q, k, v, scale, allowed=_allowed(mask, Sq, Sk))
+    check("reference max", o, l, ro, rl)
+
+
 @pytest.mark.parametrize("mask", ["none", "causal_incl", "causal_strict"])
 def test_split_step_is_deterministic_and_leaves_workspace_ready(dev, mask):
     """Split tiles are combined in key order, so repeated calls give identical bits, and
