@@ -63,13 +63,13 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "5fc3744a3a84d0db",
+    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                                      "fetch_kib": 611376.1, "write_kib": 265399.2},
-    "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "5fc3744a3a84d0db",
+    "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                               "fetch_kib": 21622.0, "write_kib": 20648.7},
-    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "5fc3744a3a84d0db",
+    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                                  "fetch_kib": 57381.9, "write_kib": 63000.0},
-    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "5fc3744a3a84d0db",
+    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                            "fetch_kib": 331822.8, "write_kib": 190624.0},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "974e5a7d3ee9555e",
                                   "fetch_kib": 2778068.0 + 14927.25, "write_kib": 31631.46 + 1040.01},

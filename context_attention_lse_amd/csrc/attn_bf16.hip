@@ -182,8 +182,8 @@ __device__ __forceinline__ float exp_pack(const floatx16& s, float sl2e, float m
   return ((pair[0] + pair[1]) + (pair[2] + pair[3])) + ((pair[4] + pair[5]) + (pair[6] + pair[7]));
 }
 
-// Moves the online reference max to the running max of each row (the tile's row max if
-// that is larger) and rescales the row's accumulators to it.
+// Raises each row's online reference max to the tile's row max where that is larger and
+// rescales the row's accumulators to the new reference.
 __device__ __forceinline__ void online_rebase(const floatx16& s, float sl2e, float& m_ref, float& l_part,
                                               floatx16 (&o)[4]) {
   // a three-level tree of 3-input maxima (v_max3_f32; this file builds without NaN
@@ -666,7 +666,7 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
           t = exp_pack(s, sl2e, m_ref, p);
           redo = __any(__float_as_uint(t) > kSumCapBits);   // t >= 0, or +inf
         }
-        if (__builtin_expect(redo, 0)) {   // the first tiles, and a max that jumps by ~20
+        if (__builtin_expect(redo, 0)) {   // the first tiles; a max up by ~20 in log2 units
           online_rebase(s, sl2e, m_ref, l_part, o);
           fresh = __any(m_ref == -INFINITY);
           t = exp_pack(s, sl2e, m_ref == -INFINITY ? 0.0f : m_ref, p);
