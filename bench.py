@@ -66,7 +66,7 @@ TRAFFIC = {
     "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                                      "fetch_kib": 611376.1, "write_kib": 265399.2},
     "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
-                                              "fetch_kib": 21622.0, "write_kib": 20648.7},
+                                              "fetch_kib": 29363.9, "write_kib": 20642.0},
     "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                                  "fetch_kib": 57381.9, "write_kib": 63000.0},
     "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
@@ -330,7 +330,8 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
 
 def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev):
     """The Wan2.2 pass's step form without its hops and merge: unsplit steps over chunks
-    0..n-1, step s on compute stream s % 2, so two launches are in flight as in the pass.
+    0..n-1, step s on compute stream s % 2, so two launches are in flight as in the pass,
+    each stream's steps after its first folding into its running partial.
     Returns fn() (launches on the current stream's work order) and the launch count."""
     cur = torch.cuda.current_stream()
     aux = torch.cuda.Stream(device=dev)
@@ -342,7 +343,7 @@ def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev):
         for s in range(n_steps):
             st = cur if s % 2 == 0 else aux
             with torch.cuda.stream(st):
-                ca.ring_attn_step(q, kp[s], vp[s], out=outs[s % 2][0], lse=outs[s % 2][1])
+                ca.ring_attn_step(q, kp[s], vp[s], out=outs[s % 2][0], lse=outs[s % 2][1], fold=s >= 2)
         cur.wait_stream(aux)
     return fn, n_steps
 
@@ -356,10 +357,12 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
     # unsplit steps, two in flight on two compute streams (160 query tiles each: one step
     # alone leaves 96 of 256 CUs idle, two fill them); each step carries the hop of the
-    # chunk two steps ahead. Key-split steps (each alone fills the device) ran the pass 10%
-    # slower: their segments' partial stores and combines cost more than the overlap gives.
+    # chunk two steps ahead and folds into its stream's running partial (a 2-way merge at
+    # the end instead of an 8-way one). Key-split steps (each alone fills the device) ran the
+    # pass 10% slower: their segments' partial stores and combines cost more than the
+    # overlap gives.
     rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=False, compute_streams=2,
-                          fused_hops=True)
+                          fused_hops=True, fold=True)
     ms = timed(torch, rp.run, max(10, args.steps), warm_calls=max(10, args.warmup))
     clk = clock.measure(torch, rp.run)
     fl_step = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D)
@@ -375,13 +378,14 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     return {"workload": wl.name, "config": "B=1 H=10 D=128 S=32768 cp=8 local=4096 bf16, QK RMS-normed, rank 0",
             "ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "clock_mhz": clk,
-            "form": "unsplit steps, two in flight on two compute streams, hops carried by the steps, 8-way LSE merge",
+            "form": "unsplit steps, two in flight on two compute streams, hops carried by the steps, each stream "
+                    "folding into a running partial, 2-way LSE merge",
             "roofline": kernel_roofline(p_ms, fl_step,
-                                        "attn_step_bf16<0, 0, false> (ring_attn_step, two launches in flight)",
+                                        "attn_step_bf16<0, 0, false> (ring_attn_step_fold, two launches in flight)",
                                         f"{fl_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
                                         key="attn_step_bf16/wan22_cp8_online_pairs",
                                         note="effective time per launch: the pass's 8 steps without hops or merge, "
-                                             "alternating over two streams, total / 8"),
+                                             "alternating over two streams and folding, total / 8"),
             "keysplit_step": {"kernel_ms": round(k_ms, 4), "tflops": round(fl_step / (k_ms * 1e-3) / 1e12, 2),
                               "frac_bf16_peak": round(fl_step / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "traffic": traffic("attn_step_bf16/wan22_cp8_online_keysplit"),
@@ -716,8 +720,8 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
     incl, strict  the headline's step kernel under the INCL / STRICT mask (32 heads, 16384^2),
                   folding into a running partial as the pass does
     wan22         the Wan2.2 share's unsplit step as its pass runs it: 8 launches (chunks 0..7)
-                  alternating over two streams, two in flight (10 heads, 4096^2); the figures
-                  are per launch (total / 8)
+                  alternating over two streams, two in flight, each stream's later steps
+                  folding (10 heads, 4096^2); the figures are per launch (total / 8)
     wan22split    the same step cut into key ranges (the form one step alone uses)
     constmax      the 720p const-max step, accumulate phase (40 heads, 9450^2)
     online720     the 720p online step

@@ -22,7 +22,7 @@ STATUS_NAMES = {
 
 # Every symbol include/ctxattn.h declares.
 EXPORTS = (
-    "ring_attn_step", "ring_attn_step_fold", "ring_attn_step_hop", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "ring_attn_const_max_step_hop", "lse_merge",
+    "ring_attn_step", "ring_attn_step_fold", "ring_attn_step_hop", "ring_attn_step_fold_hop", "ring_attn_workspace_size", "key_sqnorm_max", "const_max_bound", "ring_attn_const_max_step", "ring_attn_const_max_step_hop", "lse_merge",
     "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error",
     "ca_version", "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
     "ring_attn_const_max_step_sinks", "sink_attention_partial", "sink_attention_workspace_size",
@@ -47,6 +47,8 @@ SIGNATURES = {
                             _sz, _vp],
     "ring_attn_step_hop": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp,
                            _sz, _vp, _vp, _vp, _vp, _sz, _vp],
+    "ring_attn_step_fold_hop": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
+                                _vp, _sz, _vp, _vp, _vp, _vp, _sz, _vp],
     "ring_attn_workspace_size": [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
     "key_sqnorm_max": [_vp, ca_strides, _i, _i, _i, _i, _i, _vp, _i, _vp],
     "const_max_bound": [_vp, ca_strides, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp],

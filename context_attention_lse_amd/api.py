@@ -97,11 +97,9 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspa
     ``fold``, ``out`` and ``lse`` (required) hold a prior partial of the same rows and
     receive its LSE merge with this chunk's partial (ring_attn_step_fold). ``hop`` =
     (dst_k, dst_v, src_k, src_v), contiguous buffers of one size: the ring's next K/V hop,
-    copied by the same call (ring_attn_step_hop; not with ``fold``)."""
+    copied by the same call (ring_attn_step_hop, or ring_attn_step_fold_hop with ``fold``)."""
     _check_cuda(q, k, v, out, lse, workspace)
     if hop is not None:
-        if fold:
-            raise ValueError("hop and fold do not combine")
         nbytes = _hop_bytes(hop)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
@@ -124,7 +122,8 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspa
     args = (_ptr(q), _strides(q), _ptr(k), _ptr(v), _strides(k), _dtype_code(q), B, H, Sq, Sk, D, _scale(scale),
             MASKS[mask] if isinstance(mask, str) else int(mask), _ptr(out), _ptr(lse), *_ws(workspace))
     if hop is not None:
-        _lib.call("ring_attn_step_hop", *args, *(_ptr(t) for t in hop), nbytes, _stream(stream))
+        _lib.call("ring_attn_step_fold_hop" if fold else "ring_attn_step_hop", *args, *(_ptr(t) for t in hop), nbytes,
+                  _stream(stream))
     else:
         _lib.call("ring_attn_step_fold" if fold else "ring_attn_step", *args, _stream(stream))
     return out, lse

@@ -188,6 +188,17 @@ ca_status ring_attn_step_hop(const void* q, ca_strides qs, const void* k, const 
                              mask, o, lse, workspace, workspace_bytes, stream, 0, hop);
 }
 
+ca_status ring_attn_step_fold_hop(const void* q, ca_strides qs, const void* k, const void* v, ca_strides kvs,
+                                  int dtype, int B, int H, int Sq, int Sk, int D, float softmax_scale, int mask,
+                                  float* o, float* lse, void* workspace, size_t workspace_bytes, void* hop_dst_k,
+                                  void* hop_dst_v, const void* hop_src_k, const void* hop_src_v, size_t hop_bytes,
+                                  void* stream) {
+  const Hop hop{hop_dst_k, hop_dst_v, hop_src_k, hop_src_v, hop_bytes};
+  CA_TRY(check_hop("ring_attn_step_fold_hop", hop));
+  return ring_attn_step_impl("ring_attn_step_fold_hop launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D,
+                             softmax_scale, mask, o, lse, workspace, workspace_bytes, stream, 1, hop);
+}
+
 ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask, size_t* bytes) {
   if (!bytes) return fail(CA_ERR_NULL, "bytes is NULL");
   *bytes = 0;

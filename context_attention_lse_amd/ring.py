@@ -91,11 +91,14 @@ class RingPass:
     against 0.90 ms unsplit on one stream, 0.94 ms split on one and 0.96 ms unsplit on two
     (timed with hops on the copy stream, before the split's regular cuts).
 
-    fused_hops=True (no fold, no sinks): each step call carries the hop of the chunk two steps
-    ahead (ring_attn_step_hop), on the CUs the step leaves free when there are any, instead of
-    a copy stream. A step fills every CU's register file, so a copy kernel on its own stream
-    runs only between steps; carried by the step it costs nothing there. On the Wan2.2 share
-    (240 ranges, 16 CUs free) the pass went from 806 to 779 us.
+    fused_hops=True (no sinks): each step call carries the hop of the chunk two steps ahead
+    (ring_attn_step_hop, or ring_attn_step_fold_hop when folding), on the CUs the step leaves
+    free when there are any, instead of a copy stream. A step fills every CU's register file,
+    so a copy kernel on its own stream runs only between steps; carried by the step it costs
+    nothing there. On the Wan2.2 share (240 ranges, 16 CUs free) the pass went from 806 to
+    779 us. With fold as well, each compute stream folds its steps into one running partial
+    and the pass ends in a 2-way merge instead of an 8-way one (Wan2.2, unsplit steps two in
+    flight: 695 -> 687 us).
     """
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
@@ -123,8 +126,8 @@ class RingPass:
         # buffers keep that true with two compute streams.
         self.fused_hops = bool(fused_hops)
         if self.fused_hops:
-            if fold or sink_theta is not None:
-                raise ValueError("fused hops do not combine with fold or sinks")
+            if sink_theta is not None:
+                raise ValueError("fused hops do not combine with sinks")
             self.depth, self.nbuf = 2, 4
         B, Sq, H, D = q.shape
         chunk_shape = tuple(k_pool.shape[1:])
@@ -306,6 +309,7 @@ class RingPass:
             self.aux_stream.wait_stream(cs)
         streams = [self.aux_stream if (self.aux_stream is not None and s % 2 == 1) else cs for s in range(cp)]
         slot = 0
+        started = [False, False]   # fold: running partial of each compute stream begun
         for s in range(cp):
             st = streams[s]
             hop = self._hop_buffers(s + 2) if s + 2 < cp else None
@@ -318,6 +322,13 @@ class RingPass:
                     phase = (api.CA_PHASE_INIT if s == 0 else 0) | (api.CA_PHASE_FINAL if s == cp - 1 else 0)
                     api.ring_attn_const_max_step(self.q, k, v, self.c, self.acc, phase, out=self.out, lse=self.lse,
                                                  scale=self.scale, workspace=ws, hop=hop)
+                elif self.masks[s] is not None and self.fold:
+                    a = 1 if st is not cs else 0
+                    o_dst, l_dst = ((self.out, self.lse) if self.fold_direct
+                                    else (self.o_parts[a], self.lse_parts[a]))
+                    api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s], out=o_dst, lse=l_dst,
+                                       workspace=ws, fold=started[a], hop=hop)
+                    started[a] = True
                 elif self.masks[s] is not None:
                     api.ring_attn_step(self.q, k, v, scale=self.scale, mask=self.masks[s], out=self.o_parts[slot],
                                        lse=self.lse_parts[slot], workspace=ws, hop=hop)
@@ -328,7 +339,11 @@ class RingPass:
                     timing_events[s][1].record(st)
         if self.aux_stream is not None:
             cs.wait_stream(self.aux_stream)
-        if self.variant == "online":
+        if self.variant == "online" and self.fold:
+            if not self.fold_direct:
+                n = 2 if started[1] else 1   # stream 0 always runs step 0, the rank's own chunk
+                api.lse_merge(self.o_parts[:n], self.lse_parts[:n], out=self.out, lse_out=self.lse)
+        elif self.variant == "online":
             api.lse_merge(self.o_parts[:slot], self.lse_parts[:slot], out=self.out, lse_out=self.lse)
         return self.out, self.lse
 

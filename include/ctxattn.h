@@ -168,6 +168,27 @@ ca_status ring_attn_step_hop(const void* q, ca_strides q_strides,
                              void* stream);
 
 /*
+ * ring_attn_step_fold_hop -- ring_attn_step_fold and, in the same call, the ring's next
+ * K/V hop, exactly as ring_attn_step_hop adds one to ring_attn_step (in the step's launch
+ * on the CUs its last round leaves free, else as a copy just ahead of it). A ring whose
+ * steps fold into running partials can so carry its hops in the steps as well.
+ * Source: kernel reference page, Implementation, the ring loop; "Sharding the Input",
+ * ring attention (running log-sum-exp combination).
+ *
+ * Arguments, layouts, support and errors: as ring_attn_step_fold, plus the hop arguments
+ * of ring_attn_step_hop with the same requirements.
+ */
+ca_status ring_attn_step_fold_hop(const void* q, ca_strides q_strides,
+                                  const void* k, const void* v, ca_strides kv_strides,
+                                  int dtype, int B, int H, int Sq, int Sk, int D,
+                                  float softmax_scale, int mask,
+                                  float* o, float* lse,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* hop_dst_k, void* hop_dst_v,
+                                  const void* hop_src_k, const void* hop_src_v, size_t hop_bytes,
+                                  void* stream);
+
+/*
  * ring_attn_workspace_size -- bytes of step workspace that ring_attn_step and
  * ring_attn_const_max_step (mask CA_MASK_NONE) need for these sizes on the CURRENT
  * device (the split depends on its compute-unit count). 0: the call does not split

@@ -89,9 +89,10 @@ def _summary(label, errs):
 
 def test_wan22_cp8_online_fullsize_every_row(ca):
     # the Wan2.2 share in its timed form: unsplit steps alternating two compute streams (two
-    # in flight), each carrying the hop of the chunk two steps ahead; every row of every head
+    # in flight), each carrying the hop of the chunk two steps ahead and folding into its
+    # stream's running partial; every row of every head
     wl, t, o, lse, tok = _ring_pass(ca, "wan22_cp8_online", "online", 0, False, split=False, compute_streams=2,
-                                    fused_hops=True)
+                                    fused_hops=True, fold=True)
     errs = [_check_head("wan22 online rank 0", wl, t, o, lse, tok, h, np.arange(wl.local_S)) for h in range(wl.H)]
     _summary("wan22_cp8_online every row", errs)
 

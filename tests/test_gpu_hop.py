@@ -58,14 +58,33 @@ def test_step_hop_matches_step_and_copies(ca, B, H, Sq, Sk, mask, split, dtype):
     assert torch.equal(o0, o1) and torch.equal(l0, l1), "step outputs differ with the hop"
 
 
+@pytest.mark.parametrize("B,H,Sq,Sk,mask,split", [(1, 10, 4096, 4096, "none", False), (2, 2, 512, 700, "none", False),
+                                                  (1, 3, 1000, 1000, "causal_strict", True)])
+def test_step_fold_hop_matches_step_fold_and_copies(ca, B, H, Sq, Sk, mask, split):
+    """ring_attn_step_fold_hop: the fold of ring_attn_step_fold, bit for bit, and the hop's bytes."""
+    say(f"step_fold_hop B={B} H={H} Sq={Sq} Sk={Sk} mask={mask} split={split}")
+    q, k1, v1 = _qkv(B, Sq, Sk, H, 720)
+    _, k2, v2 = _qkv(B, Sq, Sk, H, 730)
+    ws = ca.api.step_workspace(q, k2, mask) if split else None
+    o0, l0 = ca.api.ring_attn_step(q, k1, v1, mask=mask)
+    o1, l1 = o0.clone(), l0.clone()
+    ca.api.ring_attn_step(q, k2, v2, mask=mask, out=o0, lse=l0, fold=True, workspace=ws)
+    src_k = torch.randint(-2**31, 2**31 - 1, (1_000_003 * 4,), dtype=torch.int32, device=q.device)
+    src_v = torch.randint(-2**31, 2**31 - 1, (1_000_003 * 4,), dtype=torch.int32, device=q.device)
+    dst_k = torch.zeros_like(src_k)
+    dst_v = torch.zeros_like(src_v)
+    ca.api.ring_attn_step(q, k2, v2, mask=mask, out=o1, lse=l1, fold=True, workspace=ws,
+                          hop=(dst_k, dst_v, src_k, src_v))
+    torch.cuda.synchronize()
+    assert torch.equal(dst_k, src_k) and torch.equal(dst_v, src_v), "hop bytes differ"
+    assert torch.equal(o0, o1) and torch.equal(l0, l1), "fold outputs differ with the hop"
+
+
 def test_step_hop_rejects_bad_buffers(ca):
     q, k, v = _qkv(1, 64, 64, 1, 710)
     a = torch.zeros(64, dtype=torch.uint8, device=q.device)
     with pytest.raises(ValueError):
         ca.api.ring_attn_step(q, k, v, hop=(a, a[:32], a, a))
-    with pytest.raises(ValueError):
-        ca.api.ring_attn_step(q, k, v, hop=(a, a, a, a), fold=True, out=torch.zeros(1, 1, 64, 128, device=q.device),
-                              lse=torch.zeros(1, 1, 64, device=q.device))
     # 24 bytes: not a multiple of 16 (checked by the library)
     b = torch.zeros(24, dtype=torch.uint8, device=q.device)
     with pytest.raises(ca._lib.CtxAttnError) as e:
@@ -73,14 +92,19 @@ def test_step_hop_rejects_bad_buffers(ca):
     assert e.value.status == ca._lib.CA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("wl_name,S,ranks,streams,H,layout", [
-    ("wan22_cp8_online", 8 * 328, (0, 5), 2, None, None),
-    ("wan22_cp8_online", 8 * 328, (3,), 1, None, None),
-    ("striped_causal_128k", 8 * 200, (0, 7), 2, 2, None),
+@pytest.mark.parametrize("wl_name,S,ranks,streams,H,layout,kw", [
+    ("wan22_cp8_online", 8 * 328, (0, 5), 2, None, None, {"split": True}),
+    ("wan22_cp8_online", 8 * 328, (3,), 1, None, None, {"split": True}),
+    ("striped_causal_128k", 8 * 200, (0, 7), 2, 2, None, {"split": True}),
     # contiguous causal: rank 0 sees only its own chunk, so every later step is empty and
     # its hop moves as a plain copy on that step's stream
-    ("striped_causal_128k", 8 * 200, (0, 5), 2, 2, "contiguous")])
-def test_ring_fused_hops_matches_oracle(ca, wl_name, S, ranks, streams, H, layout):
+    ("striped_causal_128k", 8 * 200, (0, 5), 2, 2, "contiguous", {"split": True}),
+    # steps folding into one running partial per compute stream, 2-way merge at the end
+    ("wan22_cp8_online", 8 * 328, (0, 5), 2, None, None, {"fold": True}),
+    ("wan22_cp8_online", 8 * 328, (3,), 1, None, None, {"fold": True}),
+    ("striped_causal_128k", 8 * 200, (0, 7), 2, 2, None, {"fold": True}),
+    ("striped_causal_128k", 8 * 200, (0, 5), 2, 2, "contiguous", {"fold": True})])
+def test_ring_fused_hops_matches_oracle(ca, wl_name, S, ranks, streams, H, layout, kw):
     dev = torch.device("cuda:0")
     wl = workloads.workload(wl_name).scaled(S=S, **({"H": H} if H else {}))
     if layout is not None:
@@ -88,9 +112,9 @@ def test_ring_fused_hops_matches_oracle(ca, wl_name, S, ranks, streams, H, layou
     t = gen.ring_inputs(wl, dev)
     scale = oracle.default_scale(wl.D)
     for r in ranks:
-        say(f"ring fused hops {wl.name} S={S} rank={r} streams={streams}")
+        say(f"ring fused hops {wl.name} S={S} rank={r} streams={streams} {kw}")
         o, l = ca.ring.ring_attention(t["q"], t["k"], t["v"], wl.cp, r, layout=wl.layout, causal=wl.causal,
-                                      split=True, compute_streams=streams, fused_hops=True)
+                                      compute_streams=streams, fused_hops=True, **kw)
         torch.cuda.synchronize()
         rows = (oracle.contiguous_tokens if wl.layout == "contiguous" else oracle.striped_tokens)(S, wl.cp, r)
         allowed = oracle.causal_allowed(rows, np.arange(S)) if wl.causal else None

@@ -90,6 +90,8 @@ CASES = [
     ("online", "striped", True, {"fused_hops": True}),
     ("constmax", "contiguous", False, {"fused_hops": True}),
     ("online", "contiguous", False, {"fold": True, "compute_streams": 2}),
+    ("online", "contiguous", False, {"fold": True, "compute_streams": 2, "fused_hops": True}),
+    ("online", "striped", True, {"fold": True, "fused_hops": True}),
 ]
 
 
