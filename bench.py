@@ -64,19 +64,19 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
-                                                     "fetch_kib": 611376.1, "write_kib": 265399.2},
+                                                     "fetch_kib": 611228.6, "write_kib": 265443.7},
     "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
-                                              "fetch_kib": 29363.9, "write_kib": 20642.0},
+                                              "fetch_kib": 29363.9, "write_kib": 20641.9},
     "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
                                                  "fetch_kib": 57381.9, "write_kib": 63000.0},
     "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "a8ad7b9370013ab7",
-                                           "fetch_kib": 331822.8, "write_kib": 190624.0},
+                                           "fetch_kib": 331804.4, "write_kib": 190626.1},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "974e5a7d3ee9555e",
-                                  "fetch_kib": 2778068.0 + 14927.25, "write_kib": 31631.46 + 1040.01},
+                                  "fetch_kib": 2778066.0 + 14927.25, "write_kib": 31632.01 + 1040.01},
     "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
                                       "fetch_kib": 779655.5, "write_kib": 190477.2},
     "const_max_bound/wan22_720p_constmax": {"source": "bound.hip", "sha256": "5c362a4869e5af73",
-                                            "fetch_kib": 378047.6 + 47347.7, "write_kib": 160.0 + 2584.7},
+                                            "fetch_kib": 378047.6 + 47348.4, "write_kib": 160.0 + 2584.7},
 }
 
 
