@@ -36,7 +36,7 @@
 //    keeps a lazy reference max: a tile is exponentiated against the reference as it
 //    stands, and only when a lane's share of the tile's row sum comes out above 2^20 (or
 //    while some row of the wave has no reference yet) does the wave find the tile's row
-//    maxima, move the reference, rescale its accumulators and redo the tile. A full tile
+//    maxima, raise the reference, rescale its accumulators and redo the tile. A full tile
 //    thus runs no max reduction at all, and probabilities stay <= 2^20;
 //  * causal masks: a workgroup visits key tiles up to its last row's diagonal; tiles
 //    past a wave's own diagonal are masked in full (every probability is 0).
@@ -101,9 +101,9 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, ui
                :: "s"(lds_byte), "v"(off), "s"(base) : "memory", "m0");
 }
 
-// End of a phase: this wave's LDS reads have returned, at most 2*PENDING of its tile copies
-// are still in flight (two per tile: K and V), then the workgroup barrier. The scheduling
-// barriers keep the compiler from moving any instruction across the phase boundary.
+// End of a vector phase (which issues no LDS reads): at most 2*PENDING of this wave's tile
+// copies are still in flight (two per tile: K and V), then the workgroup barrier. The
+// scheduling barriers keep the compiler from moving any instruction across the boundary.
 template <int PENDING>
 __device__ __forceinline__ void phase_end() {
   __builtin_amdgcn_sched_barrier(0);
