@@ -3,9 +3,9 @@
 // and two sets of keys: its prior tokens in the paged cache (all earlier than every query,
 // so all visible) and its slice of the chunk (visible by global position). The call
 //   1. gathers the prior slots from the paged cache into token-major K and V,
-//   2. runs the step kernel over them (no mask),
-//   3. runs the step kernel over the chunk slice with the interleaved causal mask,
-//   4. merges the two partials by the LSE rule into the rank's partial.
+//   2. runs the step kernel over them (no mask), writing its partial to the outputs,
+//   3. runs the step kernel over the chunk slice with the interleaved causal mask, whose
+//      epilogue merges its partial into the outputs by the LSE rule (step 4's merge).
 // Query head h reads K/V head h / (Hq / Hkv) in both steps.
 #include "internal.hpp"
 
@@ -64,10 +64,13 @@ size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 }  // namespace
 
+// The gathered prior K and V; the two partials (prior, then this rank's slice folded into it)
+// go straight to the caller's o and lse.
 size_t segmented_workspace_bytes(int Hq, int Hkv, int S, int D_, int prior) {
+  (void)Hq; (void)S;
   if (prior <= 0) return 0;
   const size_t kv = align256(size_t(prior) * Hkv * D_ * 2);
-  return 2 * kv + align256(size_t(2) * Hq * S * D_ * 4) + align256(size_t(2) * Hq * S * 4);
+  return 2 * kv;
 }
 
 hipError_t launch_segmented(const SegmentedArgs& g, hipStream_t s) {
@@ -87,26 +90,23 @@ hipError_t launch_segmented(const SegmentedArgs& g, hipStream_t s) {
   const size_t kv = align256(size_t(g.prior) * g.Hkv * D * 2);
   uint16_t* kg = reinterpret_cast<uint16_t*>(ws);
   uint16_t* vg = reinterpret_cast<uint16_t*>(ws + kv);
-  float* o_parts = reinterpret_cast<float*>(ws + 2 * kv);
-  float* lse_parts = reinterpret_cast<float*>(ws + 2 * kv + align256(size_t(2) * g.Hq * g.S * D * 4));
-  const int64_t rows = int64_t(g.Hq) * g.S;
   const int nblk = (g.prior + BS - 1) / BS;
   hipLaunchKernelGGL(prior_gather_kernel, dim3(nblk), dim3(NT), size_t(g.Hkv) * D * BS * 2, s,
                      static_cast<const uint16_t*>(g.k_cache), static_cast<const uint16_t*>(g.v_cache), g.block_table,
                      g.num_blocks, g.prior, g.Hkv, kg, vg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // prior keys: all earlier than every query
+  // prior keys: all earlier than every query; their partial goes straight to o and lse
   a.k = kg; a.v = vg; a.ksb = 0; a.kss = int64_t(g.Hkv) * D; a.ksh = D;
   a.Sk = g.prior; a.mask = CA_MASK_NONE;
-  a.o = o_parts; a.lse = lse_parts;
+  a.o = g.o; a.lse = g.lse;
   if ((e = launch_attn_bf16(a, false, s)) != hipSuccess) return e;
-  // this rank's slice of the chunk, causal on global positions
+  // this rank's slice of the chunk, causal on global positions, folded into that partial by
+  // the LSE rule in the step's epilogue (no separate merge of two partials)
   a.k = g.k_cur; a.v = g.v_cur; a.kss = g.kss; a.ksh = g.ksh;
   a.Sk = g.S_local; a.mask = kMaskDcp;
-  a.o = o_parts + rows * D; a.lse = lse_parts + rows;
-  if ((e = launch_attn_bf16(a, false, s)) != hipSuccess) return e;
-  return launch_lse_merge(2, o_parts, lse_parts, rows, D, g.o, 0, g.lse, s);
+  a.fold = 1;
+  return launch_attn_bf16(a, false, s);
 }
 
 }  // namespace ctxattn
