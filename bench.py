@@ -363,23 +363,27 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     # overlap gives.
     rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=False, compute_streams=2,
                           fused_hops=True, fold=True)
-    ms = timed(torch, rp.run, max(10, args.steps), warm_calls=max(10, args.warmup))
-    clk = clock.measure(torch, rp.run)
+    # the pass replayed as one captured HIP graph (its ten launches and stream joins, with no
+    # per-launch gaps; 0.8% faster than issuing it eagerly)
+    graph = rp.capture()
+    # windows of tens of milliseconds: a few-millisecond window caught clock transitions
+    ms = timed(torch, graph.replay, max(100, args.steps), warm_calls=max(10, args.warmup))
+    clk = clock.measure(torch, graph.replay)
     fl_step = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D)
     fl = ring_flops(wl.H, wl.local_S, wl.S, wl.D)
     pairs, n = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev)
-    p_ms = timed(torch, pairs, max(5, args.steps // 2)) / n
+    p_ms = timed(torch, pairs, max(40, args.steps)) / n
     # the key-split form a single step uses (one launch at a time, filling the device)
     ws = ca.step_workspace(q, kp[0])
     o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
     lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
-    k_ms = timed(torch, lambda: ca.ring_attn_step(q, kp[0], vp[0], out=o, lse=lse, workspace=ws), 30)
-    rp.run()
+    k_ms = timed(torch, lambda: ca.ring_attn_step(q, kp[0], vp[0], out=o, lse=lse, workspace=ws), 200)
+    graph.replay()   # the parity check below reads this replay's output
     return {"workload": wl.name, "config": "B=1 H=10 D=128 S=32768 cp=8 local=4096 bf16, QK RMS-normed, rank 0",
             "ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "clock_mhz": clk,
             "form": "unsplit steps, two in flight on two compute streams, hops carried by the steps, each stream "
-                    "folding into a running partial, 2-way LSE merge",
+                    "folding into a running partial, 2-way LSE merge; the pass replayed as one captured HIP graph",
             "roofline": kernel_roofline(p_ms, fl_step,
                                         "attn_step_bf16<0, 0, false> (ring_attn_step_fold, two launches in flight)",
                                         f"{fl_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
@@ -390,7 +394,7 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
                               "frac_bf16_peak": round(fl_step / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "traffic": traffic("attn_step_bf16/wan22_cp8_online_keysplit"),
                               "note": "attn_step_bf16<0, 0, true>: the same step cut into 240 key ranges with a "
-                                      "workspace (the form one step alone uses); mean of 30 back-to-back launches"},
+                                      "workspace (the form one step alone uses); mean of 200 back-to-back launches"},
             "_keep": {"wl": wl, "t": t, "out": rp.out, "lse": rp.lse}}
 
 
@@ -425,7 +429,7 @@ def run_constmax(args, torch, ca, workloads, gen, dev, clock):
     rp.run()
     keep = {"wl": wl, "t": t, "out": rp.out.clone(), "lse": rp.lse.clone()}
     # bound prologue: |k|^2 max over all 8 chunks + c for every query row (HBM-bound)
-    ms_b = timed(torch, rp.prologue, 20)
+    ms_b = timed(torch, rp.prologue, 100)
     clk_b = clock.measure(torch, rp.prologue)
     nbytes = (kp.numel() + q.numel()) * kp.element_size() + q.shape[1] * wl.H * 4
     res["bound"] = {"ms": round(ms_b, 4), "bytes": nbytes, "GBps": round(nbytes / (ms_b * 1e-3) / 1e9, 1),
@@ -453,7 +457,7 @@ def run_constmax(args, torch, ca, workloads, gen, dev, clock):
     # the 8-way merge of the online partials (HBM-bound: 8 x 193.5 MB in, 195 MB out)
     parts_o, parts_l = rp.o_parts[:wl.cp], rp.lse_parts[:wl.cp]
     merge = lambda: ca.lse_merge(parts_o, parts_l, out=rp.out, lse_out=rp.lse)  # noqa: E731
-    ms_m = timed(torch, merge, 20)
+    ms_m = timed(torch, merge, 50)
     clk_m = clock.measure(torch, merge)
     nbytes = (parts_o.numel() + parts_l.numel()) * 4 + (rp.out.numel() + rp.lse.numel()) * 4
     res["merge"] = {"ms": round(ms_m, 4), "bytes": nbytes, "GBps": round(nbytes / (ms_m * 1e-3) / 1e9, 1),

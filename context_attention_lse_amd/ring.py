@@ -289,6 +289,23 @@ class RingPass:
         return self.out, self.lse
 
 
+    def capture(self):
+        """Captures one run() as a HIP graph (torch.cuda.CUDAGraph) and returns it; each
+        replay() redoes the pass on the same inputs into self.out and self.lse. The pass
+        launches only kernels and stream waits, no memset or allocation, so it captures as
+        is. One eager pass first settles the library's lazy set-up outside the capture."""
+        cs = torch.cuda.current_stream()
+        side = torch.cuda.Stream(device=self.q.device)
+        side.wait_stream(cs)
+        with torch.cuda.stream(side):
+            self.run()
+        cs.wait_stream(side)
+        torch.cuda.synchronize(self.q.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        return g
+
     def _hop_buffers(self, t):
         kd, vd = self._chunk(t)
         src = ring_source_rank(self.rank, t, self.cp)
