@@ -258,16 +258,18 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
     del o, lse
 
     log("[bench] headline: every rank's ring pass")
-    copy_stream = torch.cuda.Stream()
+    copy_stream = ca.streams.side_streams(2)[0]   # a stream whose work overlaps the calling stream's
     # one compute stream folding each step into the running partial (no final merge), hops on a
     # copy stream: 16.2-16.3 ms per rank against 16.5-16.6 with two compute streams and the
     # 8-way merge (interleaved A/B, ranks 0 and 7)
     rps = [ca.ring.RingPass(qs[r], kp, vp, r, layout="striped", causal=True, copy_stream=copy_stream, fold=True,
                             compute_streams=1) for r in range(wl.cp)]
+    # each rank's pass replayed as a captured HIP graph (+0.3% over issuing it eagerly)
+    graphs = [rp.capture() for rp in rps]
 
     def step():
-        for rp in rps:
-            rp.run()
+        for g in graphs:
+            g.replay()
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     done, spent = 0, 0.0
@@ -334,7 +336,7 @@ def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev):
     each stream's steps after its first folding into its running partial.
     Returns fn() (launches on the current stream's work order) and the launch count."""
     cur = torch.cuda.current_stream()
-    aux = torch.cuda.Stream(device=dev)
+    aux = ca.streams.side_streams(2, dev)[1]   # overlaps the calling stream (its own hardware queue)
     outs = [(torch.empty(o_shape, dtype=torch.float32, device=dev),
              torch.empty(o_shape[:-1], dtype=torch.float32, device=dev)) for _ in range(2)]
 
@@ -559,7 +561,7 @@ def run_contrast(args, torch, ca, workloads, gen, dev, clock, t=None):
         t = gen.ring_inputs(wl, dev)
     kp = ca.ring.chunk_pool(t["k"], wl.cp, "contiguous")
     vp = ca.ring.chunk_pool(t["v"], wl.cp, "contiguous")
-    copy_stream = torch.cuda.Stream()
+    copy_stream = ca.streams.side_streams(2)[0]
     per_rank = []
     for r in range(wl.cp):
         q = ca.ring.shard(t["q"], wl.cp, r, "contiguous").contiguous()
@@ -891,7 +893,7 @@ def main():
                    "cp": wl.cp, "local_seq": wl.local_S, "layout": "striped", "causal": True,
                    "ranks_per_step": wl.cp, "ring_steps_per_rank": wl.cp, "flops_per_step": h["flops"]},
         "step": "every rank's ring pass (8 steps, each folded by the LSE rule into the running partial; hops on a "
-                "copy stream), ranks one after another",
+                "copy stream), ranks one after another, each pass replayed as a captured HIP graph",
         "frac_bf16_peak": round(h["tflops"] / PEAK_BF16_TFLOPS, 4),
         "roofline": h["roofline"],
         "clock_mhz": h["clock_mhz"],

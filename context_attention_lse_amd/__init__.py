@@ -29,7 +29,7 @@ from .api import (  # noqa: F401
     step_workspace,
     version,
 )
-from . import dcp, ring  # noqa: F401
+from . import dcp, ring, streams  # noqa: F401
 
 __all__ = [
     "CtxAttnError", "const_max_acc_size", "const_max_bound", "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_partial_noalloc",

@@ -19,6 +19,7 @@ This module only orders library calls; every byte of arithmetic runs in libctxat
 import torch
 
 from . import api
+from .streams import side_streams
 
 LAYOUTS = ("contiguous", "striped")
 
@@ -134,7 +135,7 @@ class RingPass:
         dev = q.device
         self.kbuf = [torch.empty(chunk_shape, dtype=k_pool.dtype, device=dev) for _ in range(self.nbuf)]
         self.vbuf = [torch.empty(chunk_shape, dtype=v_pool.dtype, device=dev) for _ in range(self.nbuf)]
-        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream(device=dev)
+        self.copy_stream = copy_stream if copy_stream is not None else side_streams(2, dev)[0]
         self.copied = [torch.cuda.Event() for _ in range(self.cp)]
         self.consumed = [torch.cuda.Event() for _ in range(self.cp)]
         self.masks = [step_mask(layout, causal, rank, ring_source_rank(rank, s, self.cp)) for s in range(self.cp)]
@@ -148,7 +149,7 @@ class RingPass:
             compute_streams = 2 if (variant == "online" and not nbytes) else 1
         if variant == "constmax" and compute_streams > 1:
             raise ValueError("const-max steps add into one accumulator and run on one stream")
-        self.aux_stream = torch.cuda.Stream(device=dev) if compute_streams > 1 else None
+        self.aux_stream = side_streams(2, dev)[1] if compute_streams > 1 else None
         # one workspace per compute stream (concurrent steps may not share one)
         self.ws = [None, None]
         if nbytes:
