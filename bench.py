@@ -452,16 +452,24 @@ def run_constmax(args, torch, ca, workloads, gen, dev, clock):
     res["constmax_sinks"] = {"ms_per_pass": round(ms_s, 4), "tflops": round(fl / (ms_s * 1e-3) / 1e12, 2),
                              "sinks_found": int(rp.sinks["sink_cnt"].sum().item())}
     del rp
-    rp = ca.ring.RingPass(q, kp, vp, 0, variant="online")
+    # two compute streams, each folding its steps into a running partial, a 2-way merge at the
+    # end (12.61 ms against 12.70 for separate partials and an 8-way merge)
+    rp = ca.ring.RingPass(q, kp, vp, 0, variant="online", fold=True, compute_streams=2)
     ms_o = timed(torch, rp.run, reps)
     o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
     lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
     k_on = timed(torch, lambda: ca.ring_attn_step(q, kp[1], vp[1], out=o, lse=lse), 8)
     res["online"] = {"ms_per_pass": round(ms_o, 4), "tflops": round(fl / (ms_o * 1e-3) / 1e12, 2),
+                     "form": "unsplit steps on two compute streams, each folding into a running partial, 2-way "
+                             "LSE merge; hops on a copy stream",
                      "step_kernel_ms": round(k_on, 4),
                      "step_tflops": round(fl_step / (k_on * 1e-3) / 1e12, 2),
                      "frac_bf16_peak_step": round(fl_step / (k_on * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    # the 8-way merge of the online partials (HBM-bound: 8 x 193.5 MB in, 195 MB out)
+    del rp
+    # the 8-way merge of the online partials (HBM-bound: 8 x 193.5 MB in, 195 MB out), on the
+    # partials of a pass that keeps one per step
+    rp = ca.ring.RingPass(q, kp, vp, 0, variant="online")
+    rp.run()
     parts_o, parts_l = rp.o_parts[:wl.cp], rp.lse_parts[:wl.cp]
     merge = lambda: ca.lse_merge(parts_o, parts_l, out=rp.out, lse_out=rp.lse)  # noqa: E731
     ms_m = timed(torch, merge, 50)
