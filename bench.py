@@ -259,11 +259,12 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
 
     log("[bench] headline: every rank's ring pass")
     copy_stream = ca.streams.side_streams(2)[0]   # a stream whose work overlaps the calling stream's
-    # two compute streams, each folding its steps into a running partial, a 2-way merge at the
-    # end, hops on a copy stream (ranks 0 + 7: 31.18 ms, against 31.29 folding on one stream and
-    # 31.43 with an 8-way merge; every side stream on a hardware queue of its own)
+    # one compute stream folding each step into the running partial (no final merge), hops on a
+    # copy stream, replayed as a HIP graph per rank. Eagerly, two compute streams each folding
+    # (2-way merge) ran ranks 0 + 7 in 31.18 ms against 31.29 for this form, about what the graph
+    # replay gains; that form is not captured (RingPass.capture refuses it).
     rps = [ca.ring.RingPass(qs[r], kp, vp, r, layout="striped", causal=True, copy_stream=copy_stream, fold=True,
-                            compute_streams=2) for r in range(wl.cp)]
+                            compute_streams=1) for r in range(wl.cp)]
     # each rank's pass replayed as a captured HIP graph (+0.3% over issuing it eagerly)
     graphs = [rp.capture() for rp in rps]
 
@@ -305,8 +306,8 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
     per_rank = [sum(ev[k][r][0].elapsed_time(ev[k][r][1]) for k in range(nrep)) / nrep for r in range(wl.cp)]
     mean = sum(per_rank) / len(per_rank)
     # step s of rank r reads rank (r - s) mod cp's chunk: INCL when that rank is <= r, else STRICT.
-    # Steps 0 and 1 start the two compute streams' partials; steps 2.. fold into them.
-    kinds = [((r - s) % wl.cp <= r, s >= 2) for r in range(wl.cp) for s in range(wl.cp)]
+    # Step 0 starts the running partial; steps 1.. fold into it.
+    kinds = [((r - s) % wl.cp <= r, s >= 1) for r in range(wl.cp) for s in range(wl.cp)]
     n_incl = sum(1 for inc, fold in kinds if inc and not fold)
     n_fold_incl = sum(1 for inc, fold in kinds if inc and fold)
     n_strict = sum(1 for inc, fold in kinds if not inc)
@@ -321,10 +322,9 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
                          "strict_steps": n_strict,
                          "strict_tflops": round(causal_flops(wl.H, wl.D, n, True) / (k_strict * 1e-3) / 1e12, 2)},
         "exposed_ms": round(ms - kernels_ms, 3),
-        "exposed_note": (f"step time minus the sum of its kernels timed alone, one at a time ({n_incl} INCL steps "
-                         f"starting a partial, {n_fold_incl} folded INCL and {n_strict} STRICT steps, all STRICT "
-                         "priced at the folded figure): the hop copies and launch gaps the steps did not hide, less "
-                         "what two compute streams gain where a step's tail overlaps the next step"),
+        "exposed_note": (f"step time minus the sum of its kernels timed alone ({n_incl} INCL steps starting the "
+                         f"partial, {n_fold_incl} folded INCL and {n_strict} folded STRICT steps): the hop copies on "
+                         "the copy stream and launch gaps that the steps did not hide"),
         "hop_bytes_per_step": int(2 * kp[0].numel() * kp.element_size() * (wl.cp - 1) * wl.cp),
     })
     # outputs kept for the parity check: rank, head, rows -> host copies taken in the cpu leg
@@ -905,9 +905,8 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "heads": wl.H, "head_dim": wl.D, "global_seq": wl.S,
                    "cp": wl.cp, "local_seq": wl.local_S, "layout": "striped", "causal": True,
                    "ranks_per_step": wl.cp, "ring_steps_per_rank": wl.cp, "flops_per_step": h["flops"]},
-        "step": "every rank's ring pass (8 steps on two compute streams, each folded by the LSE rule into its "
-                "stream's running partial, a 2-way merge at the end; hops on a copy stream), ranks one after "
-                "another, each pass replayed as a captured HIP graph",
+        "step": "every rank's ring pass (8 steps, each folded by the LSE rule into the running partial; hops on a "
+                "copy stream), ranks one after another, each pass replayed as a captured HIP graph",
         "frac_bf16_peak": round(h["tflops"] / PEAK_BF16_TFLOPS, 4),
         "roofline": h["roofline"],
         "clock_mhz": h["clock_mhz"],

@@ -56,3 +56,16 @@ def test_ring_pass_graph_replays_match_eager_and_oracle(ca, kw, causal, layout):
     allowed = oracle.causal_allowed(tok, np.arange(wl.S)) if causal else None
     ro, rl = oracle.attention_heads(t["q"][:, tok], t["k"], t["v"], oracle.default_scale(wl.D), allowed=allowed)
     check("graph replay", rp.out, rp.lse, ro, rl)
+
+
+def test_capture_refuses_two_compute_streams_with_a_copy_stream(ca):
+    """That form is run eagerly only: capture() raises before capturing anything."""
+    dev = torch.device("cuda:0")
+    wl = workloads.workload("wan22_cp8_online").scaled(S=8 * 64, H=1)
+    t = gen.ring_inputs(wl, dev)
+    q = ca.ring.shard(t["q"], wl.cp, 0, "contiguous")
+    kp = ca.ring.chunk_pool(t["k"], wl.cp, "contiguous")
+    vp = ca.ring.chunk_pool(t["v"], wl.cp, "contiguous")
+    rp = ca.ring.RingPass(q, kp, vp, 0, variant="online", fold=True, compute_streams=2)
+    with pytest.raises(NotImplementedError):
+        rp.capture()
