@@ -94,3 +94,29 @@ def test_rejections_without_gpu():
                               _fake(0x10000), 16, None) == _lib.CA_ERR_WORKSPACE
     assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(),
                               _fake(0x10010), 1 << 30, None) == _lib.CA_ERR_SHAPE   # misaligned workspace
+
+
+def test_hop_and_workspace_rejections_without_gpu():
+    lib = _lib.load()
+    st = _lib.ca_strides(0, 128, 0)
+    step = (_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None, 0)
+    for name in ("ring_attn_step_hop", "ring_attn_step_fold_hop"):
+        fn = getattr(lib, name)
+        # hop size not a multiple of 16, a misaligned hop pointer, a missing hop buffer
+        assert fn(*step, _fake(0x2000), _fake(0x3000), _fake(0x4000), _fake(0x5000), 100, None) == _lib.CA_ERR_SHAPE
+        assert fn(*step, _fake(0x2008), _fake(0x3000), _fake(0x4000), _fake(0x5000), 4096, None) == _lib.CA_ERR_SHAPE
+        assert fn(*step, None, _fake(0x3000), _fake(0x4000), _fake(0x5000), 4096, None) == _lib.CA_ERR_NULL
+        assert b"hop" in lib.ca_last_error()
+        # no hop and no rows: nothing to do
+        assert fn(None, st, None, None, st, _lib.CA_BF16, 1, 1, 0, 0, 128, 0.0, 0, None, None, None, 0,
+                  None, None, None, None, 0, None) == _lib.CA_OK
+    cm = (_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, _fake(), _fake(), 0, None, 0, None,
+          None, 0)
+    assert lib.ring_attn_const_max_step_hop(*cm, _fake(0x2000), _fake(0x3000), _fake(0x4000), _fake(0x5000), 24,
+                                            None) == _lib.CA_ERR_SHAPE
+    # segmented prefill: the workspace holds the gathered prior K and V only
+    n = ctypes.c_size_t(0)
+    assert lib.segmented_attention_workspace_size(32, 8, 8192, 128, 32768, ctypes.byref(n)) == _lib.CA_OK
+    assert n.value == 2 * 32768 * 8 * 128 * 2
+    assert lib.segmented_attention_workspace_size(32, 8, 8192, 128, 0, ctypes.byref(n)) == _lib.CA_OK
+    assert n.value == 0
