@@ -233,7 +233,7 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
     log("[bench] roofline: the INCL and STRICT step kernels alone")
     o = torch.empty((1, wl.H, n, wl.D), dtype=torch.float32, device=dev)
     lse = torch.empty((1, wl.H, n), dtype=torch.float32, device=dev)
-    reps = 10
+    reps = 30   # about 60 ms per figure: shorter windows caught clock transitions
     # in the pass, step 0 (the rank's own chunk) writes the running partial and every later
     # step folds its partial into it (ring_attn_step_fold): the roofline times that form
     incl = lambda: ca.ring_attn_step(qs[7], kp[7], vp[7], mask="causal_incl", out=o, lse=lse)  # noqa: E731
@@ -423,7 +423,7 @@ def run_constmax(args, torch, ca, workloads, gen, dev, clock):
     clk = clock.measure(torch, rp.run)
     acc = rp.acc
     cm_step = lambda: ca.ring_attn_const_max_step(q, kp[1], vp[1], rp.c, acc, 0)  # noqa: E731
-    k_ms = timed(torch, cm_step, 8)
+    k_ms = timed(torch, cm_step, 30)
     k_clk = clock.measure(torch, cm_step)
     res["constmax"] = {"ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
                        "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "clock_mhz": clk,
@@ -431,7 +431,7 @@ def run_constmax(args, torch, ca, workloads, gen, dev, clock):
                            k_ms, fl_step, "attn_step_bf16<1, 0, false> (ring_attn_const_max_step, accumulate phase)",
                            f"{fl_step / 1e12:.4f} TFLOP = 4*H*Sq*Sk*D, H=40 Sq=Sk=9450 D=128",
                            key="attn_step_bf16/wan22_720p_constmax",
-                           note="mean of 8 back-to-back launches on one stream")}
+                           note="mean of 30 back-to-back launches on one stream")}
     res["constmax"]["roofline"]["clock_mhz"] = k_clk
     rp.run()
     keep = {"wl": wl, "t": t, "out": rp.out.clone(), "lse": rp.lse.clone()}
@@ -458,7 +458,7 @@ def run_constmax(args, torch, ca, workloads, gen, dev, clock):
     ms_o = timed(torch, rp.run, reps)
     o = torch.empty((1, wl.H, wl.local_S, wl.D), dtype=torch.float32, device=dev)
     lse = torch.empty((1, wl.H, wl.local_S), dtype=torch.float32, device=dev)
-    k_on = timed(torch, lambda: ca.ring_attn_step(q, kp[1], vp[1], out=o, lse=lse), 8)
+    k_on = timed(torch, lambda: ca.ring_attn_step(q, kp[1], vp[1], out=o, lse=lse), 30)
     res["online"] = {"ms_per_pass": round(ms_o, 4), "tflops": round(fl / (ms_o * 1e-3) / 1e12, 2),
                      "form": "unsplit steps on two compute streams, each folding into a running partial, 2-way "
                              "LSE merge; hops on a copy stream",
