@@ -38,8 +38,9 @@
 //    while some row of the wave has no reference yet) does the wave find the tile's row
 //    maxima, raise the reference, rescale its accumulators and redo the tile. A full tile
 //    thus runs no max reduction at all, and probabilities stay <= 2^20;
-//  * causal masks: a workgroup visits key tiles up to its last row's diagonal; tiles
-//    past a wave's own diagonal are masked in full (every probability is 0).
+//  * causal masks: a workgroup visits key tiles up to its last row's diagonal; a wave skips
+//    the softmax and the matrix phase of the tiles past its own last row's diagonal (every
+//    probability there is 0), still copying its share of them and meeting every barrier.
 //
 // Key-split schedule (when the caller passes a workspace and one workgroup per query tile
 // would leave over a tenth of the device's workgroup slots idle, e.g. 160 tiles on 256
@@ -552,6 +553,8 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     // held in a scalar register, so the per-tile mask test is a scalar compare and branch)
     const int lane_lim = min(Skb, row_key_limit<MASK>(a, row));
     const int wave_lim = __builtin_amdgcn_readfirstlane(min(Skb, row_key_limit<MASK>(a, row_w0)));
+    // keys the wave's last row may see: a key tile at or past it is masked for every row of the wave
+    const int wave_hi = __builtin_amdgcn_readfirstlane(min(Skb, row_key_limit<MASK>(a, row_w0 + 31)));
     const int nk = max(k1 - k0, 0);   // key tiles of this segment
     // sink keys to leave out: lane l holds this head's l-th sink as a chunk-local index
     int my_sink = INT_MIN;
@@ -578,10 +581,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       settle(c2);
     }
 
-    // Issues the copies of the segment's key tile j into LDS buffer BUF. The last tile of a
-    // chunk clamps its rows to the last key (their scores are masked, their values meet p = 0).
-    auto issue = [&](auto bufc, int j) {
-      constexpr int BUF = decltype(bufc)::value;
+    // Issues the copies of the segment's key tile j into the LDS buffer at byte dst (K, then V
+    // at dst + V_OFF). The last tile of a chunk clamps its rows to the last key (their scores
+    // are masked, their values meet p = 0).
+    auto issue_to = [&](uint32_t dst, int j) {
       const int key0 = (k0 + j) * BK;
       const char* kt = kbase + key0 * kss_bytes;
       const char* vt = vbase + key0 * kss_bytes;
@@ -591,9 +594,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
         ko = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ k_swz(crow)) << 4);
         vo = uint32_t(rr * kss_bytes) + uint32_t((cchunk ^ v_swz(crow)) << 4);
       }
-      copy16_to_lds(kt, ko, lds_w + BUF * TILE_BYTES);
-      copy16_to_lds(vt, vo, lds_w + BUF * TILE_BYTES + V_OFF);
+      copy16_to_lds(kt, ko, dst);
+      copy16_to_lds(vt, vo, dst + V_OFF);
     };
+    auto issue = [&](auto bufc, int j) { issue_to(lds_w + decltype(bufc)::value * TILE_BYTES, j); };
 
     bf16x8 ka[8];    // K fragments of the tile whose scores the next matrix phase forms
     bf16x8 va[8];    // V fragments of the tile whose output update the next matrix phase does
@@ -716,19 +720,28 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       if (lagging) phase_barrier();
       matrix_phase(I0{}, true, false);   // scores and V fragments of tile 0
       reads_end_barrier();
+      // tiles from the first one masked for every row of this wave on (causal: past its last
+      // row's diagonal) carry no probability: the wave only copies its share of them and meets
+      // the barriers
+      const int n_live = MASK == CA_MASK_NONE ? nk : min(nk, max(1, (wave_hi - k0 * BK + BK - 1) / BK));
       for (int j = 0;; j += NBUF) {
         tile(I0{}, j);
-        if (j + 1 >= nk) break;
+        if (j + 1 >= n_live) break;
         tile(I1{}, j + 1);
-        if (j + 2 >= nk) break;
+        if (j + 2 >= n_live) break;
         tile(I2{}, j + 2);
-        if (j + 3 >= nk) break;
+        if (j + 3 >= n_live) break;
         tile(I3{}, j + 3);
-        if (j + 4 >= nk) break;
+        if (j + 4 >= n_live) break;
         tile(I4{}, j + 4);
-        if (j + 5 >= nk) break;
+        if (j + 5 >= n_live) break;
         tile(I5{}, j + 5);
-        if (j + 6 >= nk) break;
+        if (j + 6 >= n_live) break;
+      }
+      for (int j = n_live; j < nk; ++j) {
+        issue_to(lds_w + uint32_t((j + NBUF - 1) % NBUF) * TILE_BYTES, min(j + NBUF - 1, nk - 1));
+        phase_end<NBUF - 3>();
+        reads_end_barrier();
       }
       // every copy has landed and every wave is past its last LDS read before the buffers
       // are reused (next segment) or released
