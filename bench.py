@@ -64,7 +64,7 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
     "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
-                                                     "fetch_kib": 609597.0, "write_kib": 265710.1},
+                                                     "fetch_kib": 609844.5, "write_kib": 265705.3},
     "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
                                               "fetch_kib": 29352.9, "write_kib": 20641.6},
     "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
