@@ -87,10 +87,11 @@ class RingPass:
     tiles too few to fill the device), so each step's grid fills it; such steps run on one
     compute stream by default. Otherwise steps keep one workgroup per query tile and online
     steps alternate two compute streams, so a step can fill the CUs the previous one leaves
-    idle as it drains. compute_streams overrides either default. On the Wan2.2 share (160
-    query tiles of 256 rows per step) the fastest pass was split steps on two streams: 0.86 ms,
-    against 0.90 ms unsplit on one stream, 0.94 ms split on one and 0.96 ms unsplit on two
-    (timed with hops on the copy stream, before the split's regular cuts).
+    idle as it drains. compute_streams overrides either default. The copy stream and the
+    second compute stream come from streams.side_streams (each checked to overlap the calling
+    stream) unless copy_stream is given. On the Wan2.2 share (160 query tiles of 256 rows per
+    step) the fastest pass is unsplit steps on two streams with fused hops, each stream
+    folding: 0.687 ms, against 0.731 ms with key-split steps.
 
     fused_hops=True (no sinks): each step call carries the hop of the chunk two steps ahead
     (ring_attn_step_hop, or ring_attn_step_fold_hop when folding), on the CUs the step leaves
