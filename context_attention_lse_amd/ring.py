@@ -91,7 +91,8 @@ class RingPass:
     second compute stream come from streams.side_streams (each checked to overlap the calling
     stream) unless copy_stream is given. On the Wan2.2 share (160 query tiles of 256 rows per
     step) the fastest pass is unsplit steps on two streams with fused hops, each stream
-    folding: 0.687 ms, against 0.731 ms with key-split steps.
+    folding (0.687 ms); key-split steps on two streams, also carrying the hops, took 0.806 ms
+    against 0.731 ms for unsplit ones when the two were last compared (before the folding).
 
     fused_hops=True (no sinks): each step call carries the hop of the chunk two steps ahead
     (ring_attn_step_hop, or ring_attn_step_fold_hop when folding), on the CUs the step leaves
