@@ -639,9 +639,18 @@ def cpu_baseline_leg(h, kept, budget_s=12.0):
         el = float(np.abs(l_gpu[fin] - rl[fin]).max()) if fin.any() else 0.0
         return eo, el
 
-    def entry(eo, el, rows, what):
+    def entry(eo, el, rows, what, secs, scale_up, how):
+        # secs: oracle wall time on the sample; scale_up: the whole workload's result over the
+        # sample's (by rows, visible pairs or tokens, as `how` says)
         return {"max_abs_dO": eo, "max_abs_dLSE": el, "rows_checked": rows, "what": what,
-                "pass": bool(eo <= 2e-2 and el <= 1e-3)}
+                "pass": bool(eo <= 2e-2 and el <= 1e-3), "oracle_s": round(secs, 3),
+                "oracle_full_s": round(secs * scale_up, 1),
+                "oracle_full_how": "measured" if scale_up == 1 else f"extrapolated from the sample {how}"}
+
+    def timed_oracle(fn, *a):
+        t0 = time.perf_counter()
+        r = fn(*a)
+        return r, time.perf_counter() - t0
 
     # (1) headline rows
     wl, t = h["wl"], h["t"]
@@ -673,63 +682,72 @@ def cpu_baseline_leg(h, kept, budget_s=12.0):
            "sample": f"{rows_done} random query rows of the headline (random rank and head), each against every key "
                      f"it may see under the striped causal mask (fp64 numpy oracle, {t_total:.1f} s; the oracle "
                      f"scores every key and masks, so it does twice the algorithmic work counted)"}
-    parity[wl.name] = entry(eo, el, rows_done, "random rows of random ranks and heads, all visible keys")
+    parity[wl.name] = entry(eo, el, rows_done, "random rows of random ranks and heads, all visible keys", t_total,
+                            wl.H * S / rows_done, "by rows (every rank and head; each row costs the oracle all S keys)")
 
     # (2) other workloads
     if "wan22" in kept:
         k = kept["wan22"]
         w, tt = k["wl"], k["t"]
         tok = oracle.contiguous_tokens(w.S, w.cp, 0)
-        eo = el = 0.0
+        eo = el = secs = 0.0
         for hh in (0, w.H - 1):
-            ro, rl = oracle.attention(tt["q"][0, tok, hh].cpu(), tt["k"][0, :, hh].cpu(), tt["v"][0, :, hh].cpu(),
-                                      oracle.default_scale(w.D))
+            (ro, rl), dt = timed_oracle(oracle.attention, tt["q"][0, tok, hh].cpu(), tt["k"][0, :, hh].cpu(),
+                                        tt["v"][0, :, hh].cpu(), oracle.default_scale(w.D))
+            secs += dt
             e = err(k["out"][0, hh], k["lse"][0, hh], ro, rl)
             eo, el = max(eo, e[0]), max(el, e[1])
-        parity[w.name] = entry(eo, el, 2 * w.local_S, "every row of heads 0 and 9 of rank 0's pass")
+        parity[w.name] = entry(eo, el, 2 * w.local_S, "every row of heads 0 and 9 of rank 0's pass", secs, w.H / 2,
+                               "by rows (rank 0's pass, all heads)")
     if "constmax" in kept:
         k = kept["constmax"]
         w, tt = k["wl"], k["t"]
         tok = oracle.contiguous_tokens(w.S, w.cp, 0)
-        eo = el = 0.0
+        eo = el = secs = 0.0
         rows_n = 0
         for hh in (0, 13, 26, w.H - 1):
             rows = np.unique(np.concatenate([np.random.default_rng(hh).choice(w.local_S, 96, replace=False),
                                              np.arange(w.local_S - 106, w.local_S, 8)]))
-            ro, rl = oracle.attention(tt["q"][0, tok[rows], hh].cpu(), tt["k"][0, :, hh].cpu(),
-                                      tt["v"][0, :, hh].cpu(), oracle.default_scale(w.D))
+            (ro, rl), dt = timed_oracle(oracle.attention, tt["q"][0, tok[rows], hh].cpu(), tt["k"][0, :, hh].cpu(),
+                                        tt["v"][0, :, hh].cpu(), oracle.default_scale(w.D))
+            secs += dt
             ix = torch.from_numpy(rows).to(k["out"].device)
             e = err(k["out"][0, hh, ix], k["lse"][0, hh, ix], ro, rl)
             eo, el = max(eo, e[0]), max(el, e[1])
             rows_n += len(rows)
-        parity[w.name + "/constmax"] = entry(eo, el, rows_n, "random rows and the ragged tail of 4 heads")
+        parity[w.name + "/constmax"] = entry(eo, el, rows_n, "random rows and the ragged tail of 4 heads", secs,
+                                             w.H * w.local_S / rows_n, "by rows (rank 0's pass, all heads)")
     if "decode" in kept:
         k = kept["decode"]
         w, d = k["wl"], k["d"]
         G = w.Hq // w.Hkv
         ctx = d["ctx"]
         seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 7, 19})
-        eo = el = 0.0
+        eo = el = secs = 0.0
         for b in seqs:
             s0, s1 = int(d["offsets"][b]), int(d["offsets"][b + 1])
             for hk in range(w.Hkv):
                 hs = slice(hk * G, (hk + 1) * G)
-                ro, rl = oracle.attention(d["q"][b, hs].cpu(), d["k_seq"][s0:s1, hk].cpu(), d["v_seq"][s0:s1, hk].cpu(),
-                                          oracle.default_scale(w.D))
+                (ro, rl), dt = timed_oracle(oracle.attention, d["q"][b, hs].cpu(), d["k_seq"][s0:s1, hk].cpu(),
+                                            d["v_seq"][s0:s1, hk].cpu(), oracle.default_scale(w.D))
+                secs += dt
                 e = err(k["out"][b, hs], k["lse"][b, hs], ro, rl)
                 eo, el = max(eo, e[0]), max(el, e[1])
-        parity[w.name] = entry(eo, el, len(seqs) * w.Hq, f"sequences {seqs}, every query head, merged over both shards")
+        parity[w.name] = entry(eo, el, len(seqs) * w.Hq, f"sequences {seqs}, every query head, merged over both shards",
+                               secs, float(np.sum(ctx)) / float(np.sum(ctx[seqs])), "by context tokens")
     if "tiny" in kept:
         k = kept["tiny"]
         w, tt = k["wl"], k["t"]
         tok = oracle.contiguous_tokens(w.S, w.cp, 0)
-        ro, rl = oracle.attention_heads(tt["q"][:, tok].cpu(), tt["k"].cpu(), tt["v"].cpu(), oracle.default_scale(w.D))
+        (ro, rl), secs = timed_oracle(oracle.attention_heads, tt["q"][:, tok].cpu(), tt["k"].cpu(), tt["v"].cpu(),
+                                      oracle.default_scale(w.D))
         for variant in ("online", "constmax"):
             o, l = k[variant]
             e = err(o, l, ro, rl)
             parity[f"{w.name}/{variant}"] = {"max_abs_dO": e[0], "max_abs_dLSE": e[1], "rows_checked": w.local_S * w.H,
                                              "what": "every row (fp32 path; bar 1e-4 on both)",
-                                             "pass": bool(e[0] <= 1e-4 and e[1] <= 1e-4)}
+                                             "pass": bool(e[0] <= 1e-4 and e[1] <= 1e-4), "oracle_s": round(secs, 3),
+                                             "oracle_full_s": round(secs, 3), "oracle_full_how": "measured"}
     return cpu, parity
 
 
