@@ -96,10 +96,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // One 16-byte-per-lane copy HBM -> LDS: lane l reads base + off and its 16 bytes land at LDS
 // byte m0 + 16*l. Inline asm, so that the compiler neither waits for it before unrelated LDS
-// reads nor before barriers: the kernel places every wait for these copies itself.
+// reads nor before barriers: the kernel places every wait for these copies itself. The LDS
+// address is an input bound to m0 ("{m0}"), so the compiler writes m0 itself and knows the
+// register's value across the statement; the s_nop is the wait state an LDS-DMA load needs
+// after an SALU write of m0, which the compiler cannot see inside the asm.
 __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_byte), "v"(off), "s"(base) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "{m0}"(lds_byte), "v"(off), "s"(base) : "memory");
 }
 
 // End of a vector phase (which issues no LDS reads): at most 2*PENDING of this wave's tile
