@@ -63,14 +63,14 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
-                                                     "fetch_kib": 609844.5, "write_kib": 265705.3},
-    "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
+    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
+                                                     "fetch_kib": 610894.4, "write_kib": 265384.7},
+    "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
                                               "fetch_kib": 29352.9, "write_kib": 20641.6},
-    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
-                                                 "fetch_kib": 57384.6, "write_kib": 63000.0},
-    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "c5f84e368e664cee",
-                                           "fetch_kib": 331807.2, "write_kib": 190615.2},
+    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
+                                                 "fetch_kib": 57590.0, "write_kib": 63000.0},
+    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
+                                           "fetch_kib": 332356.9, "write_kib": 190625.0},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "974e5a7d3ee9555e",
                                   "fetch_kib": 2778066.0 + 14927.25, "write_kib": 31632.01 + 1040.01},
     "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
