@@ -51,12 +51,15 @@ ca_status check_dtype(int dtype) {
 }
 
 ca_status check_head_dim(int dtype, int D) {
-  if (dtype == CA_BF16 && D != 128)
-    return fail(CA_ERR_UNSUPPORTED, "bf16 attention supports head_dim 128 only (got %d)", D);
-  if (dtype == CA_FP32 && D != 64 && D != 128)
-    return fail(CA_ERR_UNSUPPORTED, "fp32 attention supports head_dim 64 or 128 (got %d)", D);
+  if (D != 64 && D != 128)
+    return fail(CA_ERR_UNSUPPORTED, "%s attention supports head_dim 64 or 128 (got %d)",
+                dtype == CA_BF16 ? "bf16" : "fp32", D);
   return CA_OK;
 }
+
+// The MFMA step kernel takes bf16 with head_dim 128; every other supported case (fp32, and
+// bf16 with head_dim 64) runs on the fp32 vector kernel.
+bool mfma_step(int dtype, int D) { return dtype == CA_BF16 && D == 128; }
 
 #define CA_TRY(expr)                 \
   do {                               \
@@ -78,7 +81,7 @@ ca_status attn_common(const void* q, ca_strides qs, const void* k, const void* v
 // Hands a caller workspace to the bf16 step, which then splits key ranges across a grid
 // that fills the device. NULL keeps one workgroup per query tile; the fp32 step never splits.
 ca_status attach_workspace(ctxattn::AttnArgs& a, int dtype, void* ws, size_t ws_bytes) {
-  if (!ws || dtype != CA_BF16) return CA_OK;
+  if (!ws || !mfma_step(dtype, a.D)) return CA_OK;
   const size_t need = ctxattn::attn_bf16_workspace_bytes(a.B, a.H, a.Sq, a.Sk, a.mask);
   if (need == 0) return CA_OK;
   if (ws_bytes < need)
@@ -116,7 +119,8 @@ constexpr int kMaxHopWorkgroups = 64;
 // launches it as an ordinary copy ahead of the step on the same stream.
 static hipError_t attach_hop(ctxattn::AttnArgs& a, const Hop& hop, int dtype, int mask, hipStream_t s) {
   if (hop.bytes == 0) return hipSuccess;
-  const int idle = dtype == CA_BF16 ? ctxattn::attn_bf16_idle_slots(a.B, a.H, a.Sq, a.Sk, mask, a.ws != nullptr) : 0;
+  const int idle =
+      mfma_step(dtype, a.D) ? ctxattn::attn_bf16_idle_slots(a.B, a.H, a.Sq, a.Sk, mask, a.ws != nullptr) : 0;
   if (idle < kMinHopWorkgroups) return ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, s);
   a.hop_sk = hop.sk; a.hop_sv = hop.sv; a.hop_dk = hop.dk; a.hop_dv = hop.dv;
   a.hop_units = int64_t(hop.bytes / 16);
@@ -160,7 +164,8 @@ static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = attach_hop(a, hop, dtype, mask, s);
   if (e != hipSuccess) return hip_status(e, name);
-  e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, false, s) : ctxattn::launch_attn_f32(a, false, s);
+  e = mfma_step(dtype, D) ? ctxattn::launch_attn_bf16(a, false, s)
+                          : ctxattn::launch_attn_f32(a, false, dtype == CA_BF16, s);
   return hip_status(e, name);
 }
 
@@ -206,7 +211,7 @@ ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int 
   CA_TRY(check_head_dim(dtype, D));
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0) return fail(CA_ERR_SHAPE, "negative size");
   if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
-  if (dtype == CA_BF16) *bytes = ctxattn::attn_bf16_workspace_bytes(B, H, Sq, Sk, mask);
+  if (mfma_step(dtype, D)) *bytes = ctxattn::attn_bf16_workspace_bytes(B, H, Sq, Sk, mask);
   return hip_status(hipSuccess, "");
 }
 
@@ -277,7 +282,7 @@ ca_status const_max_step_impl(const void* q, ca_strides qs, const void* k, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = attach_hop(a, hop, dtype, CA_MASK_NONE, s);
   if (e != hipSuccess) return hip_status(e, "ring_attn_const_max_step launch");
-  e = dtype == CA_BF16 ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, s);
+  e = mfma_step(dtype, D) ? ctxattn::launch_attn_bf16(a, true, s) : ctxattn::launch_attn_f32(a, true, dtype == CA_BF16, s);
   return hip_status(e, "ring_attn_const_max_step launch");
 }
 
@@ -310,7 +315,9 @@ ca_status ring_attn_const_max_step_sinks(const void* q, ca_strides qs, const voi
                                          int o_dtype, float* lse, const int32_t* sink_idx, const int32_t* sink_cnt,
                                          int sink_cap, int64_t key_offset, void* workspace, size_t workspace_bytes,
                                          void* stream) {
-  if (dtype != CA_BF16) return fail(CA_ERR_UNSUPPORTED, "sink lists need the bf16 path");
+  if (dtype != CA_BF16 || D != 128)
+    return fail(CA_ERR_UNSUPPORTED, "sink lists need the bf16 MFMA path (bf16, head_dim 128; got %s, %d)",
+                dtype == CA_BF16 ? "bf16" : "fp32", D);
   if (sink_cap < 1 || sink_cap > 64) return fail(CA_ERR_UNSUPPORTED, "sink_cap must be in [1, 64] (got %d)", sink_cap);
   if (int64_t(B) * H * Sq > 0 && (!sink_idx || !sink_cnt)) return fail(CA_ERR_NULL, "sink_idx and sink_cnt are required");
   if (key_offset < 0) return fail(CA_ERR_SHAPE, "negative key_offset");

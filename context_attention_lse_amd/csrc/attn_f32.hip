@@ -1,9 +1,12 @@
-// fp32 attention step kernels (online-max and const-max) for fp32 inputs.
+// Vector (VALU) attention step kernels, online-max and const-max, with fp32 arithmetic.
 //
-// Same two methods as the bf16 path (see attn_bf16.hip), computed with fp32 vector
-// FMAs and accurate expf/logf, for inputs that are fp32 end to end: a bf16 rounding of
-// fp32 inputs would be charged to the scores. Two lanes share one query row, each
-// holding half of the head dimension; keys stream through LDS in tiles of 32.
+// Same two methods as the MFMA path (see attn_bf16.hip), computed with fp32 vector FMAs and
+// accurate expf/logf. They serve inputs the MFMA kernel does not take: fp32 inputs end to
+// end (a bf16 rounding of fp32 inputs would be charged to the scores), and bf16 inputs with
+// head_dim 64 (the MFMA kernel is built for 128, the head size the kernel reference page's
+// Interface asserts), whose elements are widened to fp32 as they are loaded. Two lanes
+// share one query row, each holding half of the head dimension; keys stream through LDS in
+// fp32 tiles of 32.
 #include "internal.hpp"
 
 namespace ctxattn {
@@ -15,7 +18,17 @@ constexpr int TK = 32;         // keys per LDS tile
 
 enum { MODE_ONLINE = 0, MODE_CONSTMAX = 1 };
 
-template <int MODE, int MASK, int D>
+// Element loads widened to fp32: T = float (fp32 inputs) or uint16_t (bf16 bits).
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const uint16_t* p) { return bf16_bits_to_float(*p); }
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {   // 8-byte aligned: 4 elements of a 16-byte-aligned row
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <int MODE, int MASK, int D, typename T>
 __global__ __launch_bounds__(NT) void attn_step_f32(const AttnArgs a, int nqb) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float Ks[TK][D];
@@ -32,14 +45,14 @@ __global__ __launch_bounds__(NT) void attn_step_f32(const AttnArgs a, int nqb) {
   const bool live_row = i < Sq;
 
   float q[DH], acc[DH];
-  const float* qrow = static_cast<const float*>(a.q) + b * a.qsb + int64_t(live_row ? i : 0) * a.qss + h * a.qsh + half * DH;
+  const T* qrow = static_cast<const T*>(a.q) + b * a.qsb + int64_t(live_row ? i : 0) * a.qss + h * a.qsh + half * DH;
 #pragma unroll
   for (int d = 0; d < DH; ++d) {
-    q[d] = live_row ? qrow[d] : 0.0f;
+    q[d] = live_row ? load1(qrow + d) : 0.0f;
     acc[d] = 0.0f;
   }
-  const float* kbase = static_cast<const float*>(a.k) + b * a.ksb + h * a.ksh;
-  const float* vbase = static_cast<const float*>(a.v) + b * a.ksb + h * a.ksh;
+  const T* kbase = static_cast<const T*>(a.k) + b * a.ksb + h * a.ksh;
+  const T* vbase = static_cast<const T*>(a.v) + b * a.ksb + h * a.ksh;
 
   float m = -INFINITY, l = 0.0f, c = 0.0f;
   if (MODE == MODE_CONSTMAX && live_row) c = a.c[int64_t(bh) * Sq + i];
@@ -55,8 +68,8 @@ __global__ __launch_bounds__(NT) void attn_step_f32(const AttnArgs a, int nqb) {
       const int key = key0 + row;
       float4 kv = make_float4(0, 0, 0, 0), vv = kv;
       if (key < Sk) {
-        kv = *reinterpret_cast<const float4*>(kbase + key * a.kss + col);
-        vv = *reinterpret_cast<const float4*>(vbase + key * a.kss + col);
+        kv = load4(kbase + key * a.kss + col);
+        vv = load4(vbase + key * a.kss + col);
       }
       *reinterpret_cast<float4*>(&Ks[row][col]) = kv;
       *reinterpret_cast<float4*>(&Vs[row][col]) = vv;
@@ -152,29 +165,30 @@ __global__ __launch_bounds__(NT) void attn_step_f32(const AttnArgs a, int nqb) {
   }
 }
 
-template <int MODE, int MASK, int D>
+template <int MODE, int MASK, int D, typename T>
 hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.Sq + ROWS - 1) / ROWS;
   const int64_t nblk = int64_t(a.B) * a.H * nqb;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_step_f32<MODE, MASK, D>), dim3(unsigned(nblk)), dim3(NT), 0, s, a, nqb);
+  hipLaunchKernelGGL((attn_step_f32<MODE, MASK, D, T>), dim3(unsigned(nblk)), dim3(NT), 0, s, a, nqb);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename T>
 hipError_t dispatch(const AttnArgs& a, bool const_max, hipStream_t s) {
-  if (const_max) return launch_one<MODE_CONSTMAX, CA_MASK_NONE, D>(a, s);
+  if (const_max) return launch_one<MODE_CONSTMAX, CA_MASK_NONE, D, T>(a, s);
   switch (a.mask) {
-    case CA_MASK_CAUSAL_INCL: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_INCL, D>(a, s);
-    case CA_MASK_CAUSAL_STRICT: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_STRICT, D>(a, s);
-    default: return launch_one<MODE_ONLINE, CA_MASK_NONE, D>(a, s);
+    case CA_MASK_CAUSAL_INCL: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_INCL, D, T>(a, s);
+    case CA_MASK_CAUSAL_STRICT: return launch_one<MODE_ONLINE, CA_MASK_CAUSAL_STRICT, D, T>(a, s);
+    default: return launch_one<MODE_ONLINE, CA_MASK_NONE, D, T>(a, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_f32(const AttnArgs& a, bool const_max, hipStream_t s) {
-  return a.D == 64 ? dispatch<64>(a, const_max, s) : dispatch<128>(a, const_max, s);
+hipError_t launch_attn_f32(const AttnArgs& a, bool const_max, bool bf16_in, hipStream_t s) {
+  if (bf16_in) return dispatch<64, uint16_t>(a, const_max, s);   // bf16 reaches here with D == 64 only
+  return a.D == 64 ? dispatch<64, float>(a, const_max, s) : dispatch<128, float>(a, const_max, s);
 }
 
 }  // namespace ctxattn

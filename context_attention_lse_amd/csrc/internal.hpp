@@ -130,7 +130,7 @@ hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s);
 // Bytes of key-split workspace the bf16 step needs for these sizes on the current device
 // (0: the call has no key tiles and never splits).
 size_t attn_bf16_workspace_bytes(int B, int H, int Sq, int Sk, int mask);
-hipError_t launch_attn_f32(const AttnArgs& a, bool const_max, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, bool const_max, bool bf16_in, hipStream_t s);
 hipError_t launch_lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t rows,
                             int D, void* o_out, int o_bf16, float* lse_out, hipStream_t s);
 hipError_t launch_key_sqnorm_max(const void* k, int64_t sb, int64_t ss, int64_t sh, bool bf16,

@@ -99,10 +99,11 @@ typedef struct {
  *          the library, in key order (results do not depend on timing). The workspace must
  *          be 256-byte aligned and all zero before its first use; every call leaves it
  *          ready for the next. Calls that may run at the same time need separate
- *          workspaces. Ignored by the fp32 path and by calls that do not split.
- * Supported: D in {64, 128} (fp32), D == 128 (bf16; the kernel reference page's
- * Interface asserts d == 128 for this kernel, so bf16 D == 64 returns
- * CA_ERR_UNSUPPORTED); MHA (same H for q and kv). Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
+ *          workspaces. Ignored by the vector kernel (below) and by calls that do not split.
+ * Supported: D in {64, 128} for both dtypes; MHA (same H for q and kv). bf16 with D == 128
+ * runs on the MFMA kernel (the head size the kernel reference page's Interface asserts);
+ * fp32, and bf16 with D == 64, run on a vector kernel with fp32 arithmetic (bf16 elements
+ * widened as loaded), which never splits and is several times slower. Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
  * CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_WORKSPACE (too small), CA_ERR_HIP.
  */
 ca_status ring_attn_step(const void* q, ca_strides q_strides,

@@ -18,9 +18,11 @@ TOL_O_F32 = 1e-4
 TOL_LSE_F32 = 1e-4
 
 
-def tol(dtype):
-    """(output bar, LSE bar) for an input dtype name ("bf16" or "fp32")."""
-    return (TOL_O_F32, TOL_LSE_F32) if dtype == "fp32" else (TOL_O, TOL_LSE)
+def tol(dtype, D=128):
+    """(output bar, LSE bar) of a step for an input dtype name ("bf16" or "fp32") and head dim.
+    bf16 with head_dim 64 runs on the fp32 vector kernel, like fp32 inputs: its bf16 inputs are
+    exact in fp32 and no probability is rounded to bf16, so it is held to the fp32 bar."""
+    return (TOL_O_F32, TOL_LSE_F32) if dtype == "fp32" or D == 64 else (TOL_O, TOL_LSE)
 
 
 def say(msg):

@@ -46,9 +46,13 @@ def test_rejections_without_gpu():
     st = _lib.ca_strides(0, 128, 0)
     # unknown dtype
     assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, 9, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_DTYPE
-    # bf16 head_dim other than 128
+    # bf16 head_dim other than 64 and 128
     assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 96, 0.0, 0, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_UNSUPPORTED
-    assert b"128" in lib.ca_last_error()
+    assert b"64 or 128" in lib.ca_last_error()
+    # sink lists need bf16 with head_dim 128 (the MFMA kernel)
+    assert lib.ring_attn_const_max_step_sinks(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 64, 0.0,
+                                              _fake(), _fake(), 0, None, 0, None, _fake(), _fake(), 8, 0, None, 0,
+                                              None) == _lib.CA_ERR_UNSUPPORTED
     # unknown mask
     assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 7, _fake(), _fake(), None, 0, None) == _lib.CA_ERR_UNSUPPORTED
     # NULL inputs
@@ -90,6 +94,10 @@ def test_rejections_without_gpu():
     assert lib.ring_attn_workspace_size(_lib.CA_BF16, 1, 2, 300, 300, 128, 2, ctypes.byref(n)) == _lib.CA_OK
     assert n.value > 0
     assert lib.ring_attn_workspace_size(_lib.CA_BF16, 1, 2, 300, 300, 128, 9, ctypes.byref(n)) == _lib.CA_ERR_UNSUPPORTED
+    # bf16 with head_dim 64 runs on the vector kernel, which never splits
+    n = ctypes.c_size_t(1)
+    assert lib.ring_attn_workspace_size(_lib.CA_BF16, 1, 2, 300, 300, 64, 0, ctypes.byref(n)) == _lib.CA_OK
+    assert n.value == 0
     assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(),
                               _fake(0x10000), 16, None) == _lib.CA_ERR_WORKSPACE
     assert lib.ring_attn_step(_fake(), st, _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 4, 128, 0.0, 0, _fake(), _fake(),
