@@ -71,8 +71,8 @@ TRAFFIC = {
                                                  "fetch_kib": 57590.0, "write_kib": 63000.0},
     "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
                                            "fetch_kib": 332356.9, "write_kib": 190625.0},
-    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "974e5a7d3ee9555e",
-                                  "fetch_kib": 2778066.0 + 14927.25, "write_kib": 31632.01 + 1040.01},
+    "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "a324b829ca6b6ff4",
+                                  "fetch_kib": 2778052.6 + 14932.25, "write_kib": 31631.8 + 1040.0},
     "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
                                       "fetch_kib": 779655.5, "write_kib": 190477.2},
     "const_max_bound/wan22_720p_constmax": {"source": "bound.hip", "sha256": "5c362a4869e5af73",

@@ -431,7 +431,7 @@ ca_status decode_launch(const char* name, const void* q, const void* k_pool, con
                         int Hkv, int D, int block_size, int max_blocks, int num_blocks, float softmax_scale, float* o,
                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_blocks < 0 || num_blocks < 0) return fail(CA_ERR_SHAPE, "bad sizes");
-  if (D != 128) return fail(CA_ERR_UNSUPPORTED, "decode supports head_dim 128 only (got %d)", D);
+  if (D != 64 && D != 128) return fail(CA_ERR_UNSUPPORTED, "decode supports head_dim 64 or 128 (got %d)", D);
   if (block_size != 16) return fail(CA_ERR_UNSUPPORTED, "decode supports block_size 16 only (got %d)", block_size);
   if (Hq % Hkv) return fail(CA_ERR_UNSUPPORTED, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (Hq / Hkv > 16) return fail(CA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", Hq / Hkv);

@@ -13,13 +13,14 @@
 //  * V blocks are stored d-major ([D][16] per block and head), so the P.V product
 //    O^T = V^T P^T loads its A operand with 8-byte reads and P never leaves registers;
 //  * the four waves' partials fold in LDS into one (output, LSE) per split, and a
-//    second kernel folds the splits of each sequence by the LSE rule.
+//    second kernel folds the splits of each sequence by the LSE rule;
+//  * head_dim D = 128 or 64 (a template parameter): D/32 score MFMAs and D/16 output
+//    MFMAs per block.
 #include "internal.hpp"
 
 namespace ctxattn {
 namespace {
 
-constexpr int D = 128;
 constexpr int BS = 16;                          // tokens per cache block
 constexpr int NT = 256;
 constexpr int WAVES = NT / 64;
@@ -28,27 +29,29 @@ constexpr int WAVE_BLOCKS = SPLIT_BLOCKS / WAVES;       // 24
 static_assert(WAVE_BLOCKS % 2 == 0 && WAVE_BLOCKS <= 32, "block pairs per wave; one mask bit per block");
 constexpr float kRescaleSlack = 8.0f;
 
+template <int D>
 struct PairRegs {
-  uint4 k[2][4];   // [block][d chunk of 32]: 8 bf16 of row (token) c16
-  uint2 v[2][8];   // [block][d block of 16]: 4 bf16 (tokens 4g..4g+3) at d = 16*db + c16
+  uint4 k[2][D / 32];   // [block][d chunk of 32]: 8 bf16 of row (token) c16
+  uint2 v[2][D / 16];   // [block][d block of 16]: 4 bf16 (tokens 4g..4g+3) at d = 16*db + c16
 };
 
 // Loads one block pair; blk0 and blk1 are wave-uniform physical block ids, always inside
 // the pool (the caller substitutes a resident block for missing ones), so the loads carry
 // no branches and the compiler's wait counts stay exact.
-__device__ __forceinline__ void load_pair(PairRegs& r, const uint16_t* kp, const uint16_t* vp, int hkv, int Hkv,
+template <int D>
+__device__ __forceinline__ void load_pair(PairRegs<D>& r, const uint16_t* kp, const uint16_t* vp, int hkv, int Hkv,
                                           int blk0, int blk1, int g, int c16) {
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi) {
     const int64_t blk = bi == 0 ? blk0 : blk1;
     const uint16_t* kb = kp + ((blk * Hkv + hkv) * BS + c16) * D + 8 * g;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) r.k[bi][cc] = *reinterpret_cast<const uint4*>(kb + 32 * cc);
+    for (int cc = 0; cc < D / 32; ++cc) r.k[bi][cc] = *reinterpret_cast<const uint4*>(kb + 32 * cc);
     // V rows stream past the caches (non-temporal): 2.9% faster per shard than ordinary loads;
     // the same for K was 7% slower (interleaved A/B on the decode workload)
     const uint16_t* vb = vp + ((blk * Hkv + hkv) * D + c16) * BS + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < D / 16; ++db) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + 16 * BS * db));
       r.v[bi][db] = make_uint2(t[0], t[1]);
@@ -64,6 +67,7 @@ __device__ __forceinline__ int resident_len(const DecodeArgs& a, int b) {
   return min(max(n, 0), a.max_blocks * BS);
 }
 
+template <int D>
 __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArgs a) {
   __shared__ float s_o[WAVES][16][D];
   __shared__ float s_m[WAVES][16];
@@ -86,9 +90,9 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
 
   // Q fragment: head c16 of the group (zero beyond G), d = 32*cc + 8*g .. +7.
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (int64_t(b) * a.Hq + hkv * G + min(c16, G - 1)) * D + 8 * g;
-  bf16x8 qf[4];
+  bf16x8 qf[D / 32];
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
+  for (int cc = 0; cc < D / 32; ++cc) {
     uint4 t = c16 < G ? *reinterpret_cast<const uint4*>(qh + 32 * cc) : make_uint4(0, 0, 0, 0);
     qf[cc] = *reinterpret_cast<bf16x8*>(&t);
   }
@@ -98,22 +102,22 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   const int32_t* btab = a.block_table + int64_t(b) * a.max_blocks;
   const int wave_blk0 = split * SPLIT_BLOCKS + w * WAVE_BLOCKS;
 
-  floatx4 oacc[8];
+  floatx4 oacc[D / 16];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < D / 16; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;
   float l_part = 0.0f;
   const float sl2e = a.sl2e;
 
   // Block pairs stream through a ring of three register sets: the loads of pair it + 2 are
   // issued before pair it is computed, so two pairs (32 KB per wave) stay in flight.
-  auto compute = [&](const PairRegs& cur, int jb0, uint32_t zero2) {
+  auto compute = [&](const PairRegs<D>& cur, int jb0, uint32_t zero2) {
     floatx4 s[2];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
       s[bi] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int cc = 0; cc < D / 32; ++cc) {
         bf16x8 kf = *reinterpret_cast<const bf16x8*>(&cur.k[bi][cc]);
         s[bi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cc], s[bi], 0, 0, 0);
       }
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
       const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_ref - m_new);
       l_part *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
       m_ref = m_new;
     }
     const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
     const bf16x8 pb = *reinterpret_cast<bf16x8*>(&pk);
     const bool z0 = zero2 & 1, z1 = (zero2 >> 1) & 1;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < D / 16; ++db) {
       uint4 vv = make_uint4(z0 ? 0u : cur.v[0][db].x, z0 ? 0u : cur.v[0][db].y, z1 ? 0u : cur.v[1][db].x,
                             z1 ? 0u : cur.v[1][db].y);
       const bf16x8 vf = *reinterpret_cast<bf16x8*>(&vv);
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   }
 
   constexpr int PAIRS = WAVE_BLOCKS / 2;
-  PairRegs ring[3];
+  PairRegs<D> ring[3];
   load_pair(ring[0], kp, vp, hkv, a.Hkv, bid[0], bid[1], g, c16);
   load_pair(ring[1], kp, vp, hkv, a.Hkv, bid[2], bid[3], g, c16);
 #pragma unroll
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   // oacc[db][r]: O^T[d = 16*db + 4*g + r][head c16] (unnormalised, reference m_ref)
   if (c16 < G) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < D / 16; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_o[w][c16][16 * db + 4 * g + r] = oacc[db][r];
     if (g == 0) {
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
   }
   __syncthreads();
 
-  // Fold the 4 waves: G heads x 128 d outputs, 8 per thread.
+  // Fold the 4 waves: G heads x D outputs.
   const int64_t slot0 = (int64_t(b) * a.Hq + hkv * G) * a.max_splits + split;
   for (int e = tid; e < G * D; e += NT) {
     const int hh = e / D;
@@ -233,11 +237,16 @@ __global__ __launch_bounds__(NT, 2) void dcp_decode_split_kernel(const DecodeArg
 }
 
 // One wave per row (sequence, query head) folds that sequence's splits: lane i holds split
-// i's LSE (64 at a time) for the weights; for the outputs, the two half-waves take
-// alternate splits, each lane four consecutive d, eight splits' loads in flight per round.
+// i's LSE (64 at a time) for the weights; for the outputs, the wave's lanes form 128 / D
+// groups of D / 4 lanes (two half-waves for D = 128, four quarter-waves for D = 64) that
+// take alternate splits, each lane four consecutive d, eight splits' loads in flight per round.
 constexpr int COMBINE_WAVES = NT / 64;
 
+template <int D>
 __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs a) {
+  constexpr int LPR = D / 4;     // lanes holding one row's D outputs
+  constexpr int NG = 64 / LPR;   // lane groups, each taking every NG-th split
+  constexpr int U = 8 / NG;      // loads per lane per round of eight splits
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * COMBINE_WAVES + (threadIdx.x >> 6);
   if (row >= int64_t(a.B) * a.Hq) return;   // wave-uniform
@@ -245,8 +254,8 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
   const int len = resident_len(a, b);
   const int n = (len + kDecodeSplitTokens - 1) / kDecodeSplitTokens;
   const float* lp = a.ws_lse + row * a.max_splits;
-  const int half = lane >> 5;
-  const int col = (lane & 31) * 4;
+  const int grp = lane / LPR;
+  const int col = (lane % LPR) * 4;
   const float* op = a.ws_o + row * a.max_splits * D + col;
 
   // Current-token form: on the owner of position N the current token is one more part,
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
       dot = fmaf(bf16_bits_to_float(qb.x >> 16), bf16_bits_to_float(kb.x >> 16), dot);
       dot = fmaf(bf16_bits_to_float(qb.y & 0xffffu), bf16_bits_to_float(kb.y & 0xffffu), dot);
       dot = fmaf(bf16_bits_to_float(qb.y >> 16), bf16_bits_to_float(kb.y >> 16), dot);
-      s_cur = a.scale * wave_sum(half == 0 ? dot : 0.0f);
+      s_cur = a.scale * wave_sum(grp == 0 ? dot : 0.0f);
       v_cur = make_float4(bf16_bits_to_float(vb.x & 0xffffu), bf16_bits_to_float(vb.x >> 16),
                           bf16_bits_to_float(vb.y & 0xffffu), bf16_bits_to_float(vb.y >> 16));
     }
@@ -284,17 +293,17 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
       total += wl;
       const int cnt = min(64, n - s0);
       for (int s = 0; s < cnt; s += 8) {
-        float4 v[4];
-        float wt[4];
+        float4 v[U];
+        float wt[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j = s + 2 * u + half;   // split s0 + j of this half-wave
+        for (int u = 0; u < U; ++u) {
+          const int j = s + NG * u + grp;   // split s0 + j of this lane group
           wt[u] = __shfl(wl, j & 63);
           v[u] = j < cnt ? *reinterpret_cast<const float4*>(op + int64_t(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float w = s + 2 * u + half < cnt ? wt[u] : 0.0f;
+        for (int u = 0; u < U; ++u) {
+          const float w = s + NG * u + grp < cnt ? wt[u] : 0.0f;
           acc.x = fmaf(w, v[u].x, acc.x); acc.y = fmaf(w, v[u].y, acc.y);
           acc.z = fmaf(w, v[u].z, acc.z); acc.w = fmaf(w, v[u].w, acc.w);
         }
@@ -304,16 +313,19 @@ __global__ __launch_bounds__(NT) void dcp_decode_combine_kernel(const DecodeArgs
     if (cur) {
       const float wc = __expf(s_cur - M);
       total += wc;
-      if (half == 0) {
+      if (grp == 0) {
         acc.x = fmaf(wc, v_cur.x, acc.x); acc.y = fmaf(wc, v_cur.y, acc.y);
         acc.z = fmaf(wc, v_cur.z, acc.z); acc.w = fmaf(wc, v_cur.w, acc.w);
       }
     }
   }
-  // the two halves hold disjoint splits of the same four d: add them
-  acc.x += __shfl_xor(acc.x, 32); acc.y += __shfl_xor(acc.y, 32);
-  acc.z += __shfl_xor(acc.z, 32); acc.w += __shfl_xor(acc.w, 32);
-  if (half == 0) {
+  // the lane groups hold disjoint splits of the same four d: add them
+#pragma unroll
+  for (int m = LPR; m < 64; m *= 2) {
+    acc.x += __shfl_xor(acc.x, m); acc.y += __shfl_xor(acc.y, m);
+    acc.z += __shfl_xor(acc.z, m); acc.w += __shfl_xor(acc.w, m);
+  }
+  if (grp == 0) {
     const float inv = total > 0.0f ? 1.0f / total : 0.0f;
     *reinterpret_cast<float4*>(a.o + row * D + col) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     if (col == 0) a.lse[row] = total > 0.0f ? M + __logf(total) : -INFINITY;
@@ -329,17 +341,26 @@ size_t decode_workspace_bytes(int B, int Hq, int D_, int block_size, int max_blo
   return size_t(rows) * (size_t(D_) + 1) * sizeof(float);
 }
 
-hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
+namespace {
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t s) {
   if (a.max_splits > 0) {
-    hipLaunchKernelGGL(dcp_decode_split_kernel, dim3(a.max_splits, a.Hkv, a.B), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(dcp_decode_split_kernel<D>, dim3(a.max_splits, a.Hkv, a.B), dim3(NT), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t rows = int64_t(a.B) * a.Hq;
-  hipLaunchKernelGGL(dcp_decode_combine_kernel, dim3(unsigned((rows + COMBINE_WAVES - 1) / COMBINE_WAVES)), dim3(NT), 0,
-                     s, a);
+  hipLaunchKernelGGL(dcp_decode_combine_kernel<D>, dim3(unsigned((rows + COMBINE_WAVES - 1) / COMBINE_WAVES)),
+                     dim3(NT), 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dcp_decode(const DecodeArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  return a.D == 64 ? launch_decode_d<64>(a, s) : launch_decode_d<128>(a, s);
 }
 
 }  // namespace ctxattn

@@ -384,7 +384,7 @@ ca_status lse_merge(int n, const float* o_parts, const float* lse_parts, int64_t
  *                (local_filled); values are clamped to [0, max_blocks * block_size]
  *   o            OUT [B, Hq, D] fp32 partial output; lse OUT [B, Hq] fp32
  *   workspace    device scratch of at least dcp_decode_workspace_size() bytes
- * Query head h uses KV head h / (Hq / Hkv). Supported: D == 128, block_size == 16,
+ * Query head h uses KV head h / (Hq / Hkv). Supported: D in {64, 128}, block_size == 16,
  * Hq % Hkv == 0, Hq / Hkv <= 16. A sequence with local_lens 0 yields o = 0, lse = -inf.
  */
 ca_status dcp_decode_partial(const void* q, const void* k_pool, const void* v_pool,

@@ -67,8 +67,10 @@ def test_rejections_without_gpu():
     assert lib.lse_merge(0, _fake(), _fake(), 4, 128, _fake(0x9000), 1, None, None) == _lib.CA_ERR_SHAPE
     assert lib.lse_merge(2, _fake(), _fake(), 4, 96, _fake(0x9000), 1, None, None) == _lib.CA_ERR_UNSUPPORTED
     assert lib.lse_merge(2, _fake(0x1000), _fake(), 4, 128, _fake(0x1400), 1, None, None) == _lib.CA_ERR_SHAPE
-    # decode: GQA group above 16, wrong block size, small workspace
+    # decode: head_dim other than 64 and 128, GQA group above 16, wrong block size, small workspace
     args = (_fake(), _fake(), _fake(), _fake(), _fake())
+    assert lib.dcp_decode_partial(*args, 2, 64, 8, 96, 16, 8, 100, 0.0, _fake(), _fake(), _fake(), 1 << 30, None) == _lib.CA_ERR_UNSUPPORTED
+    assert b"64 or 128" in lib.ca_last_error()
     assert lib.dcp_decode_partial(*args, 2, 64, 2, 128, 16, 8, 100, 0.0, _fake(), _fake(), _fake(), 1 << 30, None) == _lib.CA_ERR_UNSUPPORTED
     assert lib.dcp_decode_partial(*args, 2, 64, 8, 128, 32, 8, 100, 0.0, _fake(), _fake(), _fake(), 1 << 30, None) == _lib.CA_ERR_UNSUPPORTED
     assert lib.dcp_decode_partial(*args, 2, 64, 8, 128, 16, 8, 100, 0.0, _fake(), _fake(), _fake(), 16, None) == _lib.CA_ERR_WORKSPACE

@@ -432,11 +432,11 @@ def test_ring_rejects_indivisible_length(dev):
 
 # ---------------------------------------------------------------- DCP decode
 
-def _decode_case(dev, B, Hq, Hkv, ctx, world=2, interleave=16, seed=4):
+def _decode_case(dev, B, Hq, Hkv, ctx, world=2, interleave=16, seed=4, D=128):
     ca = _ca()
     wl = workloads.workload("dcp_decode_gqa").scaled(B=B, Hq=Hq, Hkv=Hkv, ctx_override=tuple(ctx), seed=seed,
-                                                     shards=world, interleave=interleave)
-    say(f"decode B={B} Hq={Hq} Hkv={Hkv} ctx={ctx} world={world}")
+                                                     shards=world, interleave=interleave, D=D)
+    say(f"decode B={B} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} world={world}")
     d = gen.decode_inputs(wl, dev)
     shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], d["ctx"], r, world, interleave, 16,
                                        d["block_rand"]) for r in range(world)]
@@ -464,6 +464,12 @@ def test_decode_gqa_groups(dev, Hq, Hkv):
     _decode_case(dev, 3, Hq, Hkv, (33, 2049, 700))
 
 
+def test_decode_head_dim_64(dev):
+    """head_dim 64: contexts that span several 1536-token splits per shard (the combine's
+    four lane groups each take every fourth split), one token, and GQA groups of 4."""
+    _decode_case(dev, 4, 32, 8, (33, 9000, 4100, 1), D=64)
+
+
 def test_decode_four_shards_and_empty_shard(dev):
     run = _decode_case(dev, 2, 16, 4, (5, 1100), world=4)
     # a 5-token context lives entirely on shard 0: the others are empty for it
@@ -474,14 +480,14 @@ def test_decode_four_shards_and_empty_shard(dev):
 
 # ---------------------------------------------------------------- DCP decode with the current token
 
-def _decode_active_case(dev, B, Hq, Hkv, prior, world, interleave, seed=5):
+def _decode_active_case(dev, B, Hq, Hkv, prior, world, interleave, seed=5, D=128):
     """Sequences of prior + 1 tokens: the shards hold the first N (positions [0, N)), the
     last one is the current token, attended only by the shard that owns position N."""
     ca = _ca()
     ctx = tuple(n + 1 for n in prior)
     wl = workloads.workload("dcp_decode_gqa").scaled(B=B, Hq=Hq, Hkv=Hkv, ctx_override=ctx, seed=seed,
-                                                     shards=world, interleave=interleave)
-    say(f"decode active B={B} Hq={Hq} Hkv={Hkv} prior={prior} world={world} interleave={interleave}")
+                                                     shards=world, interleave=interleave, D=D)
+    say(f"decode active B={B} Hq={Hq} Hkv={Hkv} D={D} prior={prior} world={world} interleave={interleave}")
     d = gen.decode_inputs(wl, dev)
     shards = [ca.dcp.build_shard_cache(d["k_seq"], d["v_seq"], d["offsets"], np.asarray(prior), r, world, interleave,
                                        16, d["block_rand"]) for r in range(world)]
@@ -513,6 +519,10 @@ def test_decode_active_token_matches_oracle(dev, world, interleave):
 
 def test_decode_active_token_gqa_full_group(dev):
     _decode_active_case(dev, 3, 64, 8, (1023, 1024, 5000), 2, 16)
+
+
+def test_decode_active_token_head_dim_64(dev):
+    _decode_active_case(dev, 4, 16, 4, (0, 47, 3100, 6000), 2, 16, D=64)
 
 
 def test_decode_active_rejects_bad_rank(dev):
