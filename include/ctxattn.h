@@ -103,7 +103,9 @@ typedef struct {
  * Supported: D in {64, 128} for both dtypes; MHA (same H for q and kv). bf16 with D == 128
  * runs on the MFMA kernel (the head size the kernel reference page's Interface asserts);
  * fp32, and bf16 with D == 64, run on a vector kernel with fp32 arithmetic (bf16 elements
- * widened as loaded), which never splits and is several times slower. Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
+ * widened as loaded), which never splits and runs about 20x slower (a 40-head 9450 x 9450
+ * step on MI355X: about 55 TFLOP/s for bf16 D == 64, 35 for fp32 D == 128, against about
+ * 1150 for bf16 D == 128 on the MFMA kernel). Sk == 0 is allowed (all rows empty). Errors: CA_ERR_NULL, CA_ERR_SHAPE,
  * CA_ERR_DTYPE, CA_ERR_UNSUPPORTED, CA_ERR_WORKSPACE (too small), CA_ERR_HIP.
  */
 ca_status ring_attn_step(const void* q, ca_strides q_strides,
