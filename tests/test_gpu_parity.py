@@ -337,7 +337,7 @@ def _ring_case(dev, wl, S, ranks, variant, layout=None, causal=None, depth=1, H=
         rows = (oracle.contiguous_tokens if layout == "contiguous" else oracle.striped_tokens)(S, wl.cp, r)
         allowed = oracle.causal_allowed(rows, S_all) if causal else None
         ro, rl = oracle.attention_heads(t["q"][:, rows], t["k"], t["v"], scale, allowed=allowed)
-        check(f"rank {r}", o, l, ro, rl, *tol(wl.dtype))
+        check(f"rank {r}", o, l, ro, rl, *tol(wl.dtype, wl.D))
 
 
 def test_tiny_fp32_ring_full_config(dev):
@@ -375,6 +375,19 @@ def test_ring_fold_matches_oracle(dev, streams, split, layout, causal):
     wl = workloads.workload("wan22_cp8_online")
     _ring_case(dev, wl, 8 * 136, ranks=(0, 5), variant="online", layout=layout, causal=causal, H=2, split=split,
                fold=True, compute_streams=streams)
+
+
+@pytest.mark.parametrize("variant,layout,causal,kw", [
+    ("online", "contiguous", False, {"fold": True, "fused_hops": True}),
+    ("online", "striped", True, {"fold": True}),
+    ("constmax", "contiguous", False, {"fused_hops": True}),
+    ("constmax", "contiguous", False, {})])
+def test_ring_bf16_head_dim_64(dev, variant, layout, causal, kw):
+    """Whole ring passes with bf16 head_dim 64 (the vector step kernel): folding per stream
+    with hops carried by the step calls (here copies ahead of each step), striped causal, and
+    const-max with its bound and accumulator."""
+    wl = workloads.workload("wan22_cp8_online").scaled(D=64)
+    _ring_case(dev, wl, 8 * 150, ranks=(0, 3), variant=variant, layout=layout, causal=causal, H=2, **kw)
 
 
 @pytest.mark.parametrize("depth", [2, 3])
