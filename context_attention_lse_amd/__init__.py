@@ -21,6 +21,7 @@ from .api import (  # noqa: F401
     lse_merge,
     ring_attn_const_max_step,
     ring_attn_step,
+    ring_attn_step_pair,
     ring_attn_workspace_size,
     segmented_attention_partial,
     segmented_attention_workspace_size,
@@ -34,7 +35,8 @@ from . import dcp, ring, streams  # noqa: F401
 __all__ = [
     "CtxAttnError", "const_max_acc_size", "const_max_bound", "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_partial_noalloc",
     "dcp_decode_workspace_size",
-    "key_sqnorm_max", "kv_chunk_copy", "lse_merge", "ring_attn_const_max_step", "ring_attn_step", "ring_attn_workspace_size",
+    "key_sqnorm_max", "kv_chunk_copy", "lse_merge", "ring_attn_const_max_step", "ring_attn_step", "ring_attn_step_pair",
+    "ring_attn_workspace_size",
     "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
     "sink_attention_partial", "sink_attention_workspace_size", "step_workspace", "version",
     "dcp", "ring",

@@ -26,7 +26,7 @@ EXPORTS = (
     "dcp_decode_partial", "dcp_decode_partial_active", "dcp_decode_workspace_size", "kv_chunk_copy", "ca_last_error",
     "ca_version", "segmented_attention_partial", "segmented_attention_workspace_size", "const_max_sink_prologue",
     "ring_attn_const_max_step_sinks", "sink_attention_partial", "sink_attention_workspace_size",
-    "dcp_decode_partial_noalloc",
+    "dcp_decode_partial_noalloc", "ring_attn_step_pair",
 )
 
 
@@ -49,6 +49,8 @@ SIGNATURES = {
                            _sz, _vp, _vp, _vp, _vp, _sz, _vp],
     "ring_attn_step_fold_hop": [_vp, ca_strides, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp,
                                 _vp, _sz, _vp, _vp, _vp, _vp, _sz, _vp],
+    "ring_attn_step_pair": [_vp, ca_strides, _vp, _vp, _vp, _vp, ca_strides, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp,
+                            _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "ring_attn_workspace_size": [_i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)],
     "key_sqnorm_max": [_vp, ca_strides, _i, _i, _i, _i, _i, _vp, _i, _vp],
     "const_max_bound": [_vp, ca_strides, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp],

@@ -129,6 +129,51 @@ def ring_attn_step(q, k, v, scale=None, mask="none", out=None, lse=None, workspa
     return out, lse
 
 
+def ring_attn_step_pair(q, k1, v1, k2, v2, scale=None, out=None, lse=None, workspace=None, stream=None, fold=False,
+                        hops=()):
+    """Two consecutive ring steps in one launch: online-max attention of q [B, Sq, H, D] against
+    the keys of chunk 1 and then of chunk 2 ([B, Sk1, H, D] and [B, Sk2, H, D], one set of
+    strides, Sk1 a multiple of 32; no mask), i.e. the LSE merge of the two steps' partials.
+    ``fold``, ``out``, ``lse``, ``workspace`` as for ring_attn_step. ``hops``: up to two ring
+    hops (dst_k, dst_v, src_k, src_v) of one size, carried by the same launch."""
+    _check_cuda(q, k1, v1, k2, v2, out, lse, workspace)
+    hops = list(hops)
+    if len(hops) > 2:
+        raise ValueError("at most two hops")
+    nbytes = 0
+    for h in hops:
+        n = _hop_bytes(h)
+        if nbytes and n != nbytes:
+            raise ValueError("the two hops must have one size")
+        nbytes = n
+    B, Sq, H, D = q.shape
+    for k, v in ((k1, v1), (k2, v2)):
+        if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+            raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+        if k.stride() != v.stride():
+            raise ValueError("k and v must share strides")
+    if k1.shape[1] and k2.shape[1] and k1.stride() != k2.stride():
+        raise ValueError("both chunks must share strides")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise TypeError("q, k and v must share a dtype")
+    if fold:
+        if out is None or lse is None:
+            raise ValueError("fold needs the prior partial in out and lse")
+        if out.shape != (B, H, Sq, D) or lse.shape != (B, H, Sq) or out.dtype != torch.float32 \
+                or lse.dtype != torch.float32 or not (out.is_contiguous() and lse.is_contiguous()):
+            raise ValueError("fold: out [B, H, Sq, D] and lse [B, H, Sq] must be contiguous fp32")
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    hp = [_ptr(t) for h in hops for t in h] + [None] * (8 - 4 * len(hops))
+    _lib.call("ring_attn_step_pair", _ptr(q), _strides(q), _ptr(k1), _ptr(v1), _ptr(k2), _ptr(v2),
+              _strides(k1 if k1.shape[1] else k2),
+              _dtype_code(q), B, H, Sq, k1.shape[1], k2.shape[1], D, _scale(scale), int(bool(fold)), _ptr(out),
+              _ptr(lse), *_ws(workspace), *hp, nbytes, _stream(stream))
+    return out, lse
+
+
 def key_sqnorm_max(k, kmax_sq=None, accumulate=False, stream=None):
     """Per (b, h) max of |k_j|^2 over the chunk, optionally max-folded into kmax_sq [B, H]."""
     _check_cuda(k, kmax_sq)

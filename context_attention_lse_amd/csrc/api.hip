@@ -1,5 +1,6 @@
 // C ABI of libctxattn: argument validation, then one launch sequence per call on the
 // caller's stream. No allocation, no state kept between calls (see include/ctxattn.h).
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -137,16 +138,27 @@ static ca_status check_hop(const char* fn, const Hop& hop) {
   return CA_OK;
 }
 
+// The second chunk of a two-chunk step launch (ring_attn_step_pair); k2 == NULL: none.
+struct Pair {
+  const void* k2;
+  const void* v2;
+  int Sk1;
+};
+
 static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides qs, const void* k, const void* v,
                                      ca_strides kvs, int dtype, int B, int H, int Sq, int Sk, int D,
                                      float softmax_scale, int mask, float* o, float* lse, void* workspace,
-                                     size_t workspace_bytes, void* stream, int fold, Hop hop = Hop{}) {
-  CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D));
+                                     size_t workspace_bytes, void* stream, int fold, Hop hop = Hop{},
+                                     Pair pair = Pair{}, Hop hop2 = Hop{}) {
+  // (a two-chunk launch: k and v hold the first chunk's Sk1 keys; the caller checked the second)
+  CA_TRY(attn_common(q, qs, k, v, kvs, dtype, B, H, Sq, pair.k2 ? pair.Sk1 : Sk, D));
   if (mask < CA_MASK_NONE || mask > CA_MASK_CAUSAL_STRICT) return fail(CA_ERR_UNSUPPORTED, "unknown mask %d", mask);
-  if (int64_t(B) * H * Sq == 0) {   // no rows: only the hop, if any
-    if (hop.bytes == 0) return hip_status(hipSuccess, "");
-    return hip_status(ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, static_cast<hipStream_t>(stream)),
-                      name);
+  if (int64_t(B) * H * Sq == 0) {   // no rows: only the hops, if any
+    hipError_t e = hipSuccess;
+    if (hop.bytes) e = ctxattn::launch_kv_copy(hop.dk, hop.dv, hop.sk, hop.sv, hop.bytes, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && hop2.bytes)
+      e = ctxattn::launch_kv_copy(hop2.dk, hop2.dv, hop2.sk, hop2.sv, hop2.bytes, static_cast<hipStream_t>(stream));
+    return hip_status(e, name);
   }
   if (!o || !lse) return fail(CA_ERR_NULL, "o and lse are required");
   if (!aligned16(o)) return fail(CA_ERR_SHAPE, "o must be 16-byte aligned");
@@ -160,9 +172,18 @@ static ca_status ring_attn_step_impl(const char* name, const void* q, ca_strides
   a.G = 1;
   a.o = o; a.lse = lse;
   a.fold = fold;
+  a.k2 = pair.k2; a.v2 = pair.v2; a.Sk1 = pair.Sk1;
   CA_TRY(attach_workspace(a, dtype, workspace, workspace_bytes));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = attach_hop(a, hop, dtype, mask, s);
+  if (e == hipSuccess && hop2.bytes) {   // the second hop rides with the first, or is copied ahead
+    if (a.hop_wgs > 0) {
+      a.hop_sk2 = hop2.sk; a.hop_sv2 = hop2.sv; a.hop_dk2 = hop2.dk; a.hop_dv2 = hop2.dv;
+      a.hop_units2 = int64_t(hop2.bytes / 16);
+    } else {
+      e = ctxattn::launch_kv_copy(hop2.dk, hop2.dv, hop2.sk, hop2.sv, hop2.bytes, s);
+    }
+  }
   if (e != hipSuccess) return hip_status(e, name);
   e = mfma_step(dtype, D) ? ctxattn::launch_attn_bf16(a, false, s)
                           : ctxattn::launch_attn_f32(a, false, dtype == CA_BF16, s);
@@ -202,6 +223,39 @@ ca_status ring_attn_step_fold_hop(const void* q, ca_strides qs, const void* k, c
   CA_TRY(check_hop("ring_attn_step_fold_hop", hop));
   return ring_attn_step_impl("ring_attn_step_fold_hop launch", q, qs, k, v, kvs, dtype, B, H, Sq, Sk, D,
                              softmax_scale, mask, o, lse, workspace, workspace_bytes, stream, 1, hop);
+}
+
+ca_status ring_attn_step_pair(const void* q, ca_strides qs, const void* k1, const void* v1, const void* k2,
+                              const void* v2, ca_strides kvs, int dtype, int B, int H, int Sq, int Sk1, int Sk2,
+                              int D, float softmax_scale, int fold, float* o, float* lse, void* workspace,
+                              size_t workspace_bytes, void* hop_dst_k, void* hop_dst_v, const void* hop_src_k,
+                              const void* hop_src_v, void* hop2_dst_k, void* hop2_dst_v, const void* hop2_src_k,
+                              const void* hop2_src_v, size_t hop_bytes, void* stream) {
+  const char* name = "ring_attn_step_pair";
+  if (Sk1 < 0 || Sk2 < 0) return fail(CA_ERR_SHAPE, "%s: negative chunk length", name);
+  if (int64_t(Sk1) + Sk2 > INT_MAX) return fail(CA_ERR_UNSUPPORTED, "%s: chunks too long", name);
+  CA_TRY(check_dtype(dtype));
+  CA_TRY(check_head_dim(dtype, D));
+  if (!mfma_step(dtype, D)) return fail(CA_ERR_UNSUPPORTED, "%s: bf16 with head_dim 128 only", name);
+  if (Sk1 % 32) return fail(CA_ERR_UNSUPPORTED, "%s: the first chunk's length must be a multiple of 32 (got %d)",
+                            name, Sk1);
+  CA_TRY(check_bshd("k2", k2, kvs, dtype, B, Sk2, H, D));
+  CA_TRY(check_bshd("v2", v2, kvs, dtype, B, Sk2, H, D));
+  const Hop h1{hop_dst_k, hop_dst_v, hop_src_k, hop_src_v, hop_bytes};
+  const Hop h2 = hop2_src_k ? Hop{hop2_dst_k, hop2_dst_v, hop2_src_k, hop2_src_v, hop_bytes} : Hop{};
+  CA_TRY(check_hop(name, h1));
+  CA_TRY(check_hop(name, h2));
+  if (Sk1 == 0 || Sk2 == 0) {   // one chunk: the plain step, hops copied ahead of it
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (h2.bytes) {
+      const ca_status st = hip_status(ctxattn::launch_kv_copy(h2.dk, h2.dv, h2.sk, h2.sv, h2.bytes, s), name);
+      if (st != CA_OK) return st;
+    }
+    return ring_attn_step_impl(name, q, qs, Sk1 ? k1 : k2, Sk1 ? v1 : v2, kvs, dtype, B, H, Sq, Sk1 + Sk2, D,
+                               softmax_scale, CA_MASK_NONE, o, lse, workspace, workspace_bytes, stream, fold, h1);
+  }
+  return ring_attn_step_impl(name, q, qs, k1, v1, kvs, dtype, B, H, Sq, Sk1 + Sk2, D, softmax_scale, CA_MASK_NONE, o,
+                             lse, workspace, workspace_bytes, stream, fold, h1, Pair{k2, v2, Sk1}, h2);
 }
 
 ca_status ring_attn_workspace_size(int dtype, int B, int H, int Sq, int Sk, int D, int mask, size_t* bytes) {

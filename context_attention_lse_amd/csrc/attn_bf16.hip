@@ -415,14 +415,16 @@ __device__ __forceinline__ int64_t segment_slot(const Split& sp, int nqb, int nk
 // The ring hop of a launch that carries one: workgroup cw of a.hop_wgs copies its grid-stride
 // share of K then V, 16 bytes a lane, HOP_UNROLL vectors in flight per lane. The hop's
 // workgroups come last in the grid, so they take the CUs the step's workgroups leave free.
+// A launch over two chunks carries two hops: the same workgroups copy the second after the first.
 constexpr int HOP_UNROLL = 16;
-__device__ __forceinline__ void hop_copy(const AttnArgs& a, int cw) {
-  const floatx4* sk = static_cast<const floatx4*>(a.hop_sk);
-  const floatx4* sv = static_cast<const floatx4*>(a.hop_sv);
-  floatx4* dk = static_cast<floatx4*>(a.hop_dk);
-  floatx4* dv = static_cast<floatx4*>(a.hop_dv);
-  const int64_t units = a.hop_units, total = 2 * units;
-  const int64_t stride = int64_t(a.hop_wgs) * NT * HOP_UNROLL;
+__device__ __forceinline__ void hop_copy_one(const void* sk_, const void* sv_, void* dk_, void* dv_, int64_t units,
+                                             int hop_wgs, int cw) {
+  const floatx4* sk = static_cast<const floatx4*>(sk_);
+  const floatx4* sv = static_cast<const floatx4*>(sv_);
+  floatx4* dk = static_cast<floatx4*>(dk_);
+  floatx4* dv = static_cast<floatx4*>(dv_);
+  const int64_t total = 2 * units;
+  const int64_t stride = int64_t(hop_wgs) * NT * HOP_UNROLL;
   for (int64_t base = int64_t(cw) * NT * HOP_UNROLL + threadIdx.x; base < total; base += stride) {
     floatx4 x[HOP_UNROLL];
 #pragma unroll
@@ -437,14 +439,20 @@ __device__ __forceinline__ void hop_copy(const AttnArgs& a, int cw) {
     }
   }
 }
+template <bool PAIR>
+__device__ __forceinline__ void hop_copy(const AttnArgs& a, int cw) {
+  hop_copy_one(a.hop_sk, a.hop_sv, a.hop_dk, a.hop_dv, a.hop_units, a.hop_wgs, cw);
+  if (PAIR && a.hop_units2 > 0) hop_copy_one(a.hop_sk2, a.hop_sv2, a.hop_dk2, a.hop_dv2, a.hop_units2, a.hop_wgs, cw);
+}
 
-template <int MODE, int MASK, bool SPLIT>
-__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split sp) {
+// The step kernel's body. PAIR: a launch over two chunks (ring_attn_step_pair), whose key
+// tiles from a.Sk1 on are read from the second chunk; the other instances compile without it.
+template <int MODE, int MASK, bool SPLIT, bool PAIR>
+__device__ __forceinline__ void step_body(const AttnArgs& a, int nqb, int nkt, int nwork, const Split& sp) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   if (a.hop_wgs > 0 && int(blockIdx.x) >= int(gridDim.x) - a.hop_wgs) {
-    hop_copy(a, int(blockIdx.x) - (int(gridDim.x) - a.hop_wgs));
+    hop_copy<PAIR>(a, int(blockIdx.x) - (int(gridDim.x) - a.hop_wgs));
     return;
   }
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x - a.hop_wgs, nwork);
@@ -549,6 +557,12 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
     const int hk = h / a.G;                // K/V head of this query head
     const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k) + b * a.ksb + hk * a.ksh);
     const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v) + b * a.ksb + hk * a.ksh);
+    // a launch over two chunks: key tiles from key sk1 on come from the second chunk
+    const int sk1 = PAIR ? a.Sk1 : INT_MAX;
+    const char* kbase2 =
+        PAIR ? reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k2) + b * a.ksb + hk * a.ksh) : kbase;
+    const char* vbase2 =
+        PAIR ? reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v2) + b * a.ksb + hk * a.ksh) : vbase;
     // keys of this (batch, head): the whole chunk, or its own count
     const int Skb = a.sk_of_bh ? min(Sk, max(a.sk_of_bh[bh], 0)) : Sk;
     if (!SPLIT) k1 = min(k1, (Skb + BK - 1) / BK);
@@ -591,6 +605,10 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
       const int key0 = (k0 + j) * BK;
       const char* kt = kbase + key0 * kss_bytes;
       const char* vt = vbase + key0 * kss_bytes;
+      if (PAIR && key0 >= sk1) {   // wave-uniform
+        kt = kbase2 + (int64_t(key0) - sk1) * kss_bytes;
+        vt = vbase2 + (int64_t(key0) - sk1) * kss_bytes;
+      }
       uint32_t ko = koff, vo = voff;
       if (__builtin_expect(key0 + BK > Skb, 0)) {   // the chunk's last tile only
         const int rr = max(0, min(crow, Skb - 1 - key0));
@@ -875,6 +893,19 @@ void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split s
   }
 }
 
+template <int MODE, int MASK, bool SPLIT>
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_step_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split sp) {
+  step_body<MODE, MASK, SPLIT, false>(a, nqb, nkt, nwork, sp);
+}
+
+// Two chunks in one launch (online, no mask).
+template <bool SPLIT>
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_step_pair_bf16(const AttnArgs a, int nqb, int nkt, int nwork, const Split sp) {
+  step_body<MODE_ONLINE, CA_MASK_NONE, SPLIT, true>(a, nqb, nkt, nwork, sp);
+}
+
 // Workgroups resident at once on the current device (one per CU).
 int resident_workgroups() {
   static int cache[64] = {0};
@@ -936,12 +967,13 @@ Plan make_plan(int B, int H, int Sq, int Sk, int mask) {
   return p;
 }
 
-template <int MODE, int MASK, bool SPLIT>
+template <int MODE, int MASK, bool SPLIT, bool PAIR>
 hipError_t launch_one(const AttnArgs& a, const Plan& p, hipStream_t s) {
+  const void* kern = PAIR ? reinterpret_cast<const void*>(&attn_step_pair_bf16<SPLIT>)
+                          : reinterpret_cast<const void*>(&attn_step_bf16<MODE, MASK, SPLIT>);
   static bool attr_set = false;   // dynamic LDS above 64 KB must be allowed once
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_step_bf16<MODE, MASK, SPLIT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(LDS_BYTES));
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(LDS_BYTES));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -960,16 +992,19 @@ hipError_t launch_one(const AttnArgs& a, const Plan& p, hipStream_t s) {
   }
   if (nwork == 0 && a.hop_wgs == 0) return hipSuccess;
   const int grid = round_up8(nwork) + a.hop_wgs;
-  hipLaunchKernelGGL((attn_step_bf16<MODE, MASK, SPLIT>), dim3(grid), dim3(NT), LDS_BYTES, s, a, p.nqb, p.nkt,
-                     nwork, sp);
+  if constexpr (PAIR)
+    hipLaunchKernelGGL((attn_step_pair_bf16<SPLIT>), dim3(grid), dim3(NT), LDS_BYTES, s, a, p.nqb, p.nkt, nwork, sp);
+  else
+    hipLaunchKernelGGL((attn_step_bf16<MODE, MASK, SPLIT>), dim3(grid), dim3(NT), LDS_BYTES, s, a, p.nqb, p.nkt,
+                       nwork, sp);
   return hipGetLastError();
 }
 
-template <int MODE, int MASK>
+template <int MODE, int MASK, bool PAIR = false>
 hipError_t launch_mode(const AttnArgs& a, hipStream_t s) {
   const Plan p = make_plan(a.B, a.H, a.Sq, a.Sk, MASK);
-  if (MASK != kMaskDcp && a.ws != nullptr && p.split) return launch_one<MODE, MASK, true>(a, p, s);
-  return launch_one<MODE, MASK, false>(a, p, s);
+  if (MASK != kMaskDcp && a.ws != nullptr && p.split) return launch_one<MODE, MASK, true, PAIR>(a, p, s);
+  return launch_one<MODE, MASK, false, PAIR>(a, p, s);
 }
 
 }  // namespace
@@ -988,6 +1023,7 @@ int attn_bf16_idle_slots(int B, int H, int Sq, int Sk, int mask, bool with_works
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, bool const_max, hipStream_t s) {
+  if (a.k2 != nullptr) return launch_mode<MODE_ONLINE, CA_MASK_NONE, true>(a, s);   // two chunks: online, no mask
   if (const_max) return launch_mode<MODE_CONSTMAX, CA_MASK_NONE>(a, s);
   switch (a.mask) {
     case CA_MASK_CAUSAL_INCL: return launch_mode<MODE_ONLINE, CA_MASK_CAUSAL_INCL>(a, s);

@@ -117,6 +117,18 @@ struct AttnArgs {
   void* hop_dv;
   int64_t hop_units;
   int hop_wgs;
+  // a second hop carried by the same workgroups (hop_units2 vectors of K and of V; 0: none)
+  const void* hop_sk2;
+  const void* hop_sv2;
+  void* hop_dk2;
+  void* hop_dv2;
+  int64_t hop_units2;
+  // a second K/V chunk (bf16 path, no mask): keys [Sk1, Sk) of the launch are keys
+  // [0, Sk - Sk1) of k2 / v2, which share k's strides; Sk1 is a multiple of the key tile.
+  // NULL: one chunk.
+  const void* k2;
+  const void* v2;
+  int Sk1;
 };
 
 // Internal mask (bf16 path, online-max only): the keys are rank R's slice of a chunk

@@ -102,11 +102,19 @@ class RingPass:
     779 us. With fold as well, each compute stream folds its steps into one running partial
     and the pass ends in a 2-way merge instead of an 8-way one (Wan2.2, unsplit steps two in
     flight: 695 -> 687 us).
+
+    pair_steps=True (online, non-causal, fold and fused_hops, bf16 D = 128, chunk length a
+    multiple of 32): once two chunks have arrived, one launch computes both steps
+    (ring_attn_step_pair), so each query tile's fixed work (Q load, copy prologue, epilogue,
+    fold) is paid once per two chunks. Launches alternate the two compute streams as single
+    steps do; launch i carries the hops of chunks 2i + 4 and 2i + 5 and every received chunk
+    keeps a buffer of its own (cp - 1 of them).
     """
 
     def __init__(self, q, k_pool, v_pool, rank, *, layout="contiguous", causal=False, variant="online",
                  scale=None, prefetch_depth=2, out_dtype=torch.float32, copy_stream=None,
-                 compute_streams=None, split=False, sink_theta=None, sink_cap=32, fold=False, fused_hops=False):
+                 compute_streams=None, split=False, sink_theta=None, sink_cap=32, fold=False, fused_hops=False,
+                 pair_steps=False):
         if variant not in ("online", "constmax"):
             raise ValueError(f"unknown variant {variant!r}")
         if fold and variant != "online":
@@ -133,6 +141,15 @@ class RingPass:
                 raise ValueError("fused hops do not combine with sinks")
             self.depth, self.nbuf = 2, 4
         B, Sq, H, D = q.shape
+        self.pair_steps = bool(pair_steps)
+        if self.pair_steps:
+            if variant != "online" or causal or not fold or not self.fused_hops or split:
+                raise ValueError("pair_steps: online, non-causal, with fold=True and fused_hops=True, no split")
+            if q.dtype != torch.bfloat16 or D != 128:
+                raise ValueError("pair_steps: bf16 with head_dim 128 (the MFMA step kernel)")
+            if k_pool.shape[2] % 32:
+                raise ValueError(f"pair_steps: the chunk length ({k_pool.shape[2]}) must be a multiple of 32")
+            self.nbuf = max(1, self.cp - 1)
         chunk_shape = tuple(k_pool.shape[1:])
         dev = q.device
         self.kbuf = [torch.empty(chunk_shape, dtype=k_pool.dtype, device=dev) for _ in range(self.nbuf)]
@@ -224,6 +241,8 @@ class RingPass:
         each step's kernel on the stream that runs it."""
         cs = torch.cuda.current_stream()
         cp = self.cp
+        if self.pair_steps:
+            return self._run_pairs(cs, timing_events)
         if self.fused_hops:
             return self._run_fused(cs, timing_events)
         if self.variant == "constmax":
@@ -374,9 +393,58 @@ class RingPass:
         return self.out, self.lse
 
 
+    def _run_pairs(self, cs, timing_events):
+        """run() with two steps per launch (ring_attn_step_pair). Launch i computes chunks
+        2i and 2i + 1 on compute stream i % 2 and carries the hops of chunks 2i + 4 and
+        2i + 5, which the next launch on the same stream reads. The chunks of each stream's
+        first launch are copied ahead of it on that stream (chunk 1 before launch 0, chunks
+        2 and 3 before launch 1, beside launch 0). Each received chunk has a buffer of its own,
+        so no hop overwrites a chunk a launch on the other stream may still read."""
+        cp = self.cp
+        launches = [tuple(range(s, min(s + 2, cp))) for s in range(0, cp, 2)]
+        aux = self.aux_stream
+        streams = [aux if (aux is not None and i % 2 == 1) else cs for i in range(len(launches))]
+        if aux is not None:
+            aux.wait_stream(cs)
+        for i in range(min(2, len(launches))):
+            with torch.cuda.stream(streams[i]):
+                for t in launches[i]:
+                    if t >= 1:
+                        api.kv_chunk_copy(*self._hop_buffers(t))
+        started = [False, False]
+        for i, chunks in enumerate(launches):
+            st = streams[i]
+            a = 0 if st is cs else 1
+            hops = [self._hop_buffers(t) for t in (2 * i + 4, 2 * i + 5) if t < cp]
+            o_dst, l_dst = self.o_parts[a], self.lse_parts[a]
+            with torch.cuda.stream(st):
+                if timing_events is not None:
+                    for t in chunks:
+                        timing_events[t][0].record(st)
+                if len(chunks) == 2:
+                    (k1, v1), (k2, v2) = self._chunk(chunks[0]), self._chunk(chunks[1])
+                    api.ring_attn_step_pair(self.q, k1, v1, k2, v2, scale=self.scale, out=o_dst, lse=l_dst,
+                                            workspace=self.ws[a], fold=started[a], hops=hops)
+                else:
+                    k, v = self._chunk(chunks[0])
+                    api.ring_attn_step(self.q, k, v, scale=self.scale, out=o_dst, lse=l_dst, workspace=self.ws[a],
+                                       fold=started[a], hop=hops[0] if hops else None)
+                    for h in hops[1:]:
+                        api.kv_chunk_copy(*h)
+                if timing_events is not None:
+                    for t in chunks:
+                        timing_events[t][1].record(st)
+            started[a] = True
+        if aux is not None:
+            cs.wait_stream(aux)
+        n = 2 if started[1] else 1
+        api.lse_merge(self.o_parts[:n], self.lse_parts[:n], out=self.out, lse_out=self.lse)
+        return self.out, self.lse
+
+
 def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous", causal=False,
                    variant="online", scale=None, prefetch_depth=2, split=False, fold=False, compute_streams=None,
-                   fused_hops=False):
+                   fused_hops=False, pair_steps=False):
     """Convenience: rank ``rank``'s output for global [B, S, H, D] inputs."""
     check_divisible(q_global.shape[1], cp)
     q = shard(q_global, cp, rank, layout)
@@ -384,5 +452,5 @@ def ring_attention(q_global, k_global, v_global, cp, rank, *, layout="contiguous
     vp = chunk_pool(v_global, cp, layout)
     rp = RingPass(q, kp, vp, rank, layout=layout, causal=causal, variant=variant, scale=scale,
                   prefetch_depth=prefetch_depth, split=split, fold=fold, compute_streams=compute_streams,
-                  fused_hops=fused_hops)
+                  fused_hops=fused_hops, pair_steps=pair_steps)
     return rp.run()

@@ -192,6 +192,35 @@ ca_status ring_attn_step_fold_hop(const void* q, ca_strides q_strides,
                                   void* stream);
 
 /*
+ * ring_attn_step_pair -- two consecutive ring steps in one launch, once both chunks have
+ * arrived: attention of the resident query shard against the keys of chunk 1 and then of
+ * chunk 2, which by the LSE merge ("Kernel reference: ring_attention_const_max_fwd", the
+ * ring loop; the context-parallelism page, merging partial attention by LSE) equals the two
+ * steps' partials merged. It halves the per-launch work that does not scale with the keys
+ * (each query tile's Q load, copy prologue, epilogue and fold) where steps are short.
+ *   q               as ring_attn_step
+ *   k1, v1          [B, Sk1, H, D] the first chunk; Sk1 a multiple of 32
+ *   k2, v2          [B, Sk2, H, D] the second chunk, with the first chunk's strides kv_strides
+ *   fold            0: o and lse receive the two chunks' partial (as ring_attn_step);
+ *                   1: they hold a prior partial and receive its merge (as ring_attn_step_fold)
+ *   workspace       as ring_attn_step, sized for Sk1 + Sk2 keys
+ *   hop_*, hop2_*   up to two ring hops carried by the same launch, each as ring_attn_step_hop
+ *                   (hop2_src_k == NULL: one hop; hop_bytes 0: none); both hop_bytes long
+ * No mask (the steps it pairs are non-causal). Supported: bf16, D == 128 (the MFMA kernel),
+ * MHA. Sk1 == 0 or Sk2 == 0 runs the other chunk as ring_attn_step. Errors as
+ * ring_attn_step_hop, and CA_ERR_UNSUPPORTED when Sk1 is not a multiple of 32.
+ */
+ca_status ring_attn_step_pair(const void* q, ca_strides q_strides,
+                              const void* k1, const void* v1, const void* k2, const void* v2,
+                              ca_strides kv_strides, int dtype, int B, int H, int Sq, int Sk1, int Sk2,
+                              int D, float softmax_scale, int fold, float* o, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              void* hop_dst_k, void* hop_dst_v, const void* hop_src_k,
+                              const void* hop_src_v, void* hop2_dst_k, void* hop2_dst_v,
+                              const void* hop2_src_k, const void* hop2_src_v, size_t hop_bytes,
+                              void* stream);
+
+/*
  * ring_attn_workspace_size -- bytes of step workspace that ring_attn_step and
  * ring_attn_const_max_step (mask CA_MASK_NONE) need for these sizes on the CURRENT
  * device (the split depends on its compute-unit count). 0: the call does not split
