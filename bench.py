@@ -34,7 +34,7 @@ whatever that power allows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
                        [--only wan22,constmax,decode,prefill,tiny,contrast,copy]
-                       [--roofline-only [incl|strict|wan22|wan22split|constmax|online720|merge|bound|decode|copy]]
+                       [--roofline-only [incl|strict|wan22|wan22pair|wan22split|constmax|online720|merge|bound|decode|copy]]
 
 Warm-up: W untimed steps, then more until the warm-up has kept the GPU busy for at least
 one second, so the clock has settled whatever W is (after a few tens of milliseconds of
@@ -63,14 +63,14 @@ MIN_WARM_MS = 1000.0          # warm-up floor in GPU time
 # source the figure no longer describes the kernel and traffic is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC = {
-    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
-                                                     "fetch_kib": 610894.4, "write_kib": 265384.7},
-    "attn_step_bf16/wan22_cp8_online_pairs": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
-                                              "fetch_kib": 29352.9, "write_kib": 20641.6},
-    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
-                                                 "fetch_kib": 57590.0, "write_kib": 63000.0},
-    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "72a5a8d42c60daeb",
-                                           "fetch_kib": 332356.9, "write_kib": 190625.0},
+    "attn_step_bf16/striped_causal_128k_incl_fold": {"source": "attn_bf16.hip", "sha256": "51a4a685faeba44f",
+                                                     "fetch_kib": 609969.8, "write_kib": 265080.8},
+    "attn_step_pair_bf16/wan22_cp8_online": {"source": "attn_bf16.hip", "sha256": "51a4a685faeba44f",
+                                              "fetch_kib": 43172.3, "write_kib": 20645.1},
+    "attn_step_bf16/wan22_cp8_online_keysplit": {"source": "attn_bf16.hip", "sha256": "51a4a685faeba44f",
+                                                 "fetch_kib": 57600.9, "write_kib": 63000.0},
+    "attn_step_bf16/wan22_720p_constmax": {"source": "attn_bf16.hip", "sha256": "51a4a685faeba44f",
+                                           "fetch_kib": 332391.1, "write_kib": 190612.2},
     "dcp_decode/dcp_decode_gqa": {"source": "decode.hip", "sha256": "a324b829ca6b6ff4",
                                   "fetch_kib": 2778052.6 + 14932.25, "write_kib": 31631.8 + 1040.0},
     "lse_merge/wan22_720p_constmax": {"source": "merge.hip", "sha256": "c788302e3d8b9dc0",
@@ -335,10 +335,11 @@ def headline(args, torch, ca, workloads, gen, dev, clock):
 
 # ------------------------------------------------------------------ workloads
 
-def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev):
+def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev, two_chunks=False):
     """The Wan2.2 pass's step form without its hops and merge: unsplit steps over chunks
     0..n-1, step s on compute stream s % 2, so two launches are in flight as in the pass,
-    each stream's steps after its first folding into its running partial.
+    each stream's steps after its first folding into its running partial. two_chunks: each
+    launch takes two consecutive chunks (ring_attn_step_pair), n/2 launches.
     Returns fn() (launches on the current stream's work order) and the launch count."""
     cur = torch.cuda.current_stream()
     aux = ca.streams.side_streams(2, dev)[1]   # overlaps the calling stream (its own hardware queue)
@@ -347,12 +348,16 @@ def step_pairs(torch, ca, q, kp, vp, n_steps, o_shape, dev):
 
     def fn():
         aux.wait_stream(cur)
-        for s in range(n_steps):
+        for s in range(n_steps // 2 if two_chunks else n_steps):
             st = cur if s % 2 == 0 else aux
             with torch.cuda.stream(st):
-                ca.ring_attn_step(q, kp[s], vp[s], out=outs[s % 2][0], lse=outs[s % 2][1], fold=s >= 2)
+                if two_chunks:
+                    ca.ring_attn_step_pair(q, kp[2 * s], vp[2 * s], kp[2 * s + 1], vp[2 * s + 1], out=outs[s % 2][0],
+                                           lse=outs[s % 2][1], fold=s >= 2)
+                else:
+                    ca.ring_attn_step(q, kp[s], vp[s], out=outs[s % 2][0], lse=outs[s % 2][1], fold=s >= 2)
         cur.wait_stream(aux)
-    return fn, n_steps
+    return fn, (n_steps // 2 if two_chunks else n_steps)
 
 
 def run_wan22(args, torch, ca, workloads, gen, dev, clock):
@@ -362,23 +367,29 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout)
     kp = ca.ring.chunk_pool(t["k"], wl.cp, wl.layout)
     vp = ca.ring.chunk_pool(t["v"], wl.cp, wl.layout)
-    # unsplit steps, two in flight on two compute streams (160 query tiles each: one step
-    # alone leaves 96 of 256 CUs idle, two fill them); each step carries the hop of the
-    # chunk two steps ahead and folds into its stream's running partial (a 2-way merge at
-    # the end instead of an 8-way one). Key-split steps (each alone fills the device) ran the
-    # pass 10% slower: their segments' partial stores and combines cost more than the
-    # overlap gives.
+    # unsplit steps, two launches in flight on two compute streams (160 query tiles each: one
+    # alone leaves 96 of 256 CUs idle, two fill them), each launch computing two consecutive
+    # chunks (ring_attn_step_pair: each query tile's Q load, prologue, epilogue and fold paid
+    # once per two chunks), carrying the hops of the chunks two launches ahead and folding
+    # into its stream's running partial (a 2-way merge at the end). Key-split steps (each
+    # alone fills the device) ran the pass 10% slower: their segments' partial stores and
+    # combines cost more than the overlap gives.
     rp = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=False, compute_streams=2,
-                          fused_hops=True, fold=True)
-    # the pass replayed as one captured HIP graph (its ten launches and stream joins, with no
+                          fused_hops=True, fold=True, pair_steps=True)
+    # the pass replayed as one captured HIP graph (its launches and stream joins, with no
     # per-launch gaps; 0.8% faster than issuing it eagerly)
     graph = rp.capture()
     # windows of tens of milliseconds: a few-millisecond window caught clock transitions
     ms = timed(torch, graph.replay, max(100, args.steps), warm_calls=max(10, args.warmup))
     clk = clock.measure(torch, graph.replay)
+    # the same pass with one chunk per launch, for comparison
+    rp1 = ca.ring.RingPass(q, kp, vp, 0, layout=wl.layout, variant="online", split=False, compute_streams=2,
+                           fused_hops=True, fold=True)
+    graph1 = rp1.capture()
+    ms1 = timed(torch, graph1.replay, max(100, args.steps), warm_calls=10)
     fl_step = ring_flops(wl.H, wl.local_S, wl.local_S, wl.D)
     fl = ring_flops(wl.H, wl.local_S, wl.S, wl.D)
-    pairs, n = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev)
+    pairs, n = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev, two_chunks=True)
     p_ms = timed(torch, pairs, max(40, args.steps)) / n
     # the key-split form a single step uses (one launch at a time, filling the device)
     ws = ca.step_workspace(q, kp[0])
@@ -389,14 +400,18 @@ def run_wan22(args, torch, ca, workloads, gen, dev, clock):
     return {"workload": wl.name, "config": "B=1 H=10 D=128 S=32768 cp=8 local=4096 bf16, QK RMS-normed, rank 0",
             "ms_per_pass": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "clock_mhz": clk,
-            "form": "unsplit steps, two in flight on two compute streams, hops carried by the steps, each stream "
-                    "folding into a running partial, 2-way LSE merge; the pass replayed as one captured HIP graph",
-            "roofline": kernel_roofline(p_ms, fl_step,
-                                        "attn_step_bf16<0, 0, false> (ring_attn_step_fold, two launches in flight)",
-                                        f"{fl_step / 1e9:.2f} GFLOP = 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
-                                        key="attn_step_bf16/wan22_cp8_online_pairs",
-                                        note="effective time per launch: the pass's 8 steps without hops or merge, "
-                                             "alternating over two streams and folding, total / 8"),
+            "form": "unsplit launches of two steps each (two chunks a launch), two in flight on two compute "
+                    "streams, hops carried by the launches, each stream folding into a running partial, 2-way LSE "
+                    "merge; the pass replayed as one captured HIP graph",
+            "one_chunk_per_launch": {"ms_per_pass": round(ms1, 4), "tflops": round(fl / (ms1 * 1e-3) / 1e12, 2),
+                                     "note": "the same pass with one chunk per launch (8 launches)"},
+            "roofline": kernel_roofline(p_ms, 2 * fl_step,
+                                        "attn_step_pair_bf16<false> (ring_attn_step_pair, folding, two launches in "
+                                        "flight)",
+                                        f"{2 * fl_step / 1e9:.2f} GFLOP = 2 chunks x 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128",
+                                        key="attn_step_pair_bf16/wan22_cp8_online",
+                                        note="effective time per launch: the pass's 4 launches without hops or merge, "
+                                             "alternating over two streams and folding, total / 4"),
             "keysplit_step": {"kernel_ms": round(k_ms, 4), "tflops": round(fl_step / (k_ms * 1e-3) / 1e12, 2),
                               "frac_bf16_peak": round(fl_step / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "traffic": traffic("attn_step_bf16/wan22_cp8_online_keysplit"),
@@ -759,6 +774,8 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
     wan22         the Wan2.2 share's unsplit step as its pass runs it: 8 launches (chunks 0..7)
                   alternating over two streams, two in flight, each stream's later steps
                   folding (10 heads, 4096^2); the figures are per launch (total / 8)
+    wan22pair     the Wan2.2 pass's launches of two chunks each (ring_attn_step_pair), 4 launches
+                  alternating over two streams, folding; the figures are per launch (total / 4)
     wan22split    the same step cut into key ranges (the form one step alone uses)
     constmax      the 720p const-max step, accumulate phase (40 heads, 9450^2)
     online720     the 720p online step
@@ -785,7 +802,7 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
         fn = lambda: ca.ring_attn_step(q, kp[src], vp[src], mask=mask, out=o, lse=lse, fold=True)  # noqa: E731
         work = causal_flops(wl.H, wl.D, n, strict=(name == "strict"))
         unit, per = "flop", f"4*H*D*visible pairs, H=32 Sq=Sk=16384 D=128, mask {mask}"
-    elif name in ("wan22", "wan22split"):
+    elif name in ("wan22", "wan22split", "wan22pair"):
         wl = workloads.workload("wan22_cp8_online")
         t = gen.ring_inputs(wl, dev)
         q = ca.ring.shard(t["q"], wl.cp, 0, wl.layout)
@@ -795,6 +812,11 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
         if name == "wan22":
             fn, launches = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev)
             unit, per = "flop", "4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128, unsplit, two launches in flight"
+            reps = 5
+        elif name == "wan22pair":
+            fn, launches = step_pairs(torch, ca, q, kp, vp, wl.cp, (1, wl.H, wl.local_S, wl.D), dev, two_chunks=True)
+            work *= 2
+            unit, per = "flop", "2 chunks x 4*H*Sq*Sk*D, H=10 Sq=Sk=4096 D=128, two launches in flight"
             reps = 5
         else:
             ws = ca.step_workspace(q, kp[0])
@@ -858,7 +880,7 @@ def profile_kernel(name, torch, ca, workloads, gen, dev, reps=10):
     else:
         raise SystemExit(f"unknown kernel {name!r}")
     ms = timed(torch, fn, reps)
-    if name == "wan22":
+    if name in ("wan22", "wan22pair"):
         ms /= launches
     rate = work / (ms * 1e-3)
     if unit == "flop":
@@ -879,7 +901,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--roofline-only", nargs="?", const="incl", default=None,
-                    choices=["incl", "strict", "wan22", "wan22split", "constmax", "online720", "merge", "bound",
+                    choices=["incl", "strict", "wan22", "wan22pair", "wan22split", "constmax", "online720", "merge",
+                             "bound",
                              "decode", "copy"],
                     help="time one kernel alone, back to back (for profiling it); default: the headline's "
                          "INCL step kernel")
