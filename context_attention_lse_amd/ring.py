@@ -90,9 +90,11 @@ class RingPass:
     idle as it drains. compute_streams overrides either default. The copy stream and the
     second compute stream come from streams.side_streams (each checked to overlap the calling
     stream) unless copy_stream is given. On the Wan2.2 share (160 query tiles of 256 rows per
-    step) the fastest pass is unsplit steps on two streams with fused hops, each stream
-    folding (0.687 ms); key-split steps on two streams, also carrying the hops, took 0.806 ms
-    against 0.731 ms for unsplit ones when the two were last compared (before the folding).
+    step) the fastest pass is unsplit launches of two chunks each (pair_steps, below) on two
+    streams with fused hops, each stream folding (0.652 ms replayed as a graph, against 0.671
+    with one chunk a launch); key-split steps on two streams, also carrying the hops, took
+    0.806 ms against 0.731 ms for unsplit ones when the two were last compared (before the
+    folding).
 
     fused_hops=True (no sinks): each step call carries the hop of the chunk two steps ahead
     (ring_attn_step_hop, or ring_attn_step_fold_hop when folding), on the CUs the step leaves
