@@ -106,6 +106,24 @@ def test_rejections_without_gpu():
                               _fake(0x10010), 1 << 30, None) == _lib.CA_ERR_SHAPE   # misaligned workspace
 
 
+def test_step_pair_rejections_without_gpu():
+    lib = _lib.load()
+    st = _lib.ca_strides(0, 128, 0)
+    hops = (None,) * 8
+    # first chunk not a multiple of 32 keys; fp32 (the pair runs on the MFMA kernel only); bf16 D = 64
+    assert lib.ring_attn_step_pair(_fake(), st, _fake(), _fake(), _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 100,
+                                   64, 128, 0.0, 0, _fake(), _fake(), None, 0, *hops, 0, None) == _lib.CA_ERR_UNSUPPORTED
+    assert b"multiple of 32" in lib.ca_last_error()
+    assert lib.ring_attn_step_pair(_fake(), st, _fake(), _fake(), _fake(), _fake(), st, _lib.CA_FP32, 1, 1, 4, 64,
+                                   64, 128, 0.0, 0, _fake(), _fake(), None, 0, *hops, 0, None) == _lib.CA_ERR_UNSUPPORTED
+    assert lib.ring_attn_step_pair(_fake(), st, _fake(), _fake(), _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 64,
+                                   64, 64, 0.0, 0, _fake(), _fake(), None, 0, *hops, 0, None) == _lib.CA_ERR_UNSUPPORTED
+    # a hop of a size that is not a multiple of 16
+    assert lib.ring_attn_step_pair(_fake(), st, _fake(), _fake(), _fake(), _fake(), st, _lib.CA_BF16, 1, 1, 4, 64,
+                                   64, 128, 0.0, 0, _fake(), _fake(), None, 0, _fake(0x2000), _fake(0x3000),
+                                   _fake(0x4000), _fake(0x5000), None, None, None, None, 100, None) == _lib.CA_ERR_SHAPE
+
+
 def test_hop_and_workspace_rejections_without_gpu():
     lib = _lib.load()
     st = _lib.ca_strides(0, 128, 0)
